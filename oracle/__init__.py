@@ -1,0 +1,192 @@
+"""CPU oracle for the tree-masked speculative verify step (ctypes over sv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The functions here are the slow fp64 reference the
+GPU library is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; it imports nothing from
+the GPU library and the GPU library imports nothing from it.
+
+Every function takes and returns host numpy arrays.  Sources are cited in
+sv_oracle.c next to each definition.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sv_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle_sv.so")
+
+TREE_OK, TREE_BAD_ROOT, TREE_BAD_PARENT = 0, 1, 2
+F32, BF16 = 0, 1
+
+
+def build(src: str = _SRC, out: str = _LIB, defines: tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc (fp contraction off, OpenMP on)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC",
+           *[f"-D{d}" for d in defines], src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def _declare(lib):
+    lib.oracle_build_tree_mask.argtypes = [_i32p, _int, _int, _u64p, _i32p, _i32p]
+    lib.oracle_tree_verify_attention.argtypes = [
+        _vp, _vp, _vp, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64, _int,
+        _i32p, _int, _u64p, _int, _int, _int, _int, _int, ctypes.c_double, _i32p, _i64,
+        _f32p, _int]
+    lib.oracle_argmax.argtypes = [_f32p, _i64, _i64, _i32p, _int]
+    lib.oracle_accept_longest_path.argtypes = [
+        _f32p, _i32p, _i32p, _i32p, _int, _int, _i64, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_kv_commit.argtypes = [
+        _vp, _vp, _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64,
+        _int, _i32p, _int, _i32p, _int, _int, _int, _int]
+    for f in ("oracle_build_tree_mask", "oracle_tree_verify_attention", "oracle_argmax",
+              "oracle_accept_longest_path", "oracle_kv_commit"):
+        getattr(lib, f).restype = _int
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle shared library."""
+    path = path or _LIB
+    if not os.path.exists(path):
+        build(out=path)
+    return _declare(ctypes.CDLL(path))
+
+
+def _p(a: np.ndarray | None, t):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(t)
+
+
+@dataclass
+class Cache:
+    """A KV cache in host memory: K and V pools addressed through a block table.
+
+    Position p of sequence b, kv head h is element
+    table[b, p // block_size] * block_stride + h * head_stride + (p % block_size) * row_stride.
+    """
+    k: np.ndarray
+    v: np.ndarray
+    table: np.ndarray          # int32 [B, max_blocks]
+    block_size: int
+    block_stride: int
+    head_stride: int
+    row_stride: int
+    num_blocks: int
+    dtype: int                 # F32 or BF16 (bf16 stored as uint16 bit patterns)
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.table.shape[1])
+
+
+class Oracle:
+    """numpy-facing wrapper of the C oracle."""
+
+    def __init__(self, path: str | None = None):
+        self.lib = load(path)
+
+    def build_tree_mask(self, parents: np.ndarray):
+        parents = np.ascontiguousarray(parents, dtype=np.int32)
+        B, T = parents.shape
+        W = (T + 63) // 64
+        mask = np.zeros((B, T, W), np.uint64)
+        depth = np.zeros((B, T), np.int32)
+        err = np.zeros((B,), np.int32)
+        rc = self.lib.oracle_build_tree_mask(_p(parents, _i32p), B, T, _p(mask, _u64p),
+                                             _p(depth, _i32p), _p(err, _i32p))
+        assert rc == 0
+        return mask, depth, err
+
+    def tree_verify_attention(self, q, k_tree, v_tree, cache: Cache, prefix_len, max_prefix_len,
+                              mask, scale, rows=None, nthreads=0):
+        """q [B,Hq,T,D], k_tree/v_tree [B,Hkv,T,D] (float32, or uint16 bf16 bits).
+
+        Returns out float32 [B,T,Hq,D], or [len(rows), D] when rows (int32 [n,3] of
+        (b, h, i)) is given.
+        """
+        B, Hq, T, D = q.shape
+        Hkv = k_tree.shape[1]
+        prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        mask = np.ascontiguousarray(mask, dtype=np.uint64)
+        if rows is not None:
+            rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
+            out = np.zeros((rows.shape[0], D), np.float32)
+            nrows = rows.shape[0]
+        else:
+            out = np.zeros((B, T, Hq, D), np.float32)
+            nrows = 0
+        for a in (q, k_tree, v_tree, cache.k, cache.v, cache.table):
+            assert a.flags["C_CONTIGUOUS"]
+        rc = self.lib.oracle_tree_verify_attention(
+            q.ctypes.data, k_tree.ctypes.data, v_tree.ctypes.data, cache.k.ctypes.data,
+            cache.v.ctypes.data, _p(cache.table, _i32p), cache.block_size, cache.max_blocks,
+            cache.block_stride, cache.head_stride, cache.row_stride, cache.num_blocks,
+            cache.dtype, _p(prefix_len, _i32p), int(max_prefix_len), _p(mask, _u64p), B, Hq,
+            Hkv, T, D, float(scale), _p(rows, _i32p), nrows, _p(out, _f32p), int(nthreads))
+        assert rc == 0, rc
+        return out
+
+    def argmax(self, logits: np.ndarray, nthreads: int = 0):
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        V = logits.shape[-1]
+        flat = logits.reshape(-1, V)
+        out = np.zeros((flat.shape[0],), np.int32)
+        rc = self.lib.oracle_argmax(_p(flat, _f32p), flat.shape[0], V, _p(out, _i32p),
+                                    int(nthreads))
+        assert rc == 0
+        return out.reshape(logits.shape[:-1])
+
+    def accept_longest_path(self, logits, draft, parents, tree_err=None):
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        draft = np.ascontiguousarray(draft, dtype=np.int32)
+        parents = np.ascontiguousarray(parents, dtype=np.int32)
+        B, T = parents.shape
+        V = logits.shape[-1]
+        if tree_err is not None:
+            tree_err = np.ascontiguousarray(tree_err, dtype=np.int32)
+        am = np.zeros((B, T), np.int32)
+        L = np.zeros((B,), np.int32)
+        nodes = np.zeros((B, T), np.int32)
+        toks = np.zeros((B, T), np.int32)
+        rc = self.lib.oracle_accept_longest_path(
+            _p(logits, _f32p), _p(draft, _i32p), _p(parents, _i32p), _p(tree_err, _i32p), B, T,
+            V, _p(am, _i32p), _p(L, _i32p), _p(nodes, _i32p), _p(toks, _i32p))
+        assert rc == 0
+        return am, L, nodes, toks
+
+    def kv_commit(self, k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: Cache,
+                  prefix_len, max_prefix_len, new_prefix_len=True):
+        """Commits in place into cache.k / cache.v; returns new_prefix_len (or None)."""
+        B, Hkv, T, D = k_tree.shape
+        accepted_len = np.ascontiguousarray(accepted_len, dtype=np.int32)
+        accepted_nodes = np.ascontiguousarray(accepted_nodes, dtype=np.int32)
+        prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        if tree_err is not None:
+            tree_err = np.ascontiguousarray(tree_err, dtype=np.int32)
+        npl = np.zeros((B,), np.int32) if new_prefix_len else None
+        rc = self.lib.oracle_kv_commit(
+            k_tree.ctypes.data, v_tree.ctypes.data, _p(accepted_len, _i32p),
+            _p(accepted_nodes, _i32p), _p(tree_err, _i32p), cache.k.ctypes.data,
+            cache.v.ctypes.data, _p(cache.table, _i32p), cache.block_size, cache.max_blocks,
+            cache.block_stride, cache.head_stride, cache.row_stride, cache.num_blocks,
+            cache.dtype, _p(prefix_len, _i32p), int(max_prefix_len), _p(npl, _i32p), B, Hkv, T,
+            D)
+        assert rc == 0
+        return npl

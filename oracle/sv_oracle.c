@@ -1,0 +1,358 @@
+/*
+ * sv_oracle.c -- plain CPU oracle for the tree-masked speculative verify step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct reference the
+ * GPU library is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it; no product code path calls it.  It
+ * shares no code, header, table or constant with the GPU library: its enums,
+ * its bf16 decoding and its cache addressing are all written out here.
+ *
+ * Floating point is fp64 throughout (inputs are widened exactly from fp32 or
+ * bf16); results are narrowed to fp32 with round-to-nearest-even at the end.
+ * No blocking, fusion or reordering: each function follows the definition it
+ * cites, loop by loop.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [ADR]  "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status
+ *         table rows E1.1-E1.5 (tree attention parity ladder, output layout
+ *         [q_seq_len, num_heads, head_dim]), E4a (build_tree_mask from the
+ *         parent array), E4b.10a (smaller token wins ties), E5a (tree-walk
+ *         accept), E6 v2 (mask selects ancestors + self); section 4 Phase E1
+ *         (dynamic tree mask, apply_tree_attention) and Phase E5 (longest
+ *         matching path from root; full accept picks the deepest).
+ *  [HEADS] "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs):
+ *         "Why bother" (greedy verify accepts the longest matching argmax
+ *         prefix), "What's not implemented" item 1(c) (each tree node attends
+ *         only to its ancestors).
+ *  [ANE]  "Speculative decoding verify batches to amortize ANE dispatch"
+ *         (llms-explorer): Facts on the commit rule (argmax decides, longest
+ *         matching prefix plus one bonus token, accept(k) commits only the
+ *         accepted prefix) and on delayed KV write-through.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC sv_oracle.c -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Per-sequence tree status codes (oracle's own numbering). */
+enum { OR_TREE_OK = 0, OR_TREE_BAD_ROOT = 1, OR_TREE_BAD_PARENT = 2 };
+/* Element types of Q/K/V and the cache. */
+enum { OR_F32 = 0, OR_BF16 = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* Tree validity.  Reading: node 0 is the root (parent -1) and every other    */
+/* node's parent precedes it (0 <= parent[i] < i), the order a best-first     */
+/* expansion admits nodes in ([ADR] E4a).                                      */
+static int tree_status(const int32_t *par, int T) {
+    if (par[0] != -1) return OR_TREE_BAD_ROOT;
+    for (int i = 1; i < T; ++i)
+        if (par[i] < 0 || par[i] >= i) return OR_TREE_BAD_PARENT;
+    return OR_TREE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Mask ([ADR] E4a build_tree_mask, E6 v2 "ancestors + self"; [HEADS] item    */
+/* 1(c)).  Row i has bit j set iff node j is node i or one of its ancestors.  */
+/* depth[i] = number of proper ancestors (root 0).  A malformed parent array  */
+/* sets tree_err[b] and leaves every row self-only with depth 0.             */
+int oracle_build_tree_mask(const int32_t *parents, int B, int T, uint64_t *mask,
+                           int32_t *depth, int32_t *tree_err) {
+    if (B < 0 || T < 1) return -1;
+    const int W = (T + 63) / 64;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * T;
+        const int st = tree_status(par, T);
+        tree_err[b] = st;
+        for (int i = 0; i < T; ++i) {
+            uint64_t *row = mask + ((int64_t)b * T + i) * W;
+            for (int w = 0; w < W; ++w) row[w] = 0;
+            int steps = 0;
+            if (st != OR_TREE_OK) {
+                row[i / 64] |= (uint64_t)1 << (i % 64);
+            } else {
+                int j = i;
+                while (j != -1) {             /* walk to the root */
+                    row[j / 64] |= (uint64_t)1 << (j % 64);
+                    j = par[j];
+                    ++steps;
+                }
+                steps -= 1;                   /* self is not an ancestor */
+            }
+            if (depth) depth[(int64_t)b * T + i] = steps;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+static double elem(const void *base, int dtype, int64_t idx) {
+    if (dtype == OR_F32) return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;  /* bf16 = top half of fp32 */
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Cache addressing: position pos of sequence b, kv head h lives in block
+ * table[b][pos / bs] at slot pos % bs.  Returns the element offset of the row,
+ * or -1 when the table entry is outside [0, num_blocks). */
+static int64_t cache_row(const int32_t *table, int bs, int max_blocks, int64_t block_stride,
+                         int64_t head_stride, int64_t row_stride, int64_t num_blocks,
+                         int b, int h, int64_t pos) {
+    const int32_t blk = table[(int64_t)b * max_blocks + pos / bs];
+    if (blk < 0 || blk >= num_blocks) return -1;
+    return (int64_t)blk * block_stride + (int64_t)h * head_stride + (pos % bs) * row_stride;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention ([ADR] E1.1-E1.5 and section 4 Phase E1; [HEADS] item 1(c)).     */
+/* For query row (b, h, i): kv head = h / (Hq/Hkv); keys are the P_b cached   */
+/* prefix rows of that kv head in position order, then the tree rows j whose  */
+/* mask bit is set in row i, in increasing j.  s = scale * <q, k>;            */
+/* O = sum_k exp(s_k - max s) v_k / sum_k exp(s_k - max s), in fp64, stored   */
+/* as fp32 at out[b][i][h][:] (layout [q_seq_len, num_heads, head_dim]).      */
+/* P_b is clamped into [0, max_prefix_len]; prefix keys whose block-table     */
+/* entry is out of range are left out.                                        */
+/* rows: optional list of (b, h, i) triples; then out is [nrows][D].          */
+static void attend_one(const void *q, const void *k_tree, const void *v_tree,
+                       const void *k_cache, const void *v_cache, const int32_t *table, int bs,
+                       int max_blocks, int64_t block_stride, int64_t head_stride,
+                       int64_t row_stride, int64_t num_blocks, int dtype,
+                       const int32_t *prefix_len, int max_prefix_len, const uint64_t *mask,
+                       int Hq, int Hkv, int T, int D, double scale, int b, int h, int i,
+                       double *s, const void **vsrc, int64_t *voff, double *num, float *dst) {
+    const int W = (T + 63) / 64;
+    const int G = Hq / Hkv;
+    const int kvh = h / G;
+    int64_t P = prefix_len[b];
+    if (P < 0) P = 0;
+    if (P > max_prefix_len) P = max_prefix_len;
+    const int64_t qoff = (((int64_t)b * Hq + h) * T + i) * D;
+
+    int64_t n = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        const int64_t off = cache_row(table, bs, max_blocks, block_stride, head_stride,
+                                      row_stride, num_blocks, b, kvh, p);
+        if (off < 0) continue;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += elem(q, dtype, qoff + d) * elem(k_cache, dtype, off + d);
+        s[n] = scale * dot;
+        vsrc[n] = v_cache;
+        voff[n] = off;
+        ++n;
+    }
+    const uint64_t *mrow = mask + ((int64_t)b * T + i) * W;
+    for (int j = 0; j < T; ++j) {
+        if (!((mrow[j / 64] >> (j % 64)) & 1)) continue;
+        const int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += elem(q, dtype, qoff + d) * elem(k_tree, dtype, off + d);
+        s[n] = scale * dot;
+        vsrc[n] = v_tree;
+        voff[n] = off;
+        ++n;
+    }
+    double m = -INFINITY;
+    for (int64_t k = 0; k < n; ++k)
+        if (s[k] > m) m = s[k];
+    double den = 0.0;
+    for (int d = 0; d < D; ++d) num[d] = 0.0;
+    for (int64_t k = 0; k < n; ++k) {
+        const double w = exp(s[k] - m);
+        den += w;
+        for (int d = 0; d < D; ++d) num[d] += w * elem(vsrc[k], dtype, voff[k] + d);
+    }
+    for (int d = 0; d < D; ++d) dst[d] = (float)(num[d] / den);
+}
+
+int oracle_tree_verify_attention(const void *q, const void *k_tree, const void *v_tree,
+                                 const void *k_cache, const void *v_cache, const int32_t *table,
+                                 int bs, int max_blocks, int64_t block_stride, int64_t head_stride,
+                                 int64_t row_stride, int64_t num_blocks, int dtype,
+                                 const int32_t *prefix_len, int max_prefix_len,
+                                 const uint64_t *mask, int B, int Hq, int Hkv, int T, int D,
+                                 double scale, const int32_t *rows, int64_t nrows, float *out,
+                                 int nthreads) {
+    if (Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || T < 1 || D < 1 || B < 0) return -1;
+    const int64_t total = rows ? nrows : (int64_t)B * Hq * T;
+    const int64_t maxkeys = (int64_t)max_prefix_len + T;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+        const void **vsrc = (const void **)malloc(sizeof(void *) * (size_t)maxkeys);
+        int64_t *voff = (int64_t *)malloc(sizeof(int64_t) * (size_t)maxkeys);
+        double *num = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!s || !vsrc || !voff || !num) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < total; ++r) {
+                int b, h, i;
+                float *dst;
+                if (rows) {
+                    b = rows[3 * r];
+                    h = rows[3 * r + 1];
+                    i = rows[3 * r + 2];
+                    dst = out + r * D;
+                } else {
+                    b = (int)(r / ((int64_t)Hq * T));
+                    h = (int)((r / T) % Hq);
+                    i = (int)(r % T);
+                    dst = out + (((int64_t)b * T + i) * Hq + h) * D;
+                }
+                attend_one(q, k_tree, v_tree, k_cache, v_cache, table, bs, max_blocks,
+                           block_stride, head_stride, row_stride, num_blocks, dtype, prefix_len,
+                           max_prefix_len, mask, Hq, Hkv, T, D, scale, b, h, i, s, vsrc, voff,
+                           num, dst);
+            }
+        }
+        free(s);
+        free(vsrc);
+        free(voff);
+        free(num);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Argmax over the vocabulary ([ANE] commit rule: the target's argmax at each  */
+/* row decides).  The smallest index holding the maximum wins ties ([ADR]     */
+/* E4b.10a: smaller token wins).  NaN entries never win; an all-NaN row gives */
+/* index 0.                                                                   */
+static int32_t argmax_row(const float *x, int64_t V) {
+    int64_t best = -1;
+    float bv = 0.0f;
+    for (int64_t v = 0; v < V; ++v) {
+        if (isnan(x[v])) continue;
+        if (best < 0 || x[v] > bv) {  /* strict: an equal later value does not replace */
+            best = v;
+            bv = x[v];
+        }
+    }
+    return best < 0 ? 0 : (int32_t)best;
+}
+
+int oracle_argmax(const float *logits, int64_t R, int64_t V, int32_t *out, int nthreads) {
+    if (R < 0 || V < 1) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) out[r] = argmax_row(logits + r * V, V);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Greedy acceptance ([ADR] E5a and Phase E5; [HEADS] "Why bother"; [ANE]     */
+/* commit rule).  a[i] = argmax of row i.  Node 0 (the root) is always        */
+/* accepted; node i >= 1 matches when its parent matches and its draft token  */
+/* equals the parent's argmax.  The accepted node is the deepest matching     */
+/* node (smallest index among equals); the path is root..that node,           */
+/* L = its depth + 1, and the emitted tokens are a[] along the path (the last */
+/* is the bonus / correction token).  An invalid tree (tree_err != 0 or a     */
+/* malformed parent array) accepts nothing: L = 0, path and tokens -1.        */
+int oracle_accept_longest_path(const float *logits, const int32_t *draft, const int32_t *parents,
+                               const int32_t *tree_err, int B, int T, int64_t V,
+                               int32_t *argmax_out, int32_t *accepted_len,
+                               int32_t *accepted_nodes, int32_t *out_tokens) {
+    if (B < 0 || T < 1 || V < 1) return -1;
+    int32_t *a = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    int32_t *dep = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    unsigned char *match = (unsigned char *)malloc((size_t)T);
+    int32_t *path = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    if (!a || !dep || !match || !path) {
+        free(a); free(dep); free(match); free(path);
+        return -2;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * T;
+        const int32_t *drf = draft + (int64_t)b * T;
+        for (int i = 0; i < T; ++i) a[i] = argmax_row(logits + ((int64_t)b * T + i) * V, V);
+        if (argmax_out)
+            for (int i = 0; i < T; ++i) argmax_out[(int64_t)b * T + i] = a[i];
+        int32_t *nodes = accepted_nodes + (int64_t)b * T;
+        int32_t *toks = out_tokens + (int64_t)b * T;
+        for (int j = 0; j < T; ++j) nodes[j] = toks[j] = -1;
+        const int invalid = (tree_err && tree_err[b] != 0) || tree_status(par, T) != OR_TREE_OK;
+        if (invalid) {
+            accepted_len[b] = 0;
+            continue;
+        }
+        match[0] = 1;
+        dep[0] = 0;
+        for (int i = 1; i < T; ++i) {
+            dep[i] = dep[par[i]] + 1;
+            match[i] = match[par[i]] && drf[i] == a[par[i]];
+        }
+        int best = 0;
+        for (int i = 1; i < T; ++i)
+            if (match[i] && dep[i] > dep[best]) best = i;
+        const int L = dep[best] + 1;
+        for (int j = L - 1, n = best; j >= 0; --j, n = par[n]) path[j] = n;
+        for (int j = 0; j < L; ++j) {
+            nodes[j] = path[j];
+            toks[j] = a[path[j]];
+        }
+        accepted_len[b] = L;
+    }
+    free(a); free(dep); free(match); free(path);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Delayed KV write-through ([ANE] Facts: accept(k) commits only the accepted */
+/* prefix; rejected drafts never touch the cache).  For each sequence with a  */
+/* valid tree: cache row prefix_len[b] + j of every kv head receives tree row */
+/* accepted_nodes[b][j] (K and V, byte copy), j < accepted_len[b]; then       */
+/* new_prefix_len[b] = prefix_len[b] + accepted_len[b].  A sequence whose     */
+/* request cannot be honoured in full (prefix_len outside                      */
+/* [0, max_prefix_len], rows past capacity, a node index outside [0, T), a    */
+/* block-table entry out of range) is left untouched and keeps its length.    */
+int oracle_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
+                     const int32_t *accepted_nodes, const int32_t *tree_err, void *k_cache,
+                     void *v_cache, const int32_t *table, int bs, int max_blocks,
+                     int64_t block_stride, int64_t head_stride, int64_t row_stride,
+                     int64_t num_blocks, int dtype, const int32_t *prefix_len, int max_prefix_len,
+                     int32_t *new_prefix_len, int B, int Hkv, int T, int D) {
+    if (B < 0 || Hkv < 1 || T < 1 || D < 1 || bs < 1 || max_blocks < 1) return -1;
+    const size_t esz = dtype == OR_F32 ? 4 : 2;
+    const int64_t cap = (int64_t)max_blocks * bs;
+    for (int b = 0; b < B; ++b) {
+        const int32_t P = prefix_len[b];
+        const int32_t L = accepted_len[b];
+        const int32_t *nodes = accepted_nodes + (int64_t)b * T;
+        int ok = !(tree_err && tree_err[b] != 0);
+        ok = ok && L >= 0 && L <= T && P >= 0 && P <= max_prefix_len && (int64_t)P + L <= cap;
+        for (int j = 0; ok && j < L; ++j) {
+            if (nodes[j] < 0 || nodes[j] >= T) ok = 0;
+            else if (cache_row(table, bs, max_blocks, block_stride, head_stride, row_stride,
+                               num_blocks, b, 0, (int64_t)P + j) < 0) ok = 0;
+        }
+        if (ok) {
+            for (int h = 0; h < Hkv; ++h)
+                for (int j = 0; j < L; ++j) {
+                    const int64_t dst = cache_row(table, bs, max_blocks, block_stride, head_stride,
+                                                  row_stride, num_blocks, b, h, (int64_t)P + j);
+                    const int64_t src = (((int64_t)b * Hkv + h) * T + nodes[j]) * D;
+                    memcpy((char *)k_cache + dst * esz, (const char *)k_tree + src * esz, esz * D);
+                    memcpy((char *)v_cache + dst * esz, (const char *)v_tree + src * esz, esz * D);
+                }
+        }
+        if (new_prefix_len) new_prefix_len[b] = ok ? P + L : P;
+    }
+    return 0;
+}

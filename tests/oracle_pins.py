@@ -1,0 +1,566 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with: values printed on the pages (golden files), hand-derived worked
+examples, closed forms, library routines that compute a special case (torch
+scaled_dot_product_attention in fp64, numpy argmax / nanargmax), brute force on
+tiny inputs, or invariants.  ``tests/test_oracle_pins.py`` runs them against the
+real oracle; ``tests/test_oracle_mutants.py`` runs them against deliberately
+broken copies of it, each of which must fail at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from _support import as_f64, gather_prefix, to_np
+import oracle as O
+from tree_masked_verify_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# =========================================================================== helpers
+def closure_mask(parents: np.ndarray) -> np.ndarray:
+    """Ancestor-or-self relation by transitive closure of the parent relation
+    (boolean matrix powers), as bool [T, T]: R[i, j] = j is i or an ancestor of i."""
+    T = len(parents)
+    A = np.zeros((T, T), dtype=bool)
+    for i, p in enumerate(parents):
+        if p >= 0:
+            A[i, p] = True
+    R = np.eye(T, dtype=bool) | A
+    for _ in range(int(math.ceil(math.log2(max(T, 2)))) + 1):
+        R = R | ((R.astype(np.int64) @ R.astype(np.int64)) > 0)
+    return R
+
+
+def bits_of(mask_row: np.ndarray, T: int) -> np.ndarray:
+    out = np.zeros(T, dtype=bool)
+    for j in range(T):
+        out[j] = (int(mask_row[j // 64]) >> (j % 64)) & 1
+    return out
+
+
+def small_inputs(name: str, seed: int, **kw) -> wl.Inputs:
+    w = wl.scaled(wl.WORKLOADS[name], **kw)
+    return wl.make_inputs(w, seed=seed, device="cpu")
+
+
+def contiguous_cache(kc: np.ndarray, vc: np.ndarray, dtype: int) -> O.Cache:
+    """kc, vc [B, Hkv, cap, D] -> Cache with one block per sequence."""
+    B, Hkv, cap, D = kc.shape
+    table = np.arange(B, dtype=np.int32).reshape(B, 1)
+    return O.Cache(k=np.ascontiguousarray(kc), v=np.ascontiguousarray(vc), table=table,
+                   block_size=cap, block_stride=Hkv * cap * D, head_stride=cap * D,
+                   row_stride=D, num_blocks=B, dtype=dtype)
+
+
+def sdpa_reference(q, kp, vp, kt, vt, allowed, scale):
+    """fp64 torch SDPA for one sequence.  q [Hq,T,D]; kp/vp [Hkv,P,D] prefix;
+    kt/vt [Hkv,T,D] tree; allowed bool [T,T] (tree visibility).  -> [T,Hq,D]."""
+    Hq, T, D = q.shape
+    P = kp.shape[1]
+    k = torch.cat([torch.from_numpy(kp), torch.from_numpy(kt)], dim=1)[None]
+    v = torch.cat([torch.from_numpy(vp), torch.from_numpy(vt)], dim=1)[None]
+    m = torch.cat([torch.ones(T, P, dtype=torch.bool), torch.from_numpy(allowed)], dim=1)
+    o = F.scaled_dot_product_attention(torch.from_numpy(q)[None], k, v, attn_mask=m,
+                                       scale=scale, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()   # [T, Hq, D]
+
+
+def run_attention(orc: O.Oracle, inp: wl.Inputs, mask=None, scale=None, cache=None,
+                  prefix=None):
+    if mask is None:
+        mask, _, _ = orc.build_tree_mask(to_np(inp.parents))
+    cache = cache or _cache(inp)
+    return orc.tree_verify_attention(
+        to_np(inp.q), to_np(inp.k_tree), to_np(inp.v_tree), cache,
+        to_np(inp.prefix_len) if prefix is None else prefix, inp.max_prefix_len, mask,
+        inp.scale if scale is None else scale)
+
+
+def _cache(inp):
+    from _support import oracle_cache
+    return oracle_cache(inp)
+
+
+def check_vs_sdpa(orc, inp, scale=None, atol=2e-6, rtol=2e-6):
+    scale = inp.scale if scale is None else scale
+    out = run_attention(orc, inp, scale=scale)
+    cache = _cache(inp)
+    dt = cache.dtype
+    parents = to_np(inp.parents)
+    P = to_np(inp.prefix_len)
+    q, kt, vt = to_np(inp.q), to_np(inp.k_tree), to_np(inp.v_tree)
+    for b in range(inp.w.B):
+        Hkv = inp.w.Hkv
+        kp = np.stack([gather_prefix(cache, b, h, int(P[b]), "k") for h in range(Hkv)])
+        vp = np.stack([gather_prefix(cache, b, h, int(P[b]), "v") for h in range(Hkv)])
+        ref = sdpa_reference(as_f64(q[b], dt), kp, vp, as_f64(kt[b], dt), as_f64(vt[b], dt),
+                             closure_mask(parents[b]), scale)
+        np.testing.assert_allclose(out[b].astype(np.float64), ref, rtol=rtol, atol=atol)
+
+
+# =========================================================================== mask pins
+def pin_mask_worked_example(orc):
+    with open(os.path.join(GOLDEN, "mask_worked_example.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    parents = np.array([int(x) for x in lines[0][1:]], dtype=np.int32)[None]
+    want_mask = [int(l[1], 16) for l in lines[1:]]
+    want_depth = [int(l[2]) for l in lines[1:]]
+    mask, depth, err = orc.build_tree_mask(parents)
+    assert err[0] == O.TREE_OK
+    assert [int(x) for x in mask[0, :, 0]] == want_mask, mask[0, :, 0]
+    assert list(depth[0]) == want_depth
+
+
+def pin_mask_closed_forms(orc):
+    for T in (1, 2, 7, 63, 64):
+        chain = np.array([wl.chain_tree(T)], dtype=np.int32)
+        mask, depth, err = orc.build_tree_mask(chain)
+        assert err[0] == 0
+        for i in range(T):  # causal: lower triangle including the diagonal
+            assert int(mask[0, i, 0]) == (1 << (i + 1)) - 1, (T, i)
+            assert depth[0, i] == i
+        star = np.array([[-1] + [0] * (T - 1)], dtype=np.int32)
+        mask, depth, err = orc.build_tree_mask(star)
+        assert int(mask[0, 0, 0]) == 1
+        for i in range(1, T):
+            assert int(mask[0, i, 0]) == 1 | (1 << i)
+            assert depth[0, i] == 1
+
+
+def pin_mask_bruteforce(orc):
+    rng = np.random.Generator(np.random.PCG64(11))
+    trees = []
+    for T, lv, ch in ((8, 4, 3), (60, 8, 4), (64, 6, 8), (64, 64, 1), (100, 10, 3)):
+        trees.append(np.array(wl.random_tree(rng, T, lv, ch), dtype=np.int32))
+    trees.append(np.array(wl.eagle2_tree(rng, 64, 6, 8), dtype=np.int32))
+    for par in trees:
+        T = len(par)
+        mask, depth, err = orc.build_tree_mask(par[None])
+        assert err[0] == 0
+        R = closure_mask(par)
+        for i in range(T):
+            assert np.array_equal(bits_of(mask[0, i], T), R[i]), (T, i)
+            assert depth[0, i] == R[i].sum() - 1
+
+
+def pin_mask_invalid(orc):
+    cases = [([0, 0, 1], O.TREE_BAD_ROOT), ([-1, 1, 0], O.TREE_BAD_PARENT),
+             ([-1, 0, 2], O.TREE_BAD_PARENT), ([-1, 0, -1], O.TREE_BAD_PARENT),
+             ([-1, -2, 0], O.TREE_BAD_PARENT), ([-1, 0, 5], O.TREE_BAD_PARENT),
+             ([3, 0, 9], O.TREE_BAD_ROOT)]
+    for par, code in cases:
+        mask, depth, err = orc.build_tree_mask(np.array([par], dtype=np.int32))
+        assert err[0] == code, (par, err)
+        for i in range(3):
+            assert int(mask[0, i, 0]) == 1 << i and depth[0, i] == 0
+    # a bad sequence does not disturb its neighbours
+    par = np.array([[-1, 0, 1], [-1, 2, 0], [-1, 0, 0]], dtype=np.int32)
+    mask, depth, err = orc.build_tree_mask(par)
+    assert list(err) == [0, O.TREE_BAD_PARENT, 0]
+    assert [int(x) for x in mask[0, :, 0]] == [1, 3, 7]
+    assert [int(x) for x in mask[2, :, 0]] == [1, 3, 5]
+
+
+# =========================================================================== attention pins
+def pin_attn_decode_T1(orc):
+    """Tree of one node = ordinary single-token decode over prefix + self."""
+    inp = small_inputs("parity512", 3, T=1, tree="chain", prefix=(37, 37), capacity=64)
+    check_vs_sdpa(orc, inp)
+
+
+def pin_attn_chain_causal(orc):
+    """Chain = causal attention over prefix + chain (torch tril mask)."""
+    inp = small_inputs("parity512", 4, T=8, tree="chain", prefix=(45, 45), capacity=64)
+    out = run_attention(orc, inp)
+    cache = _cache(inp)
+    P = int(inp.max_prefix_len)
+    kp = np.stack([gather_prefix(cache, 0, h, P, "k") for h in range(2)])
+    vp = np.stack([gather_prefix(cache, 0, h, P, "v") for h in range(2)])
+    k = torch.cat([torch.from_numpy(kp), torch.from_numpy(as_f64(to_np(inp.k_tree)[0], 1))], 1)
+    v = torch.cat([torch.from_numpy(vp), torch.from_numpy(as_f64(to_np(inp.v_tree)[0], 1))], 1)
+    causal = torch.ones(8, P + 8, dtype=torch.bool).tril(diagonal=P)
+    q = torch.from_numpy(as_f64(to_np(inp.q)[0], 1))
+    ref = F.scaled_dot_product_attention(q[None], k[None], v[None], attn_mask=causal,
+                                         enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out[0].astype(np.float64), ref, rtol=2e-6, atol=2e-6)
+
+
+def pin_attn_tree_vs_sdpa(orc):
+    """Random trees, GQA, paged shuffled cache, explicit scale; fp32 and bf16."""
+    check_vs_sdpa(orc, small_inputs("parity512", 5, prefix=(0, 90), B=3))
+    check_vs_sdpa(orc, small_inputs("long32k", 6, B=2, prefix=(33, 70), T=21, Hq=8, Hkv=2, V=1000,
+                                    max_levels=5), scale=0.3)
+    check_vs_sdpa(orc, small_inputs("tiny", 7, Hq=4, Hkv=2, D=64))
+    check_vs_sdpa(orc, small_inputs("chain2k", 8, prefix=(20, 20), capacity=32, D=96, V=1000))
+
+
+def pin_attn_prefix_zero(orc):
+    check_vs_sdpa(orc, small_inputs("parity512", 9, prefix=(0, 0), capacity=16))
+
+
+def pin_attn_closed_forms(orc):
+    """Constant V -> O = V; equal keys -> O = mean of the visible V rows, which
+    also fixes the [node, head, dim] output layout and the head -> kv-head map."""
+    inp = small_inputs("long32k", 12, B=2, prefix=(5, 19), T=9, Hq=6, Hkv=3, D=32,
+                       max_levels=4, dtype="f32", block_size=4)
+    w = inp.w
+    parents = to_np(inp.parents)
+    cache = _cache(inp)
+    P = to_np(inp.prefix_len)
+    q = to_np(inp.q)
+    kt = np.zeros_like(to_np(inp.k_tree))
+    # V rows encode (kv head, position): cache row p of kv head h -> 1000*h + p, tree
+    # row j -> 1000*h + 500 + j, repeated along D.
+    vt = np.zeros_like(kt)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            vt[b, h, :, :] = (1000 * h + 500 + np.arange(w.T))[:, None]
+    kpool = np.zeros_like(cache.k)
+    vpool = np.zeros_like(cache.v)
+    for b in range(w.B):
+        for p in range(int(P[b]) + w.T):
+            blk = cache.table[b, p // cache.block_size]
+            for h in range(w.Hkv):
+                vpool[blk, h, p % cache.block_size, :] = 1000 * h + p
+    c2 = O.Cache(k=kpool, v=vpool, table=cache.table, block_size=cache.block_size,
+                 block_stride=cache.block_stride, head_stride=cache.head_stride,
+                 row_stride=cache.row_stride, num_blocks=cache.num_blocks, dtype=O.F32)
+    mask, _, _ = orc.build_tree_mask(parents)
+    out = orc.tree_verify_attention(q, kt, vt, c2, P, inp.max_prefix_len, mask, 0.7)
+    G = w.Hq // w.Hkv
+    for b in range(w.B):
+        R = closure_mask(parents[b])
+        for i in range(w.T):
+            for h in range(w.Hq):
+                kvh = h // G
+                vals = [1000 * kvh + p for p in range(int(P[b]))]
+                vals += [1000 * kvh + 500 + j for j in range(w.T) if R[i, j]]
+                want = np.float32(np.mean(np.array(vals, dtype=np.float64)))
+                assert np.all(out[b, i, h] == want), (b, i, h, out[b, i, h, 0], want)
+    # constant V: output equals that constant whatever Q and K are
+    out = orc.tree_verify_attention(q, to_np(inp.k_tree), np.full_like(vt, 2.5), O.Cache(
+        k=cache.k, v=np.full_like(cache.v, 2.5), table=cache.table,
+        block_size=cache.block_size, block_stride=cache.block_stride,
+        head_stride=cache.head_stride, row_stride=cache.row_stride,
+        num_blocks=cache.num_blocks, dtype=O.F32), P, inp.max_prefix_len, mask, inp.scale)
+    np.testing.assert_allclose(out, 2.5, rtol=1e-6)
+
+
+def pin_attn_paged_equals_contiguous(orc):
+    """The same rows laid out paged (shuffled blocks) or contiguous give identical bits."""
+    inp = small_inputs("batched8k", 13, B=3, prefix=(10, 77), T=12, Hq=4, Hkv=2, D=64)
+    paged = _cache(inp)
+    P = to_np(inp.prefix_len)
+    cap = int(P.max()) + inp.w.T
+    B, Hkv, D = inp.w.B, inp.w.Hkv, inp.w.D
+    kc = np.zeros((B, Hkv, cap, D), dtype=paged.k.dtype)
+    vc = np.zeros_like(kc)
+    pool4k = paged.k.reshape(paged.num_blocks, Hkv, paged.block_size, D)
+    pool4v = paged.v.reshape(paged.num_blocks, Hkv, paged.block_size, D)
+    for b in range(B):
+        for p in range(int(P[b])):
+            blk = paged.table[b, p // paged.block_size]
+            kc[b, :, p] = pool4k[blk, :, p % paged.block_size]
+            vc[b, :, p] = pool4v[blk, :, p % paged.block_size]
+    a = run_attention(orc, inp)
+    c = run_attention(orc, inp, cache=contiguous_cache(kc, vc, paged.dtype))
+    assert np.array_equal(a, c)
+
+
+def pin_attn_bad_block_entry(orc):
+    """A prefix block whose table entry is out of range drops exactly its rows."""
+    inp = small_inputs("batched8k", 14, B=1, prefix=(70, 70), T=5, Hq=2, Hkv=1, D=32,
+                       max_levels=3)
+    cache = _cache(inp)
+    table = cache.table.copy()
+    table[0, 2] = -1                       # positions 32..47
+    c_bad = O.Cache(**{**cache.__dict__, "table": table})
+    out = run_attention(orc, inp, cache=c_bad)
+    keep = [p for p in range(70) if not (32 <= p < 48)]
+    kp = np.stack([gather_prefix(cache, 0, 0, 70, "k")[keep]])
+    vp = np.stack([gather_prefix(cache, 0, 0, 70, "v")[keep]])
+    ref = sdpa_reference(as_f64(to_np(inp.q)[0], 1), kp, vp, as_f64(to_np(inp.k_tree)[0], 1),
+                         as_f64(to_np(inp.v_tree)[0], 1), closure_mask(to_np(inp.parents)[0]),
+                         inp.scale)
+    np.testing.assert_allclose(out[0].astype(np.float64), ref, rtol=2e-6, atol=2e-6)
+
+
+def pin_attn_chain_equals_serial(orc):
+    """A chain verified as one tree equals T serial one-node verifies, each followed
+    by a commit of its root (bit for bit: the same keys in the same order)."""
+    inp = small_inputs("chain2k", 15, prefix=(50, 50), capacity=64, D=64, Hq=4)
+    w = inp.w
+    chain = run_attention(orc, inp)
+    cache = _cache(inp)
+    q, kt, vt = to_np(inp.q), to_np(inp.k_tree), to_np(inp.v_tree)
+    P = to_np(inp.prefix_len).copy()
+    one = np.array([[-1]], dtype=np.int32)
+    m1, _, e1 = orc.build_tree_mask(one)
+    for i in range(w.T):
+        qi = np.ascontiguousarray(q[:, :, i:i + 1])
+        ki = np.ascontiguousarray(kt[:, :, i:i + 1])
+        vi = np.ascontiguousarray(vt[:, :, i:i + 1])
+        o = orc.tree_verify_attention(qi, ki, vi, cache, P, int(P.max()), m1, inp.scale)
+        assert np.array_equal(o[0, 0], chain[0, i]), i
+        P = orc.kv_commit(ki, vi, np.array([1], np.int32), np.array([[0]], np.int32), e1, cache,
+                          P, int(P.max()))
+
+
+# =========================================================================== argmax pins
+def pin_argmax_numpy(orc):
+    rng = np.random.Generator(np.random.PCG64(21))
+    x = rng.standard_normal((64, 1000)).astype(np.float32)
+    assert np.array_equal(orc.argmax(x), np.argmax(x, axis=1))
+    # ties: small integer-valued rows have repeated maxima; numpy returns the first
+    y = rng.integers(0, 5, size=(200, 37)).astype(np.float32)
+    assert np.array_equal(orc.argmax(y), np.argmax(y, axis=1))
+
+
+def pin_argmax_special_values(orc):
+    rng = np.random.Generator(np.random.PCG64(22))
+    x = rng.integers(-3, 3, size=(300, 50)).astype(np.float32)
+    x[rng.random(x.shape) < 0.2] = np.nan
+    x[5, :] = np.nan
+    want = np.array([np.nanargmax(r) if not np.all(np.isnan(r)) else 0 for r in x])
+    assert np.array_equal(orc.argmax(x), want)
+    z = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0], [-np.inf, -np.inf, -np.inf],
+                  [np.nan, np.inf, np.inf], [np.nan, -np.inf, np.nan]], dtype=np.float32)
+    assert list(orc.argmax(z)) == [0, 0, 0, 1, 1]
+
+
+def pin_argmax_planted(orc):
+    """The generator draws each row's maximum position first; the oracle finds it."""
+    gen = torch.Generator().manual_seed(5)
+    x, pos = wl.planted_max_logits(40, 5000, 2.0, gen, torch.device("cpu"))
+    assert np.array_equal(orc.argmax(x.numpy()), pos.numpy())
+
+
+# =========================================================================== accept pins
+def brute_force_accept(logits, draft, parents):
+    """Enumerate every root path; keep those whose every edge matches; the longest
+    wins, ties to the smallest end node."""
+    T = len(parents)
+    a = np.argmax(logits, axis=1)
+    best = None
+    for end in range(T):
+        path, n = [], end
+        while n != -1:
+            path.append(n)
+            n = parents[n]
+        path = path[::-1]
+        if all(draft[path[k]] == a[path[k - 1]] for k in range(1, len(path))):
+            if best is None or len(path) > len(best):
+                best = path
+    return a, best
+
+
+def pin_accept_bruteforce(orc):
+    rng = np.random.Generator(np.random.PCG64(31))
+    for trial in range(60):
+        T = int(rng.integers(1, 20))
+        V = int(rng.integers(2, 6))
+        # random recursive tree: node i picks any earlier node as parent
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, T)], dtype=np.int32)
+        logits = rng.standard_normal((T, V)).astype(np.float32)
+        draft = rng.integers(0, V, size=T).astype(np.int32)
+        am, L, nodes, toks = orc.accept_longest_path(logits[None], draft[None], par[None])
+        a, path = brute_force_accept(logits, draft, par)
+        assert np.array_equal(am[0], a)
+        assert L[0] == len(path), (trial, L[0], path)
+        assert list(nodes[0, :L[0]]) == path
+        assert list(toks[0, :L[0]]) == [a[n] for n in path]
+        assert np.all(nodes[0, L[0]:] == -1) and np.all(toks[0, L[0]:] == -1)
+
+
+def pin_accept_edge_cases(orc):
+    T, V = 6, 10
+    par = np.array([wl.chain_tree(T)], dtype=np.int32)
+    logits = np.zeros((1, T, V), np.float32)
+    for i in range(T):
+        logits[0, i, (3 * i + 1) % V] = 1.0          # argmax of row i = (3i+1) % V
+    a = [(3 * i + 1) % V for i in range(T)]
+    full = np.array([[7] + [a[i - 1] for i in range(1, T)]], np.int32)
+    _, L, nodes, toks = orc.accept_longest_path(logits, full, par)
+    assert L[0] == T and list(nodes[0]) == list(range(T)) and list(toks[0]) == a
+    none = full.copy()
+    none[0, 1] = (a[0] + 1) % V
+    _, L, nodes, toks = orc.accept_longest_path(logits, none, par)
+    assert L[0] == 1 and nodes[0, 0] == 0 and toks[0, 0] == a[0]
+    assert np.all(nodes[0, 1:] == -1)
+    # the anchor's own draft token is never read
+    for d0 in (0, 5, -9, 10 ** 6):
+        f2 = full.copy()
+        f2[0, 0] = d0
+        assert orc.accept_longest_path(logits, f2, par)[1][0] == T
+    # invalid tree (given or detected) accepts nothing
+    _, L, nodes, toks = orc.accept_longest_path(logits, full, par, np.array([2], np.int32))
+    assert L[0] == 0 and np.all(nodes == -1) and np.all(toks == -1)
+    bad = par.copy()
+    bad[0, 3] = 4
+    _, L, _, _ = orc.accept_longest_path(logits, full, bad)
+    assert L[0] == 0
+    # duplicate sibling tokens: the longest matching path wins, not the first match
+    par = np.array([[-1, 0, 0, 2]], np.int32)
+    lg = np.zeros((1, 4, 4), np.float32)
+    lg[0, :, 1] = 1.0                                 # every argmax is 1
+    drf = np.array([[0, 1, 1, 1]], np.int32)
+    _, L, nodes, _ = orc.accept_longest_path(lg, drf, par)
+    assert L[0] == 3 and list(nodes[0, :3]) == [0, 2, 3]
+    # T = 1: the root alone, its argmax is the bonus token
+    _, L, nodes, toks = orc.accept_longest_path(lg[:, :1], drf[:, :1], par[:, :1])
+    assert L[0] == 1 and nodes[0, 0] == 0 and toks[0, 0] == 1
+
+
+def _monte_carlo_chain(orc, K, p, n, seed):
+    """Chain of K drafts; each draft equals its parent's argmax with probability
+    exactly p (else one of the other V-1 tokens)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, V = K + 1, 4
+    top = rng.integers(0, V, size=(n, T))
+    logits = np.zeros((n, T, V), np.float32)
+    logits[np.arange(n)[:, None], np.arange(T)[None], top] = 1.0
+    hit = rng.random((n, T)) < p
+    other = (top + rng.integers(1, V, size=(n, T))) % V
+    draft = np.zeros((n, T), np.int32)
+    draft[:, 1:] = np.where(hit[:, 1:], top[:, :-1], other[:, :-1])
+    par = np.tile(np.array(wl.chain_tree(T), np.int32), (n, 1))
+    _, L, _, _ = orc.accept_longest_path(logits, draft, par)
+    return L.astype(np.float64)
+
+
+def pin_accept_expected_tokens_golden(orc):
+    with open(os.path.join(GOLDEN, "expected_tokens_per_burst.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for K, p, printed in rows:
+        K, p, printed = int(K), float(p), float(printed)
+        L = _monte_carlo_chain(orc, K, p, 400_000, seed=int(p * 100))
+        sigma = L.std() / math.sqrt(len(L))
+        assert abs(L.mean() - printed) <= 0.005 + 5 * sigma, (K, p, L.mean(), printed)
+
+
+def pin_accept_expected_tokens_closed_form(orc):
+    """Generalised chain: E[L] = sum_{k=0..K} p^k (K=7, p=0.5 -> 1.9921875)."""
+    for K, p in ((7, 0.5), (1, 0.8), (5, 0.9)):
+        L = _monte_carlo_chain(orc, K, p, 200_000, seed=K * 7 + int(10 * p))
+        want = sum(p ** k for k in range(K + 1))
+        sigma = L.std() / math.sqrt(len(L))
+        assert abs(L.mean() - want) <= 5 * sigma + 1e-9, (K, p, L.mean(), want)
+
+
+# =========================================================================== commit pins
+def _commit_case(orc, name, seed, **kw):
+    inp = small_inputs(name, seed, **kw)
+    parents = to_np(inp.parents)
+    mask, _, err = orc.build_tree_mask(parents)
+    _, L, nodes, _ = orc.accept_longest_path(to_np(inp.logits), to_np(inp.draft), parents, err)
+    return inp, err, L, nodes
+
+
+def check_commit_invariants(orc, inp, err, L, nodes):
+    cache = _cache(inp)
+    k0, v0 = cache.k.copy(), cache.v.copy()
+    P = to_np(inp.prefix_len)
+    npl = orc.kv_commit(to_np(inp.k_tree), to_np(inp.v_tree), L, nodes, err, cache, P,
+                        inp.max_prefix_len)
+    w = inp.w
+    bs = cache.block_size
+    kt, vt = to_np(inp.k_tree), to_np(inp.v_tree)
+    k4 = lambda a: a.reshape(cache.num_blocks, w.Hkv, bs, w.D)
+    expect_k, expect_v = k4(k0.copy()), k4(v0.copy())
+    for b in range(w.B):
+        if err[b] != 0:
+            assert npl[b] == P[b]
+            continue
+        assert npl[b] == P[b] + L[b]
+        for j in range(L[b]):
+            pos = P[b] + j
+            blk = cache.table[b, pos // bs]
+            expect_k[blk, :, pos % bs] = kt[b, :, nodes[b, j]]
+            expect_v[blk, :, pos % bs] = vt[b, :, nodes[b, j]]
+    assert np.array_equal(k4(cache.k), expect_k)
+    assert np.array_equal(k4(cache.v), expect_v)
+    changed = np.any(k4(cache.k) != k4(k0), axis=-1).sum()
+    assert changed <= int(sum(L[b] for b in range(w.B) if err[b] == 0)) * w.Hkv
+    return cache, npl
+
+
+def pin_commit_invariants(orc):
+    inp, err, L, nodes = _commit_case(orc, "batched8k", 41, B=4, prefix=(3, 60), T=20,
+                                      Hq=4, Hkv=2, D=32, V=50, max_levels=5)
+    assert L.max() > 1                     # something beyond the root was accepted
+    check_commit_invariants(orc, inp, err, L, nodes)
+    inp, err, L, nodes = _commit_case(orc, "tiny", 42, D=16)
+    check_commit_invariants(orc, inp, err, L, nodes)
+
+
+def pin_commit_single_root(orc):
+    inp, err, L, nodes = _commit_case(orc, "parity512", 43, T=1, tree="chain", D=16,
+                                      prefix=(9, 9), capacity=16)
+    assert L[0] == 1
+    cache, npl = check_commit_invariants(orc, inp, err, L, nodes)
+    assert npl[0] == 10
+
+
+def pin_commit_refusals(orc):
+    inp, err, L, nodes = _commit_case(orc, "parity512", 44, D=16, B=3, prefix=(5, 9),
+                                      capacity=24)
+    cache = _cache(inp)
+    k0 = cache.k.copy()
+    P = to_np(inp.prefix_len)
+    bad_err = np.array([1, 0, 0], np.int32)
+    L2 = L.copy()
+    L2[1] = inp.w.T + 1                    # more rows than tree nodes
+    nodes2 = nodes.copy()
+    npl = orc.kv_commit(to_np(inp.k_tree), to_np(inp.v_tree), L2, nodes2, bad_err, cache, P,
+                        inp.max_prefix_len)
+    assert npl[0] == P[0] and npl[1] == P[1] and npl[2] == P[2] + L[2]
+    k4 = cache.k.reshape(3, 2, -1, 16)
+    k04 = k0.reshape(3, 2, -1, 16)
+    assert np.array_equal(k4[0], k04[0]) and np.array_equal(k4[1], k04[1])
+    # prefix beyond the declared bound: refused
+    cache = _cache(inp)
+    npl = orc.kv_commit(to_np(inp.k_tree), to_np(inp.v_tree), L, nodes, err, cache, P,
+                        int(P.min()) - 1)
+    assert np.array_equal(npl, P) and np.array_equal(cache.k, k0)
+
+
+def pin_commit_chain_equals_serial(orc):
+    """Full accept of a chain leaves the same cache bytes as T serial root commits."""
+    inp = small_inputs("chain2k", 45, prefix=(30, 30), capacity=48, D=32, Hq=2, draft_p=1.0,
+                       V=64)
+    parents = to_np(inp.parents)
+    _, _, err = orc.build_tree_mask(parents)
+    _, L, nodes, _ = orc.accept_longest_path(to_np(inp.logits), to_np(inp.draft), parents, err)
+    assert L[0] == inp.w.T
+    c1 = _cache(inp)
+    P = to_np(inp.prefix_len)
+    orc.kv_commit(to_np(inp.k_tree), to_np(inp.v_tree), L, nodes, err, c1, P, int(P.max()))
+    c2 = _cache(inp)
+    kt, vt = to_np(inp.k_tree), to_np(inp.v_tree)
+    Pi = P.copy()
+    for i in range(inp.w.T):
+        Pi = orc.kv_commit(np.ascontiguousarray(kt[:, :, i:i + 1]),
+                           np.ascontiguousarray(vt[:, :, i:i + 1]), np.array([1], np.int32),
+                           np.array([[0]], np.int32), None, c2, Pi, int(Pi.max()))
+    assert np.array_equal(c1.k, c2.k) and np.array_equal(c1.v, c2.v)
+
+
+ALL_PINS = [
+    pin_mask_worked_example, pin_mask_closed_forms, pin_mask_bruteforce, pin_mask_invalid,
+    pin_attn_decode_T1, pin_attn_chain_causal, pin_attn_tree_vs_sdpa, pin_attn_prefix_zero,
+    pin_attn_closed_forms, pin_attn_paged_equals_contiguous, pin_attn_bad_block_entry,
+    pin_attn_chain_equals_serial,
+    pin_argmax_numpy, pin_argmax_special_values, pin_argmax_planted,
+    pin_accept_bruteforce, pin_accept_edge_cases, pin_accept_expected_tokens_golden,
+    pin_accept_expected_tokens_closed_form,
+    pin_commit_invariants, pin_commit_single_root, pin_commit_refusals,
+    pin_commit_chain_equals_serial,
+]

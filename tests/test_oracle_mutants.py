@@ -1,0 +1,91 @@
+"""Plausible mistakes planted in copies of the oracle (on the CPU) must each be
+caught by at least one pin.  This shows the pins constrain every part of the
+oracle: a dropped term, a wrong index, a transposed layout or a wrong tie rule
+anywhere fails a pin.  The real oracle source is never modified."""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sv_oracle.c")
+
+# (name, original text, replacement, occurrence index to replace)
+MUTANTS = [
+    ("mask_without_self", "int j = i;\n                while (j != -1) {",
+     "int j = par[i];\n                while (j != -1) {", 0),
+    ("mask_depth_off_by_one", "steps -= 1;", "steps -= 0;", 0),
+    ("tree_second_root_allowed", "par[i] < 0 || par[i] >= i", "par[i] < -1 || par[i] >= i", 0),
+    ("gqa_modulo_map", "const int kvh = h / G;", "const int kvh = h % Hkv;", 0),
+    ("scale_dropped_on_prefix", "s[n] = scale * dot;", "s[n] = dot;", 0),
+    ("prefix_off_by_one", "for (int64_t p = 0; p < P; ++p)",
+     "for (int64_t p = 0; p + 1 < P; ++p)", 0),
+    ("tree_mask_ignored", "if (!((mrow[j / 64] >> (j % 64)) & 1)) continue;", "", 0),
+    ("output_layout_head_major", "dst = out + (((int64_t)b * T + i) * Hq + h) * D;",
+     "dst = out + (((int64_t)b * Hq + h) * T + i) * D;", 0),
+    ("softmax_weight_dropped", "num[d] += w * elem(vsrc[k], dtype, voff[k] + d);",
+     "num[d] += elem(vsrc[k], dtype, voff[k] + d);", 0),
+    ("values_read_from_keys", "vsrc[n] = v_cache;", "vsrc[n] = k_cache;", 0),
+    ("tree_rows_from_head0", "const int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;",
+     "const int64_t off = (((int64_t)b * Hkv) * T + j) * D;", 0),
+    ("argmax_ties_to_last", "best < 0 || x[v] > bv", "best < 0 || x[v] >= bv", 0),
+    ("argmax_nan_not_skipped", "if (isnan(x[v])) continue;", "", 0),
+    ("argmax_all_nan_minus_one", "return best < 0 ? 0 : (int32_t)best;",
+     "return (int32_t)best;", 0),
+    ("accept_compares_own_argmax", "drf[i] == a[par[i]]", "drf[i] == a[i]", 0),
+    ("accept_ignores_parent_match", "match[par[i]] && drf[i] == a[par[i]]",
+     "drf[i] == a[par[i]]", 0),
+    ("accept_emits_drafts", "toks[j] = a[path[j]];", "toks[j] = drf[path[j]];", 0),
+    ("accept_ties_to_largest", "match[i] && dep[i] > dep[best]",
+     "match[i] && dep[i] >= dep[best]", 0),
+    ("accept_ignores_tree_err", "(tree_err && tree_err[b] != 0) ||", "0 ||", 0),
+    ("commit_copies_node_j", "* T + nodes[j]) * D;", "* T + j) * D;", 0),
+    ("commit_v_from_k", "memcpy((char *)v_cache + dst * esz, (const char *)v_tree",
+     "memcpy((char *)v_cache + dst * esz, (const char *)k_tree", 0),
+    ("commit_length_short", "new_prefix_len[b] = ok ? P + L : P;",
+     "new_prefix_len[b] = ok ? P + L - 1 : P;", 0),
+    ("commit_ignores_tree_err", "int ok = !(tree_err && tree_err[b] != 0);", "int ok = 1;", 0),
+]
+
+
+def _mutate(src: str, old: str, new: str, occ: int) -> str:
+    assert src.count(old) >= occ + 1, f"mutation anchor not found: {old!r}"
+    pos = -1
+    for _ in range(occ + 1):
+        pos = src.index(old, pos + 1)
+    return src[:pos] + new + src[pos + len(old):]
+
+
+_RUNNER = """
+import sys
+sys.path[:0] = [{tests!r}, {root!r}]
+import oracle, oracle_pins
+orc = oracle.Oracle({lib!r})
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(orc)
+    except AssertionError:
+        print("caught by", pin.__name__)
+        sys.exit(3)
+sys.exit(0)
+"""
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, occ):
+    src = open(SRC).read()
+    tests = os.path.dirname(os.path.abspath(__file__))
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "mutant.c")
+        with open(path, "w") as f:
+            f.write(_mutate(src, old, new, occ))
+        lib = oracle.build(src=path, out=os.path.join(td, f"lib{name}.so"))
+        code = _RUNNER.format(tests=tests, root=os.path.dirname(tests), lib=lib)
+        # each mutant runs in its own process, under a time limit
+        r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                           timeout=120, env={**os.environ, "OMP_NUM_THREADS": "2"})
+        assert r.returncode == 3, f"mutant {name} passed every pin (rc={r.returncode})\n{r.stderr[-2000:]}"
