@@ -1,0 +1,202 @@
+"""Throughput of the tree-verify step on one MI355X.
+
+A step is one pass of the whole path over one batch: ancestor mask -> tree-masked
+split-KV attention -> vocab argmax + longest-path acceptance -> KV commit, four C-ABI
+calls back to back on one stream, inputs resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload long32k] [--splits S]
+
+value = verified tree tokens/s = B*T / seconds per step.  The roofline object covers
+the attention call (its split kernel plus its merge kernel), timed with HIP events on
+the stream it runs on; cpu_baseline times the oracle on one sequence of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tree tokens/s + tree-verify attention HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attention_traffic(inp, depth):
+    """Algorithmic bytes and flops of one attention call (what the method must move)."""
+    import numpy as np
+    w = inp.w
+    e = 2 if w.dtype == "bf16" else 4
+    P = inp.prefix_len.cpu().numpy().astype(np.int64)
+    kv_prefix = int(P.sum()) * w.Hkv * w.D * e * 2
+    kv_tree = w.B * w.Hkv * w.T * w.D * e * 2
+    q = w.B * w.Hq * w.T * w.D * e
+    o = w.B * w.T * w.Hq * w.D * 4
+    anc = depth.cpu().numpy().astype(np.int64) + 1            # [B, T] keys from the tree
+    keys = (P[:, None] + anc).sum() * w.Hq                      # sum over (b, h, i)
+    flops = 4 * w.D * int(keys)
+    return kv_prefix + kv_tree + q + o, flops
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The oracle on sequence 0 of the workload (all its heads, nodes and stages)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle as O
+    from _support import to_np
+
+    w = inp.w
+    b = 0
+    nblk = int((inp.block_table[b] >= 0).sum())
+    blocks = inp.block_table[b, :nblk].long()
+    kp = to_np(inp.k_pool.index_select(0, blocks))
+    vp = to_np(inp.v_pool.index_select(0, blocks))
+    table = np.arange(nblk, dtype=np.int32)[None]
+    _, Hkv, bs, D = inp.k_pool.shape
+    cache = O.Cache(k=kp, v=vp, table=table, block_size=bs, block_stride=Hkv * bs * D,
+                    head_stride=bs * D, row_stride=D, num_blocks=nblk,
+                    dtype=O.BF16 if w.dtype == "bf16" else O.F32)
+    parents = to_np(inp.parents[b:b + 1])
+    q, kt, vt = to_np(inp.q[b:b + 1]), to_np(inp.k_tree[b:b + 1]), to_np(inp.v_tree[b:b + 1])
+    P = to_np(inp.prefix_len[b:b + 1])
+    logits, draft = to_np(inp.logits[b:b + 1]), to_np(inp.draft[b:b + 1])
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    orc = O.Oracle()
+
+    # size the sample: time a few rows, then take as many heads as fit the budget
+    t0 = time.perf_counter()
+    rows = np.array([[0, 0, i] for i in range(min(w.T, threads))], dtype=np.int32)
+    mask, _, err = orc.build_tree_mask(parents)
+    orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
+                              nthreads=threads)
+    per_row = (time.perf_counter() - t0) / max(1, len(rows)) * threads
+    heads = max(1, min(w.Hq, int(budget_s / max(per_row * w.T / threads, 1e-9))))
+
+    t0 = time.perf_counter()
+    mask, _, err = orc.build_tree_mask(parents)
+    rows = np.array([[0, h, i] for h in range(heads) for i in range(w.T)], dtype=np.int32)
+    orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
+                              nthreads=threads)
+    t_attn = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    _, L, nodes, _ = orc.accept_longest_path(logits, draft, parents, err)
+    orc.kv_commit(kt, vt, L, nodes, err, cache, P, int(P.max()))
+    t_rest = time.perf_counter() - t1
+    # one sequence's step = attention over all Hq heads + accept + commit
+    t_seq = t_attn * (w.Hq / heads) + t_rest
+    t_step = t_seq * w.B
+    return {"value": w.B * w.T / t_step, "unit": "verified tree tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"sequence 0 of {w.B}: mask, attention for {heads} of {w.Hq} q heads "
+                      f"x {w.T} nodes (scaled to all heads), accept over {w.V} logits, "
+                      f"commit; step time = {w.B} x that sequence; {t_attn + t_rest:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long32k")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify path has no multi-GPU code)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tree_masked_verify_amd import workloads as wl
+    from tree_masked_verify_amd.step import VerifyStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    log(f"[bench] generating {w.name} inputs (seed {args.seed})")
+    inp = wl.make_inputs(w, seed=args.seed, device=dev)
+    st = VerifyStep.from_inputs(inp, num_splits=args.splits)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        st.build_mask()
+        ea[k][0].record(stream)
+        st.attention()
+        ea[k][1].record(stream)
+        st.accept()
+        st.commit()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev[0].elapsed_time(ev[1]) / args.steps
+    ms_attn = sum(a.elapsed_time(b) for a, b in ea) / args.steps
+
+    # per-stage split (separate pass, one call type at a time)
+    stages = {}
+    for name, fn in (("mask", st.build_mask), ("attention", st.attention),
+                     ("accept", st.accept), ("commit", st.commit)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stages[name] = round(e0.elapsed_time(e1) / args.steps * 1000.0, 2)
+
+    bytes_attn, flops_attn = attention_traffic(inp, st.depth)
+    gbs = bytes_attn / (ms_attn * 1e-3) / 1e9
+    tflops = flops_attn / (ms_attn * 1e-3) / 1e12
+    bytes_argmax = w.B * w.T * w.V * 4
+    tokens = w.B * w.T
+    result = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "prefix": list(w.prefix), "tree_nodes": w.T,
+                   "tree": w.tree, "vocab": w.V, "paged_block": w.block_size,
+                   "num_splits": args.splits, "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "tree-verify attention (split + merge kernels)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": bytes_attn, "us_per_launch": round(ms_attn * 1e3, 2),
+                     "mfma_tflops": round(tflops, 1),
+                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "stages_us": stages,
+        "accepted_tokens_per_step": int(st.accepted_len.sum()),
+        "argmax_gbs": round(bytes_argmax / (stages["accept"] * 1e-6) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * sv.h -- C ABI of the tree-masked speculative verify library (libsv.so, gfx950).
+ *
+ * One verify step of speculative decoding, for a batch of B independent
+ * sequences that each carry a draft token tree of T nodes:
+ *
+ *   1. sv_build_tree_mask        parent array -> ancestor-and-self bitmask
+ *   2. sv_tree_verify_attention  tree rows attend to the cached prefix plus their
+ *                                ancestors (split-KV, GQA, log-sum-exp merge)
+ *   3. sv_accept_longest_path    vocab argmax per row -> longest matching root path
+ *                                -> accepted nodes and emitted tokens
+ *   4. sv_kv_commit              copy only the accepted rows' K/V into the cache
+ *
+ * Sources (web pages, by title and section):
+ *   "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status rows
+ *     E1.1-E1.5 (tree attention; output layout [q_seq_len, num_heads, head_dim];
+ *     head_dim 256/512), E1 review gate (dtype and byte-length validation), E4a
+ *     (build_tree_mask from the parent array, checked overflow), E5a (tree-walk
+ *     accept), E6 (zero-head guard before the GQA modulo), E6 v2 (ancestors +
+ *     self); section 4, Phases E1 and E5.
+ *   "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs): "Why
+ *     bother" (greedy longest-matching-prefix verification) and "What's not
+ *     implemented" item 1 (ancestor-only tree attention, per-path argmax).
+ *   "Speculative decoding verify batches to amortize ANE dispatch"
+ *     (llms-explorer): Facts on the commit rule and on delayed KV write-through.
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is device memory owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never synchronises
+ *     the stream.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs in stream order.
+ *   - Host-checkable argument errors return a negative sv_status before anything
+ *     is enqueued; then no output is written.  SV_ERR_HIP reports a failed
+ *     launch (hipGetLastError after the launch).
+ *   - Data-dependent problems found on the device (a malformed parent array, an
+ *     out-of-range block-table entry) never fault: they are reported through
+ *     tree_err or handled as documented per function.
+ *   - Integers are little-endian int32 unless stated; bf16 is stored as its
+ *     16-bit pattern.
+ */
+#ifndef SV_H
+#define SV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_ERR_NULL = -1,       /* a required pointer is NULL */
+    SV_ERR_SHAPE = -2,      /* a size is negative/zero where not allowed, or inconsistent */
+    SV_ERR_DTYPE = -3,      /* unknown dtype, or dtype not supported for this call */
+    SV_ERR_GQA = -4,        /* Hkv <= 0, Hq <= 0 or Hq not a multiple of Hkv */
+    SV_ERR_HEAD_DIM = -5,   /* head_dim not 256 or 512 */
+    SV_ERR_TREE_SIZE = -6,  /* T outside [1, 64] */
+    SV_ERR_CAPACITY = -7,   /* max_prefix_len + T exceeds the rows the block table reserves */
+    SV_ERR_OVERFLOW = -8,   /* a byte size does not fit in 64 bits / an index in 32 bits */
+    SV_ERR_WORKSPACE = -9,  /* workspace NULL or smaller than the *_workspace_size result */
+    SV_ERR_HIP = -10,       /* the HIP runtime reported an error */
+    SV_ERR_ALIGN = -11      /* a pointer or stride is not 16-byte aligned */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Per-sequence tree status written by sv_build_tree_mask into tree_err[b]. */
+enum { SV_TREE_OK = 0, SV_TREE_BAD_ROOT = 1, SV_TREE_BAD_PARENT = 2 };
+
+/*
+ * KV cache descriptor: one layout for contiguous and paged caches.
+ *   Row `pos` of sequence b, kv head h starts at element
+ *     block_table[b * max_blocks_per_seq + pos / block_size] * block_stride
+ *       + h * head_stride + (pos % block_size) * row_stride
+ *   of the K pool (and the same offset in the V pool); a row holds head_dim
+ *   contiguous elements of `dtype`.
+ *   Paged   [num_blocks][Hkv][block_size][D]: block_stride = Hkv*bs*D,
+ *           head_stride = bs*D, row_stride = D.
+ *   Contiguous [B][Hkv][cap][D]: block_size = cap, max_blocks_per_seq = 1,
+ *           block_table[b] = b, same stride formulas.
+ * Requirements: block_size a positive multiple of 16; strides multiples of 8
+ * elements (16 bytes); k, v 16-byte aligned.  Block-table entries outside
+ * [0, num_blocks) are never dereferenced (see each call).
+ */
+typedef struct sv_kv_cache {
+    void *k;                     /* K pool, device */
+    void *v;                     /* V pool, device */
+    const int32_t *block_table;  /* [B][max_blocks_per_seq], device */
+    int32_t block_size;          /* rows per block */
+    int32_t max_blocks_per_seq;  /* row length of block_table */
+    int64_t num_blocks;          /* blocks in each pool */
+    int64_t block_stride;        /* elements */
+    int64_t head_stride;         /* elements */
+    int64_t row_stride;          /* elements */
+    int32_t dtype;               /* sv_dtype; must equal the Q/K/V dtype */
+} sv_kv_cache;
+
+/*
+ * Ancestor-and-self mask of each sequence's draft tree.
+ * Defined by: ADR-037 Phase status rows E4a (build_tree_mask) and E6 v2
+ * (ancestors + self); Medusa/EAGLE-2 page, "What's not implemented" 1(c).
+ *
+ *   parents  int32 [B][T]  node 0 is the root (parent -1); 0 <= parents[i] < i
+ *   mask     uint64 [B][T][W], W = ceil(T/64) (= 1 since T <= 64): bit j of
+ *            row i is set iff node j is node i or an ancestor of node i
+ *   depth    int32 [B][T] or NULL: number of proper ancestors (root 0)
+ *   tree_err int32 [B]: SV_TREE_OK, SV_TREE_BAD_ROOT (parents[0] != -1) or
+ *            SV_TREE_BAD_PARENT (some parents[i] outside [0, i)).  A bad tree's
+ *            rows are self-only with depth 0.
+ * Errors: SV_ERR_NULL (parents, mask, tree_err), SV_ERR_SHAPE (B < 0),
+ *         SV_ERR_TREE_SIZE (T outside [1, 64]), SV_ERR_HIP.
+ */
+int sv_build_tree_mask(const int32_t *parents, int32_t B, int32_t T, uint64_t *mask,
+                       int32_t *depth, int32_t *tree_err, hipStream_t stream);
+
+/*
+ * Bytes of workspace sv_tree_verify_attention needs for this shape and split
+ * count (num_splits 0 = automatic).  Returns 0 when the arguments would be
+ * rejected by sv_tree_verify_attention's shape checks.
+ */
+size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                               int32_t D, int32_t max_prefix_len, int32_t dtype,
+                                               int32_t num_splits);
+
+/*
+ * Tree-masked attention of every tree node's query over its sequence's cached
+ * prefix and its own ancestors plus itself.
+ * Defined by: ADR-037 Phase status rows E1.1-E1.5 and section 4 Phase E1
+ * (tree mask; tree = 1 equals decode, a chain equals causal attention);
+ * Medusa/EAGLE-2 page "What's not implemented" 1(c).
+ *
+ * For query head h (kv head h / (Hq/Hkv)), node i of sequence b:
+ *   keys  = cache rows 0 .. P_b-1 of that kv head, then tree rows j with bit j of
+ *           mask[b][i] set;  P_b = prefix_len[b] clamped into [0, max_prefix_len]
+ *   out[b][i][h][:] = softmax(scale * q . k) weighted sum of the matching values
+ *   q       [B][Hq][T][D]   dtype (SV_BF16, or SV_F32)
+ *   k_tree, v_tree [B][Hkv][T][D]  the tree nodes' own K/V (not yet in the cache)
+ *   cache   prefix K/V; cache->dtype must equal the Q/K/V dtype
+ *   prefix_len int32 [B] device; max_prefix_len host upper bound of prefix_len
+ *   mask    from sv_build_tree_mask
+ *   out     float32 [B][T][Hq][D]   (layout [q_seq_len, num_heads, head_dim] per sequence)
+ *   scale   usually 1/sqrt(D)
+ *   workspace  device, >= sv_tree_verify_attention_workspace_size(...) bytes,
+ *              256-byte aligned; scratch for per-split partial results
+ *   num_splits 0 = automatic; otherwise the number of prefix chunks per sequence
+ * Arithmetic: bf16 (or fp32) operands, fp32 accumulation; the result matches
+ * the exact softmax attention to within bf16 rounding of the probabilities.
+ * Prefix rows whose block-table entry is outside [0, num_blocks) are left out.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, max_prefix_len < 0, block_size not a
+ * positive multiple of 16, num_splits < 0, strides not positive),
+ * SV_ERR_GQA, SV_ERR_HEAD_DIM, SV_ERR_TREE_SIZE, SV_ERR_DTYPE, SV_ERR_CAPACITY
+ * (max_prefix_len + T > max_blocks_per_seq * block_size), SV_ERR_ALIGN,
+ * SV_ERR_OVERFLOW, SV_ERR_WORKSPACE, SV_ERR_HIP.
+ */
+int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tree,
+                             const sv_kv_cache *cache, const int32_t *prefix_len,
+                             int32_t max_prefix_len, const uint64_t *mask, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t T, int32_t D, float scale, float *out,
+                             void *workspace, size_t workspace_bytes, int32_t num_splits,
+                             hipStream_t stream);
+
+/* Bytes of workspace sv_accept_longest_path needs (0 when the shape is invalid). */
+size_t sv_accept_longest_path_workspace_size(int32_t B, int32_t T, int64_t V);
+
+/*
+ * Greedy acceptance.
+ * Defined by: llms-explorer page Facts, commit rule (the target's argmax at each
+ * draft row decides; longest matching prefix plus one bonus token); ADR-037 Phase
+ * status row E5a and section 4 Phase E5 (longest matching path from the root;
+ * full accept picks the deepest); row E4b.10a (smaller token wins ties);
+ * Medusa/EAGLE-2 page "Why bother".
+ *
+ *   logits  float32 [B][T][V]; a[b][i] = smallest index of the row maximum, NaN
+ *           never wins, an all-NaN row gives 0
+ *   draft   int32 [B][T]: draft[b][i] is node i's token (draft[b][0] unused)
+ *   parents int32 [B][T] (as for sv_build_tree_mask)
+ *   tree_err int32 [B] or NULL: a non-zero entry (or a malformed parent array)
+ *           makes that sequence accept nothing
+ *   argmax_out int32 [B][T] or NULL: a[][]
+ *   accepted_len int32 [B]: L = depth of the accepted node + 1 (0 if invalid)
+ *   accepted_nodes int32 [B][T]: the path root..accepted node, then -1
+ *   out_tokens int32 [B][T]: a[] along the path (L-1 accepted drafts + 1 bonus
+ *           token), then -1
+ * Node i >= 1 matches when its parent matches and draft[b][i] == a[b][parent];
+ * the accepted node is the deepest matching node, the smallest index among equals.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, V < 1), SV_ERR_TREE_SIZE,
+ * SV_ERR_OVERFLOW, SV_ERR_WORKSPACE, SV_ERR_HIP.
+ */
+int sv_accept_longest_path(const float *logits, const int32_t *draft, const int32_t *parents,
+                           const int32_t *tree_err, int32_t B, int32_t T, int64_t V,
+                           int32_t *argmax_out, int32_t *accepted_len, int32_t *accepted_nodes,
+                           int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Delayed KV write-through: commit only the accepted rows.
+ * Defined by: llms-explorer page Facts on Forge's accept(k) (only the accepted
+ * prefix reaches the cache; rejected drafts never touch it) and on delayed KV
+ * write-through (commit after the acceptance decision).
+ *
+ * For every sequence b with tree_err[b] == 0 (or tree_err NULL): for
+ * j < accepted_len[b] and every kv head, cache row prefix_len[b] + j receives
+ * tree row accepted_nodes[b][j] of k_tree and v_tree (byte copy); then
+ * new_prefix_len[b] = prefix_len[b] + accepted_len[b].  A sequence whose request
+ * cannot be honoured in full (prefix_len[b] outside [0, max_prefix_len],
+ * accepted_len outside [0, T], a node index outside [0, T), a block-table entry
+ * outside [0, num_blocks)) is left untouched and new_prefix_len[b] =
+ * prefix_len[b].  new_prefix_len may be NULL, or may alias prefix_len.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_TREE_SIZE, SV_ERR_HEAD_DIM,
+ * SV_ERR_DTYPE, SV_ERR_CAPACITY, SV_ERR_ALIGN, SV_ERR_OVERFLOW, SV_ERR_HIP.
+ */
+int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
+                 const int32_t *accepted_nodes, const int32_t *tree_err,
+                 const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                 int32_t *new_prefix_len, int32_t B, int32_t Hkv, int32_t T, int32_t D,
+                 hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *sv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SV_H */

@@ -1,0 +1,136 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/sv.h
+declares, and rejects bad arguments on the host before anything reaches a GPU.
+(No call here gets past validation, so none launches a kernel.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_masked_verify_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sv.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced by these calls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(sv.ENTRY_POINTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in sv.STATUS.items():
+        s = sv.sv_status_string(code)
+        assert s and s != "unknown status", (code, s)
+    assert sv.sv_status_string(12345) == "unknown status"
+
+
+def test_mask_validation(lib):
+    f = lib.sv_build_tree_mask
+    assert f(FAKE, 2, 0, FAKE, None, FAKE, None) == -6
+    assert f(FAKE, 2, 65, FAKE, None, FAKE, None) == -6
+    assert f(FAKE, -1, 8, FAKE, None, FAKE, None) == -2
+    assert f(None, 0, 8, None, None, None, None) == 0       # nothing to do
+    assert f(None, 2, 8, FAKE, None, FAKE, None) == -1
+    assert f(FAKE, 2, 8, FAKE, None, None, None) == -1
+
+
+def cache(**kw):
+    c = dict(k=FAKE, v=FAKE, block_table=FAKE, block_size=16, max_blocks_per_seq=10,
+             num_blocks=100, block_stride=2 * 16 * 256, head_stride=16 * 256, row_stride=256,
+             dtype=sv.SV_BF16)
+    c.update(kw)
+    return sv.sv_kv_cache(**c)
+
+
+def attn(lib, c=None, q=FAKE, B=2, Hq=8, Hkv=2, T=8, D=256, maxp=100, ws=FAKE, wsb=1 << 30,
+         splits=0, out=FAKE, null_cache=False):
+    c = c or cache()
+    return lib.sv_tree_verify_attention(q, FAKE, FAKE, None if null_cache else ctypes.byref(c),
+                                        FAKE, maxp, FAKE, B, Hq, Hkv, T, D, 0.0625, out, ws, wsb,
+                                        splits, None)
+
+
+def test_attention_validation(lib):
+    assert attn(lib, null_cache=True) == -1
+    assert attn(lib, Hkv=0) == -4
+    assert attn(lib, Hq=0) == -4
+    assert attn(lib, Hq=6, Hkv=4) == -4
+    assert attn(lib, D=128) == -5
+    assert attn(lib, T=0) == -6 and attn(lib, T=65) == -6
+    assert attn(lib, B=-1) == -2 and attn(lib, maxp=-1) == -2 and attn(lib, splits=-2) == -2
+    assert attn(lib, c=cache(dtype=9)) == -3
+    assert attn(lib, c=cache(block_size=8)) == -2
+    assert attn(lib, c=cache(num_blocks=0)) == -2
+    assert attn(lib, maxp=153) == -7                  # 153 + 8 > 10 * 16
+    assert attn(lib, maxp=152, ws=None) == -9         # exactly at capacity, but no workspace
+    assert attn(lib, wsb=16) == -9
+    assert attn(lib, q=FAKE + 2) == -11
+    assert attn(lib, out=FAKE + 4) == -11
+    assert attn(lib, c=cache(row_stride=260)) == -11
+    assert attn(lib, c=cache(k=FAKE + 8)) == -11
+    assert attn(lib, ws=FAKE + 16) == -11             # workspace must be 256-byte aligned
+    assert attn(lib, B=0, null_cache=False) == 0
+    assert attn(lib, c=cache(block_table=None)) == -1
+    assert attn(lib, c=cache(num_blocks=1 << 62, block_stride=1 << 20)) == -8
+
+
+def test_attention_workspace_size(lib):
+    f = sv.sv_tree_verify_attention_workspace_size
+    a = f(16, 32, 8, 60, 256, 32768, sv.SV_BF16)
+    b = f(16, 32, 8, 60, 256, 32768, sv.SV_BF16, 4)
+    assert a > 0 and b > 0
+    assert b >= 16 * 8 * 4 * 240 * 256 * 4            # 4 chunks of fp32 partials per row
+    assert f(16, 32, 0, 60, 256, 32768, sv.SV_BF16) == 0
+    assert f(16, 32, 8, 60, 128, 32768, sv.SV_BF16) == 0
+    assert f(1, 1, 1, 1, 256, 0, sv.SV_F32) > 0
+
+
+def test_accept_validation(lib):
+    f = lib.sv_accept_longest_path
+    args = lambda B=2, T=8, V=1000, lg=FAKE, ws=FAKE, wsb=1 << 30: (
+        lg, FAKE, FAKE, None, B, T, V, None, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert f(*args(V=0)) == -2
+    assert f(*args(B=-3)) == -2
+    assert f(*args(T=0)) == -6 and f(*args(T=65)) == -6
+    assert f(*args(V=1 << 31)) == -8
+    assert f(*args(lg=None)) == -1
+    assert f(*args(lg=FAKE + 2)) == -11
+    assert f(*args(wsb=8)) == -9
+    assert f(*args(ws=None)) == -9
+    assert f(*args(B=0)) == 0
+    assert sv.sv_accept_longest_path_workspace_size(2, 8, 1000) > 0
+    assert sv.sv_accept_longest_path_workspace_size(2, 0, 1000) == 0
+
+
+def test_commit_validation(lib):
+    f = lib.sv_kv_commit
+    def call(c=None, Hkv=2, T=8, D=256, maxp=100, kt=FAKE, B=2):
+        c = c or cache()
+        return f(kt, FAKE, FAKE, FAKE, None, ctypes.byref(c), FAKE, maxp, None, B, Hkv, T, D,
+                 None)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, None, 2, 2, 8, 256, None) == -1
+    assert call(Hkv=0) == -4
+    assert call(T=70) == -6
+    assert call(D=100) == -5
+    assert call(c=cache(dtype=3)) == -3
+    assert call(maxp=153) == -7
+    assert call(maxp=-1) == -2
+    assert call(kt=FAKE + 2) == -11
+    assert call(kt=None) == -1
+    assert call(B=0) == 0

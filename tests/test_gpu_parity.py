@@ -1,0 +1,108 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, same seeded inputs.
+
+Bit-exact: masks, depths, tree errors, argmax, accepted lengths / nodes / tokens, new
+prefix lengths and every byte of both cache pools after the commit.  Attention
+outputs: max-abs <= 1e-2 and relative RMS <= 2^-6.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity import compare, gpu_step, host_copy, oracle_step, sample_rows
+from tree_masked_verify_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def orc():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return O.Oracle()
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(orc, w, seed, num_splits=0, rows=None, **mk):
+    _say(f"[case] {w.name} seed={seed} splits={num_splits} B={w.B} T={w.T} D={w.D}")
+    inp = wl.make_inputs(w, seed=seed, device=DEV, **mk)
+    h = host_copy(inp)
+    g = gpu_step(inp, num_splits=num_splits)
+    o = oracle_step(orc, inp, h, rows=rows)
+    err = compare(g, o, rows=rows)
+    _say(f"       attention max-abs {err['max_abs']:.3e} rel-rms {err['rel_rms']:.3e}, "
+         f"accepted {list(g['L'][:8])}")
+    return inp, g, o
+
+
+# ----------------------------------------------------------------- the five workload shapes
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny(orc, seed):
+    run_case(orc, wl.WORKLOADS["tiny"], seed)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_parity512(orc, seed):
+    run_case(orc, wl.WORKLOADS["parity512"], seed)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_chain2k(orc, seed):
+    run_case(orc, wl.WORKLOADS["chain2k"], seed)
+
+
+def test_batched8k_full_size(orc):
+    w = wl.WORKLOADS["batched8k"]
+    run_case(orc, w, 0, rows=sample_rows(w, 48, 1))
+
+
+def test_long32k_full_size(orc):
+    w = wl.WORKLOADS["long32k"]
+    run_case(orc, w, 0, rows=sample_rows(w, 48, 2))
+
+
+# ----------------------------------------------------------------- reduced shapes, every row
+@pytest.mark.parametrize("seed", [0, 1])
+def test_batched_reduced_ragged(orc, seed):
+    w = wl.scaled(wl.WORKLOADS["batched8k"], name="batched_small", B=4, prefix=(290, 1111),
+                  V=5003)
+    run_case(orc, w, seed)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+def test_long_reduced_splits(orc, splits):
+    w = wl.scaled(wl.WORKLOADS["long32k"], name="long_small", B=2, prefix=(1501, 1501), V=4096)
+    run_case(orc, w, 3, num_splits=splits)
+
+
+def test_peaked_attention(orc):
+    """Sharp softmax (Q, K with std 3): outputs of order one, so 1e-2 is tight."""
+    w = wl.scaled(wl.WORKLOADS["long32k"], name="peaked", B=2, prefix=(700, 900), V=2048,
+                  qkv_std=3.0)
+    run_case(orc, w, 5)
+    w = wl.scaled(wl.WORKLOADS["parity512"], name="peaked512", qkv_std=3.0)
+    run_case(orc, w, 6)
+
+
+def test_prefix_zero_and_single_node(orc):
+    run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="p0", prefix=(0, 0), capacity=16), 7)
+    run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="t1", T=1, tree="chain",
+                            prefix=(333, 333), capacity=352), 8)
+    run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], name="t1f", T=1, tree="chain",
+                            parents=(-1,)), 9)
+
+
+def test_fp32_gqa(orc):
+    run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], name="f32gqa", Hq=8, Hkv=2, prefix=(40, 90),
+                            B=3, tree="random", max_levels=4, max_children=3, capacity=160,
+                            block_size=0), 10)
+
+
+def test_unaligned_vocab(orc):
+    run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="v1001", V=1001, B=3), 11)

@@ -1,0 +1,80 @@
+// attn_reduce.hip -- merge the per-chunk partial attention results of each query row.
+//
+// Chunk s of a row left an unnormalised output O_s, its reference max m_s (log2
+// units) and the sum l_s of its exp2(score - m_s) weights.  With M = max_s m_s:
+//   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
+// the split-then-merge scheme the pages' flash_attn_vec_reduce plays (ADR-037
+// Phase status row E1.2 and the E6 full-layer rows).  One wavefront per output row
+// (b, i, h), chunks in a fixed order, no atomics: the result is deterministic.
+// The output is laid out [B][T][Hq][D] (ADR-037 row E1.3).
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr float kNegInfR = -__builtin_huge_valf();
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restrict__ ws_o,
+                                                          const float *__restrict__ ws_ml,
+                                                          const int32_t *__restrict__ prefix_len,
+                                                          int max_P, int B, int Hq, int Hkv,
+                                                          int T, int R, int S, int C,
+                                                          float *__restrict__ out) {
+    constexpr int VPL = D / 64 / 4;  // float4 vectors per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t x = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t nrows = (int64_t)B * T * Hq;
+    if (x >= nrows) return;
+    const int h = (int)(x % Hq);
+    const int i = (int)((x / Hq) % T);
+    const int b = (int)(x / ((int64_t)Hq * T));
+    const int G = Hq / Hkv;
+    const int kvh = h / G;
+    const int r = (h - kvh * G) * T + i;
+
+    int P = prefix_len[b];
+    P = P < 0 ? 0 : (P > max_P ? max_P : P);
+    int nv = (P + C - 1) / C;
+    nv = nv < 1 ? 1 : (nv > S ? S : nv);
+
+    const int64_t base0 = ((int64_t)b * Hkv + kvh) * S * (int64_t)R + r;
+    float M = kNegInfR;
+    for (int s = 0; s < nv; ++s) M = fmaxf(M, ws_ml[(base0 + (int64_t)s * R) * 2]);
+
+    f32x4 acc[VPL];
+    for (int v = 0; v < VPL; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.0f;
+    for (int s = 0; s < nv; ++s) {
+        const int64_t base = base0 + (int64_t)s * R;
+        const float m = ws_ml[base * 2];
+        const float l = ws_ml[base * 2 + 1];
+        const float wgt = m == kNegInfR ? 0.0f : exp2f(m - M);
+        L += wgt * l;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(ws_o + base * D);
+        for (int v = 0; v < VPL; ++v) acc[v] += wgt * src[lane + 64 * v];
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(out + (((int64_t)b * T + i) * Hq + h) * D);
+    for (int v = 0; v < VPL; ++v) dst[lane + 64 * v] = acc[v] * inv;
+}
+
+}  // namespace
+
+hipError_t launch_attn_reduce(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
+    const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
+    if (nrows == 0) return hipSuccess;
+    const int per = 4;
+    dim3 grid((unsigned)((nrows + per - 1) / per));
+    if (a.D == 256)
+        hipLaunchKernelGGL(attn_reduce_kernel<256>, grid, dim3(64 * per), 0, stream, a.ws_o,
+                           a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
+                           pl.R, pl.S, pl.C, a.out);
+    else
+        hipLaunchKernelGGL(attn_reduce_kernel<512>, grid, dim3(64 * per), 0, stream, a.ws_o,
+                           a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
+                           pl.R, pl.S, pl.C, a.out);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,268 @@
+// sv_api.hip -- the C ABI of include/sv.h: argument validation, work planning, launches.
+//
+// Every check that can be made on the host is made before anything is enqueued
+// (the pages' validation culture: dtype and buffer-length checks, the zero-head
+// guard before the GQA modulo, checked size arithmetic -- ADR-037 Phase status
+// rows E1 review gate, E4a and E6).  Sizes are multiplied with overflow checks.
+#include <limits.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+
+bool prod_ok(std::initializer_list<int64_t> xs, int64_t *r) {
+    int64_t acc = 1;
+    for (int64_t x : xs)
+        if (!mul_ok(acc, x, &acc)) return false;
+    *r = acc;
+    return true;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize_of(int dtype) { return dtype == SV_BF16 ? 2 : (dtype == SV_F32 ? 4 : 0); }
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+int check_cache(const sv_kv_cache *c, int dtype, int64_t need_rows, int B) {
+    if (c->block_size <= 0 || c->block_size % 16 != 0 || c->max_blocks_per_seq <= 0 ||
+        c->num_blocks <= 0 || c->block_stride <= 0 || c->head_stride <= 0 || c->row_stride <= 0)
+        return SV_ERR_SHAPE;
+    if (c->dtype != dtype) return SV_ERR_DTYPE;
+    int64_t cap;
+    if (!mul_ok(c->max_blocks_per_seq, c->block_size, &cap)) return SV_ERR_OVERFLOW;
+    if (need_rows > cap) return SV_ERR_CAPACITY;
+    const int es = esize_of(dtype);
+    if ((c->block_stride * es) % 16 || (c->head_stride * es) % 16 || (c->row_stride * es) % 16)
+        return SV_ERR_ALIGN;
+    if (!aligned16(c->k) || !aligned16(c->v)) return SV_ERR_ALIGN;
+    int64_t tmp;
+    if (!prod_ok({c->num_blocks, c->block_stride, es}, &tmp)) return SV_ERR_OVERFLOW;
+    if (!prod_ok({(int64_t)B, c->max_blocks_per_seq}, &tmp)) return SV_ERR_OVERFLOW;
+    return SV_OK;
+}
+
+CacheView view_of(const sv_kv_cache *c) {
+    CacheView v;
+    v.k = c->k;
+    v.v = c->v;
+    v.table = c->block_table;
+    v.bs = c->block_size;
+    v.max_blocks = c->max_blocks_per_seq;
+    v.num_blocks = c->num_blocks;
+    v.bstride = c->block_stride;
+    v.hstride = c->head_stride;
+    v.rstride = c->row_stride;
+    return v;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
+
+// Shape checks shared by the attention size query and the attention call.
+int check_attn_shape(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int dtype,
+                     int num_splits) {
+    if (B < 0 || max_prefix_len < 0 || num_splits < 0) return SV_ERR_SHAPE;
+    if (Hkv <= 0 || Hq <= 0) return SV_ERR_GQA;  // before the modulo
+    if (Hq % Hkv != 0) return SV_ERR_GQA;
+    if (D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+    int64_t tmp;
+    if (!prod_ok({(int64_t)B, Hq, T, D, 4}, &tmp)) return SV_ERR_OVERFLOW;
+    if ((int64_t)max_prefix_len + T > INT_MAX) return SV_ERR_OVERFLOW;
+    return SV_OK;
+}
+
+}  // namespace
+
+int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int dtype,
+                   int num_splits, AttnPlan *p) {
+    const int rc = check_attn_shape(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits);
+    if (rc != SV_OK) return rc;
+    const int R = (Hq / Hkv) * T;
+    p->R = R;
+    p->mfma = dtype == SV_BF16 && R >= 16;
+    if (p->mfma) {
+        // 32-row blocks, each shared by D/256 wavefronts; at most 8 wavefronts
+        const int dsplit = D / 256;
+        const int blocks = (R + 31) / 32;
+        int nw = blocks * dsplit;
+        nw = nw > 8 ? 8 : nw;
+        p->rows_per_wg = (nw / dsplit) * 32;
+        p->nthreads = 64 * nw;
+    } else {
+        p->rows_per_wg = 16;
+        p->nthreads = 256;
+    }
+    p->n_rg = (R + p->rows_per_wg - 1) / p->rows_per_wg;
+    int64_t units = (int64_t)(B > 0 ? B : 1) * Hkv * p->n_rg;
+    int64_t want = num_splits > 0 ? num_splits : (kNumCU + units - 1) / units;
+    if (want < 1) want = 1;
+    const int64_t P = max_prefix_len > 0 ? max_prefix_len : 1;
+    int64_t C = (P + want - 1) / want;
+    C = (C + kKeyTile - 1) / kKeyTile * kKeyTile;
+    if (C < kKeyTile) C = kKeyTile;
+    int64_t S = (max_prefix_len + C - 1) / C;
+    if (S < 1) S = 1;
+    p->C = (int)C;
+    p->S = (int)S;
+    int64_t work, o_elems, ml_elems;
+    if (!prod_ok({units, S}, &work) || work > INT_MAX) return SV_ERR_OVERFLOW;
+    if (!prod_ok({(int64_t)B, Hkv, S, R, D}, &o_elems)) return SV_ERR_OVERFLOW;
+    if (!prod_ok({(int64_t)B, Hkv, S, R, 2}, &ml_elems)) return SV_ERR_OVERFLOW;
+    p->ws_o = round256((size_t)o_elems * 4);
+    p->ws_ml = round256((size_t)ml_elems * 4);
+    p->ws_total = p->ws_o + p->ws_ml;
+    return SV_OK;
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+const char *sv_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "ok";
+        case SV_ERR_NULL: return "a required pointer is NULL";
+        case SV_ERR_SHAPE: return "invalid or inconsistent size";
+        case SV_ERR_DTYPE: return "unsupported or mismatched dtype";
+        case SV_ERR_GQA: return "head counts must be positive with Hq a multiple of Hkv";
+        case SV_ERR_HEAD_DIM: return "head_dim must be 256 or 512";
+        case SV_ERR_TREE_SIZE: return "tree size T must be in [1, 64]";
+        case SV_ERR_CAPACITY: return "max_prefix_len + T exceeds the cache rows reserved per sequence";
+        case SV_ERR_OVERFLOW: return "a size overflows";
+        case SV_ERR_WORKSPACE: return "workspace missing or too small";
+        case SV_ERR_HIP: return "HIP runtime error";
+        case SV_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int sv_build_tree_mask(const int32_t *parents, int32_t B, int32_t T, uint64_t *mask,
+                       int32_t *depth, int32_t *tree_err, hipStream_t stream) {
+    if (B < 0) return SV_ERR_SHAPE;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (B == 0) return SV_OK;
+    if (!parents || !mask || !tree_err) return SV_ERR_NULL;
+    return hip_status(launch_tree_mask(parents, B, T, mask, depth, tree_err, stream));
+}
+
+size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                                               int32_t D, int32_t max_prefix_len, int32_t dtype,
+                                               int32_t num_splits) {
+    AttnPlan p;
+    if (make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, &p) != SV_OK)
+        return 0;
+    return p.ws_total;
+}
+
+int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tree,
+                             const sv_kv_cache *cache, const int32_t *prefix_len,
+                             int32_t max_prefix_len, const uint64_t *mask, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t T, int32_t D, float scale, float *out,
+                             void *workspace, size_t workspace_bytes, int32_t num_splits,
+                             hipStream_t stream) {
+    if (!cache) return SV_ERR_NULL;
+    const int dtype = cache->dtype;
+    AttnPlan plan;
+    int rc = make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, &plan);
+    if (rc != SV_OK) return rc;
+    if (B == 0) return SV_OK;
+    if (!q || !k_tree || !v_tree || !prefix_len || !mask || !out || !cache->k || !cache->v ||
+        !cache->block_table)
+        return SV_ERR_NULL;
+    rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
+    if (rc != SV_OK) return rc;
+    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+        return SV_ERR_ALIGN;
+    if (!workspace || workspace_bytes < plan.ws_total) return SV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SV_ERR_ALIGN;
+
+    AttnArgs a;
+    a.q = q;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.cache = view_of(cache);
+    a.prefix_len = prefix_len;
+    a.max_prefix_len = max_prefix_len;
+    a.mask = mask;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.D = D;
+    a.scale = scale;
+    a.out = out;
+    a.ws_o = static_cast<float *>(workspace);
+    a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_o);
+    hipError_t e = plan.mfma ? launch_attn_mfma(a, plan, stream)
+                             : launch_attn_valu(a, plan, dtype, stream);
+    if (e != hipSuccess) return SV_ERR_HIP;
+    return hip_status(launch_attn_reduce(a, plan, stream));
+}
+
+size_t sv_accept_longest_path_workspace_size(int32_t B, int32_t T, int64_t V) {
+    if (B < 0 || T < 1 || T > 64 || V < 1 || V > INT_MAX) return 0;
+    ArgmaxPlan p;
+    if (make_argmax_plan((int64_t)B * T, V, &p) != 0) return 0;
+    return round256(p.ws_bytes);
+}
+
+int sv_accept_longest_path(const float *logits, const int32_t *draft, const int32_t *parents,
+                           const int32_t *tree_err, int32_t B, int32_t T, int64_t V,
+                           int32_t *argmax_out, int32_t *accepted_len, int32_t *accepted_nodes,
+                           int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (B < 0 || V < 1) return SV_ERR_SHAPE;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    int64_t tmp;
+    if (V > INT_MAX || !prod_ok({(int64_t)B, T, V, 4}, &tmp)) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!logits || !draft || !parents || !accepted_len || !accepted_nodes || !out_tokens)
+        return SV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return SV_ERR_ALIGN;
+    ArgmaxPlan p;
+    if (make_argmax_plan((int64_t)B * T, V, &p) != 0) return SV_ERR_SHAPE;
+    if (!workspace || workspace_bytes < p.ws_bytes) return SV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SV_ERR_ALIGN;
+    hipError_t e = launch_argmax_partial(logits, (int64_t)B * T, V, p, workspace, stream);
+    if (e != hipSuccess) return SV_ERR_HIP;
+    return hip_status(launch_accept(workspace, p, draft, parents, tree_err, B, T, argmax_out,
+                                    accepted_len, accepted_nodes, out_tokens, stream));
+}
+
+int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
+                 const int32_t *accepted_nodes, const int32_t *tree_err,
+                 const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                 int32_t *new_prefix_len, int32_t B, int32_t Hkv, int32_t T, int32_t D,
+                 hipStream_t stream) {
+    if (!cache) return SV_ERR_NULL;
+    if (B < 0 || max_prefix_len < 0) return SV_ERR_SHAPE;
+    if (Hkv <= 0) return SV_ERR_GQA;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    const int dtype = cache->dtype;
+    const int es = esize_of(dtype);
+    if (es == 0) return SV_ERR_DTYPE;
+    int64_t tmp;
+    if (!prod_ok({(int64_t)B, Hkv, T, D, es}, &tmp)) return SV_ERR_OVERFLOW;
+    if ((int64_t)max_prefix_len + T > INT_MAX) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!k_tree || !v_tree || !accepted_len || !accepted_nodes || !prefix_len || !cache->k ||
+        !cache->v || !cache->block_table)
+        return SV_ERR_NULL;
+    int rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
+    if (rc != SV_OK) return rc;
+    if (!aligned16(k_tree) || !aligned16(v_tree)) return SV_ERR_ALIGN;
+    return hip_status(launch_kv_commit(k_tree, v_tree, accepted_len, accepted_nodes, tree_err,
+                                       cache->k, cache->v, view_of(cache), prefix_len,
+                                       max_prefix_len, new_prefix_len, B, Hkv, T, D, es,
+                                       stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// sv_internal.h -- shared declarations of the gfx950 kernels behind include/sv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kNumCU = 256;     // MI355X compute units (8 XCDs x 32)
+constexpr int kNumXCD = 8;
+constexpr int kKeyTile = 32;    // keys per attention tile; split sizes are multiples of it
+
+// Paged cache as seen by a kernel (element strides).
+struct CacheView {
+    const void *k;
+    const void *v;
+    const int32_t *table;
+    int32_t bs;
+    int32_t max_blocks;
+    int64_t num_blocks;
+    int64_t bstride;
+    int64_t hstride;
+    int64_t rstride;
+};
+
+// How one attention call is cut into workgroups.
+struct AttnPlan {
+    int mfma;          // 1: MFMA kernel (bf16, >= 16 rows per kv head); 0: VALU kernel
+    int R;             // query rows per kv head = (Hq / Hkv) * T, row r = g * T + i
+    int rows_per_wg;   // rows one workgroup owns
+    int n_rg;          // row groups per kv head
+    int nthreads;      // threads per workgroup
+    int S;             // prefix chunks (splits) per sequence
+    int C;             // keys per chunk, multiple of kKeyTile
+    size_t ws_o;       // bytes of partial outputs  [B][Hkv][S][R][D] fp32
+    size_t ws_ml;      // bytes of partial (m, l)   [B][Hkv][S][R][2] fp32
+    size_t ws_total;
+};
+
+struct AttnArgs {
+    const void *q;
+    const void *k_tree;
+    const void *v_tree;
+    CacheView cache;
+    const int32_t *prefix_len;
+    int32_t max_prefix_len;
+    const uint64_t *mask;
+    int32_t B, Hq, Hkv, T, D;
+    float scale;
+    float *out;
+    float *ws_o;
+    float *ws_ml;
+};
+
+// Returns 0 and fills *p, or a negative sv_status for unsupported shapes.
+int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int dtype,
+                   int num_splits, AttnPlan *p);
+
+hipError_t launch_tree_mask(const int32_t *parents, int B, int T, uint64_t *mask,
+                            int32_t *depth, int32_t *tree_err, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
+hipError_t launch_attn_valu(const AttnArgs &a, const AttnPlan &p, int dtype,
+                            hipStream_t stream);
+hipError_t launch_attn_reduce(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
+
+// Vocab argmax in chunks: partial (value, index) pairs [rows][chunks].
+struct ArgmaxPlan {
+    int64_t chunk;     // elements per chunk
+    int nchunks;       // chunks per row
+    size_t ws_bytes;
+};
+int make_argmax_plan(int64_t rows, int64_t V, ArgmaxPlan *p);
+hipError_t launch_argmax_partial(const float *logits, int64_t rows, int64_t V,
+                                 const ArgmaxPlan &p, void *ws, hipStream_t stream);
+hipError_t launch_accept(const void *ws, const ArgmaxPlan &p, const int32_t *draft,
+                         const int32_t *parents, const int32_t *tree_err, int B, int T,
+                         int32_t *argmax_out, int32_t *accepted_len, int32_t *accepted_nodes,
+                         int32_t *out_tokens, hipStream_t stream);
+
+hipError_t launch_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
+                            const int32_t *accepted_nodes, const int32_t *tree_err,
+                            void *k_cache, void *v_cache, const CacheView &c,
+                            const int32_t *prefix_len, int32_t max_prefix_len,
+                            int32_t *new_prefix_len, int B, int Hkv, int T, int D, int esize,
+                            hipStream_t stream);
+
+}  // namespace sv
