@@ -141,7 +141,7 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  *   prefix_len int32 [B] device; max_prefix_len host upper bound of prefix_len
  *   mask    from sv_build_tree_mask
  *   out     float32 [B][T][Hq][D]   (layout [q_seq_len, num_heads, head_dim] per sequence)
- *   scale   usually 1/sqrt(D)
+ *   scale   softmax scale, usually 1/sqrt(D); must be positive and finite
  *   workspace  device, >= sv_tree_verify_attention_workspace_size(...) bytes,
  *              256-byte aligned; scratch for per-split partial results
  *   num_splits 0 = automatic; otherwise the number of prefix chunks per sequence
@@ -149,7 +149,8 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  * the exact softmax attention to within bf16 rounding of the probabilities.
  * Prefix rows whose block-table entry is outside [0, num_blocks) are left out.
  * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, max_prefix_len < 0, block_size not a
- * positive multiple of 16, num_splits < 0, strides not positive),
+ * positive multiple of 16, num_splits < 0, strides not positive, scale not
+ * positive and finite),
  * SV_ERR_GQA, SV_ERR_HEAD_DIM, SV_ERR_TREE_SIZE, SV_ERR_DTYPE, SV_ERR_CAPACITY
  * (max_prefix_len + T > max_blocks_per_seq * block_size), SV_ERR_ALIGN,
  * SV_ERR_OVERFLOW, SV_ERR_WORKSPACE, SV_ERR_HIP.
@@ -208,8 +209,9 @@ int sv_accept_longest_path(const float *logits, const int32_t *draft, const int3
  * accepted_len outside [0, T], a node index outside [0, T), a block-table entry
  * outside [0, num_blocks)) is left untouched and new_prefix_len[b] =
  * prefix_len[b].  new_prefix_len may be NULL, or may alias prefix_len.
- * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_TREE_SIZE, SV_ERR_HEAD_DIM,
- * SV_ERR_DTYPE, SV_ERR_CAPACITY, SV_ERR_ALIGN, SV_ERR_OVERFLOW, SV_ERR_HIP.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_GQA (Hkv <= 0), SV_ERR_TREE_SIZE,
+ * SV_ERR_HEAD_DIM, SV_ERR_DTYPE, SV_ERR_CAPACITY, SV_ERR_ALIGN, SV_ERR_OVERFLOW,
+ * SV_ERR_HIP.
  */
 int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                  const int32_t *accepted_nodes, const int32_t *tree_err,

@@ -59,10 +59,10 @@ def cache(**kw):
 
 
 def attn(lib, c=None, q=FAKE, B=2, Hq=8, Hkv=2, T=8, D=256, maxp=100, ws=FAKE, wsb=1 << 30,
-         splits=0, out=FAKE, null_cache=False):
+         splits=0, out=FAKE, null_cache=False, scale=0.0625):
     c = c or cache()
     return lib.sv_tree_verify_attention(q, FAKE, FAKE, None if null_cache else ctypes.byref(c),
-                                        FAKE, maxp, FAKE, B, Hq, Hkv, T, D, 0.0625, out, ws, wsb,
+                                        FAKE, maxp, FAKE, B, Hq, Hkv, T, D, scale, out, ws, wsb,
                                         splits, None)
 
 
@@ -88,6 +88,8 @@ def test_attention_validation(lib):
     assert attn(lib, B=0, null_cache=False) == 0
     assert attn(lib, c=cache(block_table=None)) == -1
     assert attn(lib, c=cache(num_blocks=1 << 62, block_stride=1 << 20)) == -8
+    assert attn(lib, scale=0.0) == -2 and attn(lib, scale=-1.0) == -2
+    assert attn(lib, scale=float("inf")) == -2 and attn(lib, scale=float("nan")) == -2
 
 
 def test_attention_workspace_size(lib):

@@ -25,8 +25,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], obj_dir: str) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -34,20 +34,21 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build_library(extra: list[str] | None = None, jobs: int = 8) -> str:
-    """Compile every csrc/*.hip and link libsv.so next to this file."""
+def build_library(extra: list[str] | None = None, jobs: int = 8, out: str = LIB,
+                  obj_dir: str = OBJ_DIR) -> str:
+    """Compile every csrc/*.hip and link libsv.so (next to this file by default)."""
     extra = extra or []
-    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, obj_dir), srcs))
+    tmp = out + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -90,7 +90,7 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
         const int dsplit = D / 256;
         const int blocks = (R + 31) / 32;
         int nw = blocks * dsplit;
-        nw = nw > 8 ? 8 : nw;
+        nw = nw > kAttnMaxWaves ? kAttnMaxWaves : nw;
         p->rows_per_wg = (nw / dsplit) * 32;
         p->nthreads = 64 * nw;
     } else {
@@ -168,6 +168,7 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
                              void *workspace, size_t workspace_bytes, int32_t num_splits,
                              hipStream_t stream) {
     if (!cache) return SV_ERR_NULL;
+    if (!(scale > 0.0f) || scale > 3.0e38f) return SV_ERR_SHAPE;  // positive and finite
     const int dtype = cache->dtype;
     AttnPlan plan;
     int rc = make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, &plan);

@@ -17,6 +17,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNumCU = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCD = 8;
 constexpr int kKeyTile = 32;    // keys per attention tile; split sizes are multiples of it
+#ifndef SV_ATTN_MAX_WAVES
+#define SV_ATTN_MAX_WAVES 8
+#endif
+constexpr int kAttnMaxWaves = SV_ATTN_MAX_WAVES;  // wavefronts per attention workgroup (<= 8)
 
 // Paged cache as seen by a kernel (element strides).
 struct CacheView {
