@@ -81,6 +81,22 @@ def test_long_reduced_splits(orc, splits):
     run_case(orc, w, 3, num_splits=splits)
 
 
+@pytest.mark.parametrize("bs", [32, 48, 64, 256])
+def test_block_sizes(orc, bs):
+    # cache blocks larger than a 16-key group: both groups of a tile often share a block
+    w = wl.scaled(wl.WORKLOADS["long32k"], name=f"bs{bs}", B=2, prefix=(1501, 2000), V=2048,
+                  block_size=bs)
+    run_case(orc, w, 5)
+
+
+def test_chunk_beyond_staged_table(orc):
+    # one chunk of 40000 keys in 16-key blocks touches 2500 table entries, more than
+    # the kernel stages in LDS, so its tiles read the block table directly
+    w = wl.scaled(wl.WORKLOADS["long32k"], name="chunk40k", B=1, Hq=8, Hkv=2,
+                  prefix=(40000, 40000), V=2048)
+    run_case(orc, w, 6, num_splits=1, rows=sample_rows(w, 32, 3))
+
+
 def test_peaked_attention(orc):
     """Sharp softmax (Q, K with std 3): outputs of order one, so 1e-2 is tight."""
     w = wl.scaled(wl.WORKLOADS["long32k"], name="peaked", B=2, prefix=(700, 900), V=2048,

@@ -10,27 +10,28 @@
 // output and its (reference max, sum) per row, merged afterwards by attn_reduce.
 //
 // Organisation (8 wavefronts per workgroup, two per SIMD, one workgroup per CU):
-//   * a 32-row block of queries belongs to DSPLIT wavefronts (1 at head_dim 256,
-//     2 at head_dim 512); each keeps the Q fragments of its share of head_dim in
-//     registers and owns that share of the output;
+//   * a wavefront owns 32 query rows as two 16-row blocks (with head_dim 512, two
+//     wavefronts share them, each with half of head_dim); their Q fragments stay in
+//     registers and the wavefront owns their output accumulators;
 //   * keys stream through an NST-deep ring of LDS stages, 32 keys of K and V per
 //     stage, filled by direct global->LDS loads (global_load_lds_dwordx4) issued
-//     NST-1 tiles ahead, so HBM latency hides behind the matrix work of the tiles
-//     in between; one barrier per tile;
-//   * LDS rows are padded (K by 16 bytes, V by 64 bytes) so that the K fragment reads
-//     (ds_read_b128, 16 lanes per LDS cycle) and the V fragment reads
-//     (ds_read_b64_tr_b16, a transposing read, 32 lanes per cycle) each touch 64
-//     distinct banks, and every fragment address is one base register plus an
-//     immediate;
-//   * scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16 with keys
-//     as M and query rows as N), so each lane holds one query row and 16 of the
-//     tile's keys: the row max needs one swap between lane halves; with DSPLIT = 2
-//     the two partial score tiles are summed through LDS first;
-//   * the output is accumulated transposed, O^T = V^T P^T, so a lane keeps the
-//     accumulators of the row it computed probabilities for; inside a 16-key step
-//     the key order follows the score fragment's register order, so the P^T
-//     fragment is the score registers as they stand, and the transposing read
-//     delivers V^T in exactly that key order;
+//     ahead of use, so HBM latency hides behind the matrix work; one barrier per tile;
+//   * scores are formed transposed, S^T = K Q^T, as 2 x 2 blocks of
+//     v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows each): four independent
+//     accumulation chains.  A lane holds 8 of a row's 32 keys, so the row max takes
+//     two lane swaps; with head_dim 512 the two partial score tiles are summed
+//     through LDS first;
+//   * the output is accumulated transposed, O^T = V^T P^T, in 16 x 16 blocks, so a
+//     lane keeps the accumulators of the rows it computed probabilities for; the key
+//     order inside the 32-key step follows the score registers, so the P^T fragment is
+//     the score registers as they stand, and the transposing LDS read
+//     (ds_read_b64_tr_b16) delivers V^T in exactly that key order;
+//   * LDS rows are padded (K by 16 bytes, V by 32 bytes): the K fragment reads
+//     (ds_read_b128, 16 lanes per LDS cycle) and the V fragment reads (32 lanes per
+//     cycle) each touch 64 distinct banks, and every fragment address is one base
+//     register plus an immediate;
+//   * with head_dim 256 the wavefronts run in two groups half a tile apart
+//     (ping-pong), so one wavefront's softmax overlaps the other's matrix work;
 //   * the reference max only moves when a tile raises it by more than 2^8, so the
 //     accumulators are rarely rescaled (the merged result does not depend on the
 //     reference values used).
@@ -42,22 +43,41 @@ namespace {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
+constexpr int kTblMax = 2048;  // block-table entries of one chunk that fit the LDS copy
 
 template <int D>
 struct MCfg {
-    static constexpr int DSPLIT = D / 256;          // wavefronts sharing one row block
+    static constexpr int DSPLIT = D / 256;          // wavefronts sharing 32 rows
     static constexpr int DW = D / DSPLIT;           // head_dim share of one wavefront
-    static constexpr int KS = DW / 16;              // k-steps of S^T = K Q^T
-    static constexpr int DB = DW / 32;              // 32-wide d blocks of O^T
-    static constexpr int KROW = D * 2 + 16;         // padded K row in LDS
-    static constexpr int VROW = D * 2 + 64;         // padded V row in LDS
-    static constexpr int KTILE = kKeyTile * KROW;
-    static constexpr int STAGE_BYTES = kKeyTile * (KROW + VROW);  // K tile then V tile
-    static constexpr int NST = D == 256 ? 4 : 2;    // ring depth
-    static constexpr int NI = 2 * kKeyTile / kWaves;          // row loads per wavefront per tile
-    static constexpr int XBYTES = DSPLIT > 1 ? kWaves / 2 * 64 * 16 * 4 : 0;  // score exchange
-    static constexpr int SMEM = NST * STAGE_BYTES + XBYTES;
+    static constexpr int KS = DW / 32;              // 32-wide k-steps of S^T = K Q^T
+    static constexpr int DB = DW / 16;              // 16-wide d blocks of O^T
+    // An LDS tile is made of 1 KB units, each filled by one wavefront-wide direct load:
+    // with head_dim 256 unit p holds keys p and p + 16 of the tile side by side, with
+    // head_dim 512 unit p holds key p.  Units are padded (K by 16 bytes, V by 32) so
+    // that the fragment reads touch 64 distinct banks.
+    static constexpr int UNITS = kKeyTile * D * 2 / 1024;    // 16 or 32
+    static constexpr int KU = 1024 + 16;
+    static constexpr int VU = 1024 + 32;
+    static constexpr int KHALF = D == 256 ? 512 : 16 * KU;   // key r + 16 relative to key r
+    static constexpr int VHALF = D == 256 ? 512 : 16 * VU;
+    static constexpr int KTILE = UNITS * KU;
+    static constexpr int STAGE_BYTES = UNITS * (KU + VU);    // K tile then V tile
+    static constexpr int NST = D == 256 ? 4 : 2;             // ring depth
+#ifndef SV_ATTN_PINGPONG
+#define SV_ATTN_PINGPONG 1
+#endif
+    // ping-pong scheduling needs no workgroup-wide barrier inside a tile, so not with
+    // the paired score exchange of DSPLIT = 2
+    static constexpr bool PINGPONG = SV_ATTN_PINGPONG && DSPLIT == 1;
+    static constexpr int LOOK = PINGPONG ? NST - 2 : NST - 1;   // tiles loaded ahead
+    static constexpr int NI = 2 * UNITS / kWaves;               // loads per wavefront per tile
+    static constexpr int VMWAIT = NI * (LOOK - 1);              // loads left in flight at a wait
     static constexpr int ROWS_PER_WG = kWaves / DSPLIT * 32;
+    static constexpr int XBYTES = DSPLIT > 1 ? kWaves / 2 * 64 * 16 * 4 : 0;  // score exchange
+    static constexpr int TBL_OFF = NST * STAGE_BYTES + XBYTES;  // staged block-table entries
+    static constexpr int MASK_OFF = TBL_OFF + kTblMax * 4;      // ancestor-mask rows
+    static constexpr int SMEM = MASK_OFF + ROWS_PER_WG * 8;
+    static_assert(KS % NI == 0 || NI % KS == 0, "load spacing");
 };
 
 struct MfmaParams {
@@ -93,26 +113,45 @@ __device__ __forceinline__ int xcd_logical_id() {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Block-table entry of prefix position pos, or -1 when out of range.  The table is
-// read through the constant address space: with a uniform pos this is a scalar load,
-// which keeps the vector-memory counter free for the tile loads.
-__device__ __forceinline__ int block_of(const MfmaParams &p, int b, int pos) {
+// Block-table entry number `idx` of sequence b, or -1 when it is out of range.  The
+// table is read through the constant address space: with a uniform index this is a
+// scalar load, which keeps the vector-memory counter free for the tile loads.
+__device__ __forceinline__ int table_entry(const MfmaParams &p, int b, int idx) {
     const __attribute__((address_space(4))) int32_t *tbl =
         (const __attribute__((address_space(4))) int32_t *)p.table;
-    const int blk = tbl[(int64_t)b * p.max_blocks + pos / p.bs];
+    const int blk = tbl[(int64_t)b * p.max_blocks + idx];
     return (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+}
+
+// Position of a prefix key inside the paged cache: (block number in the sequence's
+// table, row inside the block).  Tiles advance by 32 keys, so positions are carried
+// forward by additions instead of divisions by the block size (a multiple of 16).
+struct Cursor {
+    int idx;
+    int slot;
+};
+
+__device__ __forceinline__ Cursor cursor_add(Cursor c, int n, int bs) {
+    c.slot += n;
+    while (c.slot >= bs) {  // n <= 32 and bs >= 16: at most two steps
+        c.slot -= bs;
+        ++c.idx;
+    }
+    return c;
 }
 
 // One 16-byte direct global->LDS load per lane: lane l's bytes land at LDS address
 // lds_base + 16 * l.  Written as inline assembly so that the compiler does not see an
 // LDS write it cannot disambiguate (it would then drain every load before each LDS
-// read); completion is tracked explicitly with vmcnt.  M0 carries the LDS base; an
-// SALU write of M0 needs one wait state before an LDS-DMA instruction reads it.
+// read); completion is tracked explicitly with vmcnt, and the stages a load writes
+// are ordered against their readers by the barriers (which carry memory clobbers).
+// M0 carries the LDS base; an SALU write of M0 needs one wait state before an
+// LDS-DMA instruction reads it.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
+                 : "m0");
 }
 
 // Workgroup barrier for LDS traffic only (no wait on the tile loads in flight).
@@ -120,52 +159,152 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until at most N of this wavefront's tile loads are still in flight (loads
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char *)p;
 }
 
-// Issue this wavefront's share of the direct global->LDS loads of one tile (keys
-// [k0, k0 + 32) of K and V) into one ring stage: wavefronts 0-3 load K rows, 4-7 V
-// rows, eight rows each, one row per load (rows are padded in LDS, so a load never
-// spans two rows).  Keys past kend (and prefix keys whose block is out of range)
-// load an in-range row instead; the score mask removes them.
-template <int D>
-__device__ __forceinline__ void issue_tile(const MfmaParams &p, int b, int kvh, bool tree,
-                                           int k0, int kend, unsigned char *stage) {
-    using Cf = MCfg<D>;
-    constexpr int LANES = D / 8;  // 16-byte pieces per row: 32 or 64 lanes
-    const int lane = threadIdx.x & 63;
-    const int w = uni(threadIdx.x >> 6);
-    const int tensor = w >> 2;            // 0: K, 1: V
-    const int row0 = (w & 3) * Cf::NI;    // eight rows inside one 16-key group
-    const __bf16 *src0;
-    int64_t step;                         // elements between consecutive rows
-    int pos0 = k0 + row0;
-    pos0 = pos0 < kend ? pos0 : kend - 1;
-    if (tree) {
-        src0 = (tensor ? p.vt : p.kt) + (((int64_t)b * p.Hkv + kvh) * p.T + pos0) * D;
-        step = D;
-    } else {
-        int blk = block_of(p, b, pos0);
-        blk = blk < 0 ? 0 : blk;
-        src0 = (tensor ? p.vc : p.kc) + (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
-               (int64_t)(pos0 % p.bs) * p.rstride;
-        step = p.rstride;
+// Block-table entries of a chunk, checked against the pool size (-1: out of range),
+// copied to LDS at kernel start when at most kTblMax of them; each wavefront then
+// reads them through a 64-entry window held one entry per lane, so a lookup is a lane
+// read, not a memory access.  Larger chunks read the table directly.
+struct BlockLookup {
+    const int *tbl;  // LDS copy, indexed relative to idx0
+    int idx0;        // first table entry of the chunk
+    int nent;        // entries the chunk touches
+    bool staged;     // tbl holds all of them
+    int win;         // lane i: relative entry wbase + i (-1 past the end)
+    int wbase;
+};
+
+__device__ __forceinline__ int lookup_entry(const MfmaParams &p, int b, BlockLookup &bl, int idx) {
+    if (!bl.staged) return table_entry(p, b, idx);
+    const int rel = idx - bl.idx0;
+    if (rel - bl.wbase >= 63) {  // lookups only move forward; keep rel and rel + 1 inside
+        bl.wbase = rel;
+        const int r = rel + (int)(threadIdx.x & 63);
+        bl.win = r < bl.nent ? bl.tbl[r] : -1;
     }
-    unsigned char *dst0 = stage + (tensor ? Cf::KTILE + row0 * Cf::VROW : row0 * Cf::KROW);
-    const int rowb = tensor ? Cf::VROW : Cf::KROW;
-#pragma unroll
-    for (int n = 0; n < Cf::NI; ++n) {
-        int pos = k0 + row0 + n;
-        pos = pos < kend ? pos : kend - 1;
-        const __bf16 *src = src0 + (int64_t)(pos - pos0) * step + lane * 8;
-        if (LANES == 64 || lane < LANES) dma16(src, lds_addr(dst0 + n * rowb));
-    }
+    return __builtin_amdgcn_readlane(bl.win, rel - bl.wbase);
 }
 
-// Validity of the 32 keys of a tile (bit kk: key k0 + kk is real), from uniform values.
-__device__ __forceinline__ uint32_t tile_valid(const MfmaParams &p, int b, bool tree, int k0,
-                                               int kend) {
+// Cache blocks of the two 16-key groups of a prefix tile (group 1 falls back to group
+// 0 when it lies past the chunk end; an out-of-range entry reads block 0, whose keys
+// the score mask removes).  Looked up one tile before the loads that use them.
+struct TileBlocks {
+    int blk[2];
+    int slot[2];
+};
+
+__device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, BlockLookup &bl,
+                                                    Cursor c, int k0, int kend) {
+    TileBlocks tb;
+    const int e0 = lookup_entry(p, b, bl, c.idx);
+    tb.blk[0] = e0 < 0 ? 0 : e0;
+    tb.slot[0] = c.slot;
+    tb.blk[1] = tb.blk[0];
+    tb.slot[1] = c.slot;
+    if (k0 + 16 < kend) {
+        // c.slot is a multiple of 16 below the block size (also a multiple of 16)
+        if (c.slot + 16 < p.bs) {
+            tb.slot[1] = c.slot + 16;
+        } else {
+            const int e1 = lookup_entry(p, b, bl, c.idx + 1);
+            tb.blk[1] = e1 < 0 ? 0 : e1;
+            tb.slot[1] = 0;
+        }
+    }
+    return tb;
+}
+
+// One wavefront's share of a tile's loads: NI loads of 1 KB, load j filling LDS unit
+// (first unit + j) of the wavefront's tensor from row j (counted from each lane's first
+// row) of the source.  Prefix tiles are issued one load at a time between matrix
+// products of the tile before; tree tiles (rows past the last node clamped to it) and
+// the trailing repeat slots are issued whole when prepared.  Wavefronts 0-3 load K,
+// 4-7 load V, a quarter of the units each.
+struct TileLoad {
+    const unsigned char *src;   // per lane: its 16 bytes of the first row
+    int64_t step;               // bytes between successive rows
+    uint32_t lds;               // LDS address of the first unit
+    int ustride;                // bytes between units
+    bool spread;                // loads still to be issued one by one
+};
+
+__device__ __forceinline__ void load_unit(const TileLoad &t, int j) {
+    dma16(t.src + j * t.step, t.lds + j * t.ustride);
+}
+
+// Lane layout of a load: with head_dim 256 lanes 0-31 carry key p, 32-63 key p + 16
+// (16 bytes each); with head_dim 512 all 64 lanes carry key p.
+template <int D>
+__device__ __forceinline__ int load_lane_half(int q) {
+    return D == 256 ? (int)((threadIdx.x & 63) >> 5) : (q >> 1);
+}
+
+template <int D>
+__device__ __forceinline__ int load_lane_piece() {
+    return D == 256 ? (int)(threadIdx.x & 31) : (int)(threadIdx.x & 63);
+}
+
+template <int D>
+__device__ __forceinline__ TileLoad prepare_prefix(const MfmaParams &p, int kvh, const TileBlocks &tb,
+                                                   uint32_t stage) {
+    using Cf = MCfg<D>;
+    const int w = uni(threadIdx.x >> 6);
+    const int tensor = w >> 2;  // 0: K, 1: V
+    const int q = w & 3;
+    const int half = load_lane_half<D>(q);
+    const int blk = half ? tb.blk[1] : tb.blk[0];
+    // keys of one group stay inside its block: slot + 15 < block size
+    const int row = (half ? tb.slot[1] : tb.slot[0]) + (D == 256 ? 4 * q : 8 * (q & 1));
+    TileLoad t;
+    t.src = reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
+            ((int64_t)blk * p.bstride + (int64_t)kvh * p.hstride + (int64_t)row * p.rstride) * 2 +
+            load_lane_piece<D>() * 16;
+    t.step = p.rstride * 2;
+    t.ustride = tensor ? Cf::VU : Cf::KU;
+    t.lds = stage + (tensor ? Cf::KTILE : 0) + q * Cf::NI * t.ustride;
+    t.spread = true;
+    return t;
+}
+
+// Issues the whole tile; the returned descriptor re-reads the last node (for repeat
+// slots).
+template <int D>
+__device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int k0,
+                                               uint32_t stage) {
+    using Cf = MCfg<D>;
+    const int w = uni(threadIdx.x >> 6);
+    const int tensor = w >> 2;
+    const int q = w & 3;
+    const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
+                                ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + load_lane_piece<D>() * 16;
+    const int row = k0 + (D == 256 ? 4 * q + 16 * load_lane_half<D>(q) : 8 * q);
+    TileLoad t;
+    t.ustride = tensor ? Cf::VU : Cf::KU;
+    t.lds = stage + (tensor ? Cf::KTILE : 0) + q * Cf::NI * t.ustride;
+#pragma unroll
+    for (int j = 0; j < Cf::NI; ++j)
+        dma16(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
+    t.src = base + (int64_t)(p.T - 1) * (D * 2);
+    t.step = 0;
+    t.spread = false;
+    return t;
+}
+
+// Validity of the 32 keys of a prefix tile starting at cursor c (bit kk: key k0 + kk
+// exists and its block-table entry is in range).
+__device__ __forceinline__ uint32_t prefix_valid(const MfmaParams &p, int b, int k0, Cursor c,
+                                                 int kend, bool all_blocks_ok) {
+    if (all_blocks_ok && k0 + kKeyTile <= kend) return 0xffffffffu;
     uint32_t v = 0;
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
@@ -173,35 +312,84 @@ __device__ __forceinline__ uint32_t tile_valid(const MfmaParams &p, int b, bool 
         if (pos < kend) {
             const int n = kend - pos < 16 ? kend - pos : 16;
             uint32_t bits = (n == 16 ? 0xffffu : ((1u << n) - 1u)) << (16 * grp);
-            if (!tree && block_of(p, b, pos) < 0) bits = 0;
+            const int idx = c.idx + (c.slot + 16 * grp >= p.bs ? 1 : 0);
+            if (!all_blocks_ok && table_entry(p, b, idx) < 0) bits = 0;
             v |= bits;
         }
     }
     return v;
 }
 
+__device__ __forceinline__ uint32_t tree_valid(int k0, int T) {
+    const int n = T - k0;
+    return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
+
+// Per-wavefront state of the online softmax: two 16-row blocks per lane (rows
+// rb*16 + (lane & 15)), each with its reference max (log2 units) and partial sum.
 template <int D>
-__device__ __forceinline__ void tile_math(const unsigned char *ks, const unsigned char *vs,
-                                          float *xs, uint32_t kvalid, bool tree, int k0,
-                                          int dpart,
-                                          const bf16x8 (&qf)[MCfg<D>::KS], uint64_t mrow,
-                                          f32x16 (&o)[MCfg<D>::DB], float &mref, float &lsum,
-                                          float scale_log2) {
+struct RowState {
+    f32x4 o[2][MCfg<D>::DB];   // O^T accumulators: [row block][16-wide d block]
+    float mref[2];
+    float lsum[2];
+};
+
+#ifndef SV_ATTN_PERMLANE
+#define SV_ATTN_PERMLANE 1
+#endif
+
+// Max over the four 16-lane groups (lanes n, n + 16, n + 32, n + 48 end up equal).
+__device__ __forceinline__ float max_over_groups(float m) {
+#if SV_ATTN_PERMLANE
+    // gfx950 row swaps: permlane16_swap exchanges rows 1 and 3 of its first operand
+    // with rows 0 and 2 of its second, permlane32_swap the upper half of the first with
+    // the lower half of the second; with both operands equal, the two results hold the
+    // two partners of each lane pair.
+    const unsigned u = __float_as_uint(m);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(m);
+    const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+#else
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    return fmaxf(m, __shfl_xor(m, 32, 64));
+#endif
+}
+
+// First half of a tile: scores, mask, online softmax (rescaling the accumulators when
+// the reference max moves); leaves the bf16 P^T fragments in pf[row block].
+// Lane l = 16 g + n: score registers sacc[rb][kb][r] hold row rb*16 + n, key
+// kb*16 + 4g + r.  hook(kstep) runs before the matrix products of each k-step (the
+// caller issues tile loads there).
+template <int D, class Hook>
+__device__ __forceinline__ void tile_scores(const unsigned char *ks, float *xs, uint32_t kvalid,
+                                            bool tree, int k0, int dpart,
+                                            const bf16x8 (&qf)[2][MCfg<D>::KS],
+                                            const uint64_t *mrow, RowState<D> &st,
+                                            float scale_log2, bf16x8 (&pf)[2], Hook &&hook) {
     using Cf = MCfg<D>;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int h = lane >> 5;
-    const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int n = lane & 15;
 
-    // ---- S^T = K Q^T over this wavefront's share of head_dim.
-    //      lane (h, l32) receives query row l32, keys (r/4)*8 + 4h + r%4, r = 0..15
-    f32x16 sacc;
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-    const unsigned char *kbase = ks + l32 * Cf::KROW + dpart * Cf::DW * 2 + h * 16;
+    // ---- S^T = K Q^T over this wavefront's share of head_dim: A = K (16 keys x 32 d,
+    //      lane: key kb*16 + n, d 32*ks + 8g .. +8), B = Q^T (lane: row rb*16 + n, same d)
+    f32x4 sacc[2][2];
+    for (int rb = 0; rb < 2; ++rb)
+        for (int kb = 0; kb < 2; ++kb) sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const unsigned char *kbase = ks + n * Cf::KU + dpart * Cf::DW * 2 + g * 16;
 #pragma unroll
     for (int kstep = 0; kstep < Cf::KS; ++kstep) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbase + kstep * 32);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kstep], sacc, 0, 0, 0);
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kbase + kstep * 64);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kbase + Cf::KHALF + kstep * 64);
+        hook(kstep);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            sacc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[rb][kstep], sacc[rb][0], 0, 0, 0);
+            sacc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[rb][kstep], sacc[rb][1], 0, 0, 0);
+        }
     }
     if (Cf::DSPLIT > 1) {
         // sum the two partial score tiles of a wavefront pair (same rows, halves of
@@ -209,101 +397,91 @@ __device__ __forceinline__ void tile_math(const unsigned char *ks, const unsigne
         // the sum back, so both hold bit-identical scores
         f32x4 *slot = reinterpret_cast<f32x4 *>(xs + ((w >> 1) * 64 + lane) * 16);
         if (dpart == 1)
-            for (int v = 0; v < 4; ++v)
-                slot[v] = f32x4{sacc[4 * v], sacc[4 * v + 1], sacc[4 * v + 2], sacc[4 * v + 3]};
+            for (int v = 0; v < 4; ++v) slot[v] = sacc[v >> 1][v & 1];
         lds_barrier();
         if (dpart == 0)
             for (int v = 0; v < 4; ++v) {
-                const f32x4 t = slot[v];
-                sacc[4 * v] += t[0];
-                sacc[4 * v + 1] += t[1];
-                sacc[4 * v + 2] += t[2];
-                sacc[4 * v + 3] += t[3];
-                slot[v] = f32x4{sacc[4 * v], sacc[4 * v + 1], sacc[4 * v + 2], sacc[4 * v + 3]};
+                sacc[v >> 1][v & 1] += slot[v];
+                slot[v] = sacc[v >> 1][v & 1];
             }
         lds_barrier();
         if (dpart == 1)
-            for (int v = 0; v < 4; ++v) {
-                const f32x4 t = slot[v];
-                sacc[4 * v] = t[0];
-                sacc[4 * v + 1] = t[1];
-                sacc[4 * v + 2] = t[2];
-                sacc[4 * v + 3] = t[3];
-            }
+            for (int v = 0; v < 4; ++v) sacc[v >> 1][v & 1] = slot[v];
     }
 
     // ---- mask, online softmax in log2 units; probabilities become bf16 P^T fragments.
     //      Full prefix tiles (the common case) need no masking at all.
     if (tree || kvalid != 0xffffffffu) {
-        const uint32_t kv = kvalid >> (4 * h);                          // keys 4h + ...
-        const uint64_t mt64 = tree ? (mrow >> (k0 + 4 * h)) : ~0ull;   // same key offset
+        const uint32_t kv = kvalid >> (4 * g);   // bit kb*16 + r: key kb*16 + 4g + r
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int off = (r >> 2) * 8 + (r & 3);
-            const bool ok = ((kv >> off) & 1u) && ((mt64 >> off) & 1ull);
-            sacc[r] = ok ? sacc[r] : kNegInf;
+        for (int rb = 0; rb < 2; ++rb) {
+            const uint64_t mt64 = tree ? (mrow[rb * 16] >> (k0 + 4 * g)) : ~0ull;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int off = kb * 16 + r;
+                    const bool ok = ((kv >> off) & 1u) && ((mt64 >> off) & 1ull);
+                    sacc[rb][kb][r] = ok ? sacc[rb][kb][r] : kNegInf;
+                }
         }
     }
-    float mt = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;   // row max over the tile, log2 units
-    const bool raise = mt > mref + kRescaleSlack;
-    if (__any(raise)) {
-        const float mnew = fmaxf(mref, mt);
-        const float alpha = mnew == kNegInf ? 1.0f : exp2f(mref - mnew);
-        lsum *= alpha;
+    for (int rb = 0; rb < 2; ++rb) {
+        float mt = fmaxf(fmaxf(fmaxf(sacc[rb][0][0], sacc[rb][0][1]),
+                               fmaxf(sacc[rb][0][2], sacc[rb][0][3])),
+                         fmaxf(fmaxf(sacc[rb][1][0], sacc[rb][1][1]),
+                               fmaxf(sacc[rb][1][2], sacc[rb][1][3])));
+        mt = max_over_groups(mt) * scale_log2;  // row max, log2 units
+        const bool raise = mt > st.mref[rb] + kRescaleSlack;
+        if (__any(raise)) {
+            const float mnew = fmaxf(st.mref[rb], mt);
+            const float alpha = mnew == kNegInf ? 1.0f : exp2f(st.mref[rb] - mnew);
+            st.lsum[rb] *= alpha;
 #pragma unroll
-        for (int db = 0; db < Cf::DB; ++db) o[db] *= alpha;
-        mref = mnew;
-    }
-    // exp2(s * scale_log2 - mref); a masked score (-inf) gives 0, and while a row has
-    // seen no valid key its reference is taken as 0
-    const float mneg = mref == kNegInf ? 0.0f : -mref;
-    bf16x8 pf[2];
-    float add = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[r], scale_log2, mneg));
-        const __bf16 pb = (__bf16)pr;
-        add += (float)pb;  // the denominator sums exactly the weights the numerator uses
-        pf[r >> 3][r & 7] = pb;
-    }
-    lsum += add;
-
-    // ---- O^T += V^T P^T.  The transposing read: in each 16-lane group, source lane
-    //      4r + q points at 4 consecutive d of key row (16*kk2 + 8t + 4h + r); lane j of
-    //      the group then receives that d column's 4 keys.
-    const int g = lane >> 4;
-    const int rr = (lane >> 2) & 3;
-    const int qq = lane & 3;
-    const unsigned char *vbase =
-        vs + (4 * h + rr) * Cf::VROW + dpart * Cf::DW * 2 + ((g & 1) * 16 + 4 * qq) * 2;
-#pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-#pragma unroll
-        for (int db = 0; db < Cf::DB; ++db) {
-            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(vbase + (16 * kk2) * Cf::VROW + db * 64));
-            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(vbase + (16 * kk2 + 8) * Cf::VROW + db * 64));
-            const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kk2], o[db], 0, 0, 0);
+            for (int db = 0; db < Cf::DB; ++db) st.o[rb][db] *= alpha;
+            st.mref[rb] = mnew;
         }
+        // exp2(s * scale_log2 - mref); a masked score (-inf) gives 0, and while a row
+        // has seen no valid key its reference is taken as 0
+        const float mneg = st.mref[rb] == kNegInf ? 0.0f : -st.mref[rb];
+        float add = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(sacc[rb][j >> 2][j & 3], scale_log2, mneg));
+            const __bf16 pb = (__bf16)pr;
+            add += (float)pb;  // the denominator sums exactly the weights the numerator uses
+            pf[rb][j] = pb;
+        }
+        st.lsum[rb] += add;
     }
 }
 
-// Wait until at most `left` tiles' loads of this wavefront are still in flight.
-template <int NI>
-__device__ __forceinline__ void wait_tiles_left(int left) {
-    static_assert(2 * NI < 64, "vmcnt range");
-    if (left >= 2) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
-    } else if (left == 1) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Second half of a tile: O^T += V^T P^T in 16 x 16 blocks (A = V^T: 16 d x 32 keys,
+// lane 16g + n holds d = db*16 + n and keys 4g + 0..3, 16 + 4g + 0..3, the P^T
+// fragment's key order).  The transposing read: in each 16-lane group, source lane
+// 4r + q points at 4 consecutive d of key row (16t + 4g + r); lane n of the group then
+// receives column db*16 + n of those 4 keys.  hook(db) runs before each d block.
+template <int D, class Hook>
+__device__ __forceinline__ void tile_pv(const unsigned char *vs, int dpart,
+                                        const bf16x8 (&pf)[2], RowState<D> &st, Hook &&hook) {
+    using Cf = MCfg<D>;
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int rr = (lane >> 2) & 3;
+    const int qq = lane & 3;
+    const unsigned char *vbase = vs + (4 * g + rr) * Cf::VU + dpart * Cf::DW * 2 + qq * 8;
+#pragma unroll
+    for (int db = 0; db < Cf::DB; ++db) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(vbase + db * 32));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(vbase + Cf::VHALF + db * 32));
+        hook(db);
+        const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[0], st.o[0][db], 0, 0, 0);
+        st.o[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[1], st.o[1][db], 0, 0, 0);
     }
 }
 
@@ -335,87 +513,187 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int h = lane >> 5;
-    const int l32 = lane & 31;
+    const int g = lane >> 4;
+    const int n = lane & 15;
     const int dpart = w % Cf::DSPLIT;
-    const int row = rg * Cf::ROWS_PER_WG + (w / Cf::DSPLIT) * 32 + l32;
-    const bool valid = row < p.R;
-    const int g = valid ? row / p.T : 0;
-    const int i = valid ? row - g * p.T : 0;
+    const int row_base = rg * Cf::ROWS_PER_WG + (w / Cf::DSPLIT) * 32 + n;
 
-    // Q fragments (B operand of S^T): lane holds row l32, d = dpart*DW + 16*kstep + 8h .. +8
-    bf16x8 qf[Cf::KS];
-    {
-        const __bf16 *qp = p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + g) * p.T + i) * D +
-                           dpart * Cf::DW + 8 * h;
+    // Q fragments (B operand of S^T): row rb*16 + n, d = dpart*DW + 32*kstep + 8g .. +8;
+    // and each row's ancestor mask, kept in LDS (read on tree tiles only)
+    bf16x8 qf[2][Cf::KS];
+    uint64_t *mrow = reinterpret_cast<uint64_t *>(smem + Cf::MASK_OFF) + (w / Cf::DSPLIT) * 32 + n;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = row_base + rb * 16;
+        const bool valid = row < p.R;
+        const int gh = valid ? row / p.T : 0;
+        const int i = valid ? row - gh * p.T : 0;
+        const __bf16 *qp = p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gh) * p.T + i) * D +
+                           dpart * Cf::DW + 8 * g;
 #pragma unroll
         for (int kstep = 0; kstep < Cf::KS; ++kstep) {
             if (valid) {
-                qf[kstep] = *reinterpret_cast<const bf16x8 *>(qp + 16 * kstep);
+                qf[rb][kstep] = *reinterpret_cast<const bf16x8 *>(qp + 32 * kstep);
             } else {
-                for (int j = 0; j < 8; ++j) qf[kstep][j] = (__bf16)0.0f;
+                for (int j = 0; j < 8; ++j) qf[rb][kstep][j] = (__bf16)0.0f;
             }
         }
+        const uint64_t m = valid ? p.mask[(int64_t)b * p.T + i] : 0ull;
+        if (g == 0 && dpart == 0) mrow[rb * 16] = m;
     }
-    const uint64_t mrow = valid ? p.mask[(int64_t)b * p.T + i] : 0ull;
-    // consume Q and the mask row here, so the loads are complete before the ring starts
-    // and no wait for them lands inside the tile loop
+    // consume Q and the mask rows here, so the loads are complete before the ring
+    // starts and no wait for them lands inside the tile loop
 #pragma unroll
-    for (int kstep = 0; kstep < Cf::KS; ++kstep) asm volatile("" ::"v"(qf[kstep]));
-    asm volatile("" ::"v"(mrow));
-
-    // ring prologue: tiles 0 .. NST-2 in flight
+    for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-    for (int u = 0; u < Cf::NST - 1; ++u) {
-        if (u < nt) {
-            const bool tr = u >= ntp;
-            const int k0 = tr ? (u - ntp) * kKeyTile : start + u * kKeyTile;
-            issue_tile<D>(p, b, kvh, tr, k0, tr ? p.T : end, smem + u * Cf::STAGE_BYTES);
-        }
+        for (int kstep = 0; kstep < Cf::KS; ++kstep) asm volatile("" ::"v"(qf[rb][kstep]));
     }
 
-    f32x16 o[Cf::DB];
-#pragma unroll
-    for (int db = 0; db < Cf::DB; ++db)
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float mref = kNegInf, lsum = 0.0f;
-
-    for (int u = 0; u < nt; ++u) {
-        // tiles issued after tile u that may still be in flight: min(NST - 2, nt - 1 - u)
-        const int left = min(Cf::NST - 2, nt - 1 - u);
-        wait_tiles_left<Cf::NI>(left);
-        lds_barrier();  // tile u visible to all; stage of tile u-1 free for reuse
-        const int un = u + Cf::NST - 1;
-        if (un < nt) {
-            const bool tr = un >= ntp;
-            const int k0 = tr ? (un - ntp) * kKeyTile : start + un * kKeyTile;
-            issue_tile<D>(p, b, kvh, tr, k0, tr ? p.T : end,
-                          smem + (un % Cf::NST) * Cf::STAGE_BYTES);
+    // block-table entries this chunk touches: all in range? (then full tiles need no
+    // masking); staged in LDS for the per-tile lookups when they fit
+    const Cursor cstart = {start / p.bs, start % p.bs};
+    const int nent = ntp > 0 ? (end - 1) / p.bs - cstart.idx + 1 : 0;
+    BlockLookup bl{reinterpret_cast<const int *>(smem + Cf::TBL_OFF), cstart.idx, nent,
+                   nent <= kTblMax, -1, -1000};
+    bool all_ok = true;
+    if (ntp > 0) {
+        int *tbl = reinterpret_cast<int *>(smem + Cf::TBL_OFF);
+        for (int i = (int)threadIdx.x; i < nent; i += blockDim.x) {
+            const int blk = p.table[(int64_t)b * p.max_blocks + cstart.idx + i];
+            const bool ok = blk >= 0 && blk < p.num_blocks;
+            all_ok = all_ok && ok;
+            if (bl.staged) tbl[i] = ok ? blk : -1;
         }
-        const unsigned char *st = smem + (u % Cf::NST) * Cf::STAGE_BYTES;
+        all_ok = __syncthreads_and(all_ok) != 0;  // also publishes the LDS copy
+    }
+
+    RowState<D> rs;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        rs.mref[rb] = kNegInf;
+        rs.lsum[rb] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < Cf::DB; ++db) rs.o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bf16x8 pf[2];
+
+    // Tile loads.  Every tile slot k < nt + LOOK issues exactly NI loads per wavefront
+    // (slots past the last tile repeat the last tile's sources into a free stage), so
+    // "tile u has landed" is always the same vmcnt, and the ring drains before exit.
+    const uint32_t smem0 = lds_addr(smem);
+    Cursor cissue = cstart;   // prefix tile whose block entries tbn holds
+    Cursor ccomp = cstart;    // next prefix tile to compute
+    TileBlocks tbn = ntp > 0 ? lookup_blocks(p, b, bl, cissue, start, end) : TileBlocks{{0, 0}, {0, 0}};
+    TileLoad tl;
+    auto prepare = [&](int k) {
+        const uint32_t stage = smem0 + (k % Cf::NST) * Cf::STAGE_BYTES;
+        if (k < ntp) {
+            tl = prepare_prefix<D>(p, kvh, tbn, stage);
+            cissue = cursor_add(cissue, kKeyTile, p.bs);
+            if (k + 1 < ntp) tbn = lookup_blocks(p, b, bl, cissue, start + (k + 1) * kKeyTile, end);
+        } else if (k < nt) {
+            tl = issue_tree<D>(p, b, kvh, (k - ntp) * kKeyTile, stage);
+        } else {
+            tl.lds = stage + (tl.lds - smem0) % Cf::STAGE_BYTES;
+            tl.spread = true;
+        }
+    };
+    auto issue = [&](int k) {
+        prepare(k);
+        if (tl.spread)
+#pragma unroll
+            for (int j = 0; j < Cf::NI; ++j) load_unit(tl, j);
+    };
+    auto nohook = [](int) {};
+    // spread the NI loads of the prepared tile over the k-steps of a score product ...
+    auto load_in_scores = [&](int kstep) {
+        constexpr int every = Cf::KS >= Cf::NI ? Cf::KS / Cf::NI : 1;
+        constexpr int per = Cf::NI > Cf::KS ? Cf::NI / Cf::KS : 1;
+        if (kstep % every == 0 && tl.spread)
+#pragma unroll
+            for (int j = 0; j < per; ++j) load_unit(tl, kstep / every * per + j);
+    };
+    // ... or over the d blocks of a PV product
+    auto load_in_pv = [&](int db) {
+        constexpr int every = Cf::DB / Cf::NI;
+        if (db % every == 0 && tl.spread) load_unit(tl, db / every);
+    };
+    auto scores = [&](int u, auto &&hook) {
+        const unsigned char *stg = smem + (u % Cf::NST) * Cf::STAGE_BYTES;
         const bool tr = u >= ntp;
-        const int k0 = tr ? (u - ntp) * kKeyTile : start + u * kKeyTile;
-        const uint32_t kvalid = tile_valid(p, b, tr, k0, tr ? p.T : end);
-        tile_math<D>(st, st + Cf::KTILE, xs, kvalid, tr, k0, dpart, qf, mrow, o, mref, lsum,
-                     p.scale_log2);
+        int k0;
+        uint32_t kvalid;
+        if (tr) {
+            k0 = (u - ntp) * kKeyTile;
+            kvalid = tree_valid(k0, p.T);
+        } else {
+            k0 = start + u * kKeyTile;
+            kvalid = prefix_valid(p, b, k0, ccomp, end, all_ok);
+            ccomp = cursor_add(ccomp, kKeyTile, p.bs);
+        }
+        tile_scores<D>(stg, xs, kvalid, tr, k0, dpart, qf, mrow, rs, p.scale_log2, pf, hook);
+    };
+    auto pv = [&](int u, auto &&hook) {
+        tile_pv<D>(smem + (u % Cf::NST) * Cf::STAGE_BYTES + Cf::KTILE, dpart, pf, rs, hook);
+    };
+
+    for (int k = 0; k < Cf::LOOK; ++k) issue(k);   // ring prologue
+    if (Cf::PINGPONG) {
+        // Wavefronts 4-7 run half a tile behind 0-3: barrier k sits at the start of
+        // tile k for the first group and between the softmax and the PV product of
+        // tile k-1 for the second, so on every SIMD one wavefront's vector work
+        // overlaps the other's matrix work.  After barrier k the stages of tiles k-1
+        // and k may still be read, so loads run two tiles ahead (stage of tile k-2),
+        // issued by the first group during its score product and by the second during
+        // its PV product.
+        if (w < 4) {
+            for (int u = 0; u < nt; ++u) {
+                wait_loads<Cf::VMWAIT>();
+                lds_barrier();
+                prepare(u + Cf::LOOK);
+                scores(u, load_in_scores);
+                pv(u, nohook);
+            }
+            lds_barrier();  // matches the second group's last barrier
+        } else {
+            wait_loads<Cf::VMWAIT>();
+            lds_barrier();
+            issue(Cf::LOOK);
+            for (int u = 0; u < nt; ++u) {
+                scores(u, nohook);
+                wait_loads<Cf::VMWAIT>();
+                lds_barrier();
+                prepare(u + 1 + Cf::LOOK);
+                pv(u, load_in_pv);
+            }
+        }
+    } else {
+        for (int u = 0; u < nt; ++u) {
+            wait_loads<Cf::VMWAIT>();
+            lds_barrier();  // tile u visible to all; stage of tile u-1 free for reuse
+            prepare(u + Cf::LOOK);
+            scores(u, load_in_scores);
+            pv(u, nohook);
+        }
     }
+    wait_loads<0>();  // the trailing repeat loads
 
     // ---- partial results: O (unnormalised), reference max (log2 units) and sum per row
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-    if (valid) {
-        const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
-        float *op = p.ws_o + base * D + dpart * Cf::DW;
 #pragma unroll
-        for (int db = 0; db < Cf::DB; ++db)
+    for (int rb = 0; rb < 2; ++rb) {
+        float ltot = rs.lsum[rb] + __shfl_xor(rs.lsum[rb], 16, 64);
+        ltot += __shfl_xor(ltot, 32, 64);
+        const int row = row_base + rb * 16;
+        if (row < p.R) {
+            const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
+            float *op = p.ws_o + base * D + dpart * Cf::DW + 4 * g;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 v = {o[db][4 * g4 + 0], o[db][4 * g4 + 1], o[db][4 * g4 + 2],
-                                 o[db][4 * g4 + 3]};
-                *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8 + 4 * h) = v;
+            for (int db = 0; db < Cf::DB; ++db)
+                *reinterpret_cast<f32x4 *>(op + db * 16) = rs.o[rb][db];
+            if (g == 0 && dpart == 0) {
+                p.ws_ml[base * 2 + 0] = rs.mref[rb];
+                p.ws_ml[base * 2 + 1] = ltot;
             }
-        if (h == 0 && dpart == 0) {
-            p.ws_ml[base * 2 + 0] = mref;
-            p.ws_ml[base * 2 + 1] = ltot;
         }
     }
 }
