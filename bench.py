@@ -49,58 +49,83 @@ def attention_traffic(inp, depth):
 
 
 def cpu_baseline(inp, budget_s=15.0):
-    """The oracle on sequence 0 of the workload (all its heads, nodes and stages)."""
+    """The oracle on whole sequences of the workload, one after another, until the time
+    budget is spent: mask, attention for every head and node, accept, commit."""
     import numpy as np
-    import torch
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as O
     from _support import to_np
 
     w = inp.w
-    b = 0
-    nblk = int((inp.block_table[b] >= 0).sum())
-    blocks = inp.block_table[b, :nblk].long()
-    kp = to_np(inp.k_pool.index_select(0, blocks))
-    vp = to_np(inp.v_pool.index_select(0, blocks))
-    table = np.arange(nblk, dtype=np.int32)[None]
-    _, Hkv, bs, D = inp.k_pool.shape
-    cache = O.Cache(k=kp, v=vp, table=table, block_size=bs, block_stride=Hkv * bs * D,
-                    head_stride=bs * D, row_stride=D, num_blocks=nblk,
-                    dtype=O.BF16 if w.dtype == "bf16" else O.F32)
-    parents = to_np(inp.parents[b:b + 1])
-    q, kt, vt = to_np(inp.q[b:b + 1]), to_np(inp.k_tree[b:b + 1]), to_np(inp.v_tree[b:b + 1])
-    P = to_np(inp.prefix_len[b:b + 1])
-    logits, draft = to_np(inp.logits[b:b + 1]), to_np(inp.draft[b:b + 1])
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     orc = O.Oracle()
-
-    # size the sample: time a few rows, then take as many heads as fit the budget
-    t0 = time.perf_counter()
-    rows = np.array([[0, 0, i] for i in range(min(w.T, threads))], dtype=np.int32)
-    mask, _, err = orc.build_tree_mask(parents)
-    orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
-                              nthreads=threads)
-    per_row = (time.perf_counter() - t0) / max(1, len(rows)) * threads
-    heads = max(1, min(w.Hq, int(budget_s / max(per_row * w.T / threads, 1e-9))))
-
-    t0 = time.perf_counter()
-    mask, _, err = orc.build_tree_mask(parents)
-    rows = np.array([[0, h, i] for h in range(heads) for i in range(w.T)], dtype=np.int32)
-    orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
-                              nthreads=threads)
-    t_attn = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    _, L, nodes, _ = orc.accept_longest_path(logits, draft, parents, err)
-    orc.kv_commit(kt, vt, L, nodes, err, cache, P, int(P.max()))
-    t_rest = time.perf_counter() - t1
-    # one sequence's step = attention over all Hq heads + accept + commit
-    t_seq = t_attn * (w.Hq / heads) + t_rest
-    t_step = t_seq * w.B
+    _, Hkv, bs, D = inp.k_pool.shape
+    done, spent, heads_used = 0, 0.0, w.Hq
+    for b in range(w.B):
+        nblk = int((inp.block_table[b] >= 0).sum())
+        blocks = inp.block_table[b, :nblk].long()
+        cache = O.Cache(k=to_np(inp.k_pool.index_select(0, blocks)),
+                        v=to_np(inp.v_pool.index_select(0, blocks)),
+                        table=np.arange(nblk, dtype=np.int32)[None], block_size=bs,
+                        block_stride=Hkv * bs * D, head_stride=bs * D, row_stride=D,
+                        num_blocks=nblk, dtype=O.BF16 if w.dtype == "bf16" else O.F32)
+        parents = to_np(inp.parents[b:b + 1])
+        q, kt, vt = to_np(inp.q[b:b + 1]), to_np(inp.k_tree[b:b + 1]), to_np(inp.v_tree[b:b + 1])
+        P = to_np(inp.prefix_len[b:b + 1])
+        logits, draft = to_np(inp.logits[b:b + 1]), to_np(inp.draft[b:b + 1])
+        heads = w.Hq
+        if b == 0:
+            # a sequence too large for the budget is sampled by heads (scaled to all heads)
+            rows = np.array([[0, 0, i] for i in range(w.T)], dtype=np.int32)
+            t0 = time.perf_counter()
+            mask, _, err = orc.build_tree_mask(parents)
+            orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale,
+                                      rows=rows, nthreads=threads)
+            t_head = time.perf_counter() - t0
+            heads = heads_used = max(1, min(w.Hq, int(budget_s / max(t_head, 1e-9))))
+        t0 = time.perf_counter()
+        mask, _, err = orc.build_tree_mask(parents)
+        rows = np.array([[0, h, i] for h in range(heads) for i in range(w.T)], dtype=np.int32)
+        orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
+                                  nthreads=threads)
+        t_attn = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        _, L, nodes, _ = orc.accept_longest_path(logits, draft, parents, err)
+        orc.kv_commit(kt, vt, L, nodes, err, cache, P, int(P.max()))
+        t_rest = time.perf_counter() - t1
+        spent += t_attn * (w.Hq / heads) + t_rest     # that sequence's full step
+        done += 1
+        if heads < w.Hq or spent >= budget_s:
+            break
+    t_step = spent / done * w.B
     return {"value": w.B * w.T / t_step, "unit": "verified tree tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"sequence 0 of {w.B}: mask, attention for {heads} of {w.Hq} q heads "
-                      f"x {w.T} nodes (scaled to all heads), accept over {w.V} logits, "
-                      f"commit; step time = {w.B} x that sequence; {t_attn + t_rest:.1f} s"}
+            "sample": f"sequences 0..{done - 1} of {w.B} in full (mask, attention for "
+                      f"{heads_used} of {w.Hq} q heads x {w.T} nodes"
+                      f"{' scaled to all heads' if heads_used < w.Hq else ''}, accept over "
+                      f"{w.V} logits, commit); step time = {w.B} x the mean sequence; "
+                      f"{spent:.1f} s of oracle time"}
+
+
+def counter_traffic(workload):
+    """HBM bytes per attention call from the committed rocprofv3 counter summary of this
+    workload, or None when the kernel sources have changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for name in fields.get("sources", "").split():
+        with open(os.path.join(ROOT, "tree_masked_verify_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if not fields.get("sources") or h.hexdigest() != fields.get("sources_sha256"):
+        return None
+    return int(fields["hbm_bytes_per_call"])
 
 
 def main():
@@ -196,7 +221,7 @@ def main():
                    "num_splits": args.splits, "seed": args.seed},
         "roofline": {"bound": "hbm", "kernel": "tree-verify attention (split + merge kernels)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name),
                      "bytes_per_launch": bytes_attn, "us_per_launch": round(ms_attn * 1e3, 2),
                      "mfma_tflops": round(tflops, 1),
                      "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
