@@ -23,11 +23,15 @@ FLAGS = [
     # no packed fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-file additions.  The head_dim-256 attention kernel handles finite scores and -inf
+# (masked keys) only; without NaN semantics its row maxima need no canonicalising
+# moves before each v_max.
+FILE_FLAGS = {"attn_mfma256.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra: list[str], obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

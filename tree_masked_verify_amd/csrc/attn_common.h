@@ -1,0 +1,203 @@
+// attn_common.h -- device helpers shared by the matrix-core attention kernels: the
+// kernel parameters, direct global->LDS tile loads and their bookkeeping, LDS-only
+// barriers, the paged-cache cursor and block-table lookups, and key validity.
+#pragma once
+
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTblMax = 2048;  // block-table entries of one chunk that fit the LDS copy
+
+struct MfmaParams {
+    const __bf16 *q;
+    const __bf16 *kt;
+    const __bf16 *vt;
+    const __bf16 *kc;
+    const __bf16 *vc;
+    const int32_t *table;
+    int32_t bs, max_blocks;
+    int64_t num_blocks, bstride, hstride, rstride;
+    const int32_t *prefix_len;
+    int max_P;
+    const uint64_t *mask;
+    int B, Hq, Hkv, T, G, R;
+    float scale_log2;
+    int S, C, n_rg, total;
+    float *ws_o;
+    float *ws_ml;
+};
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+__device__ __forceinline__ int xcd_logical_id() {
+    // consecutive workgroup ids are dealt round-robin to the 8 XCDs; give each XCD a
+    // contiguous range of logical ids, so the row groups of one (sequence, kv head,
+    // chunk) run side by side under one L2
+    const int n = gridDim.x;  // a multiple of kNumXCD
+    const int x = blockIdx.x;
+    return (x % kNumXCD) * (n / kNumXCD) + x / kNumXCD;
+}
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Block-table entry number `idx` of sequence b, or -1 when it is out of range.  The
+// table is read through the constant address space: with a uniform index this is a
+// scalar load, which keeps the vector-memory counter free for the tile loads.
+__device__ __forceinline__ int table_entry(const MfmaParams &p, int b, int idx) {
+    const __attribute__((address_space(4))) int32_t *tbl =
+        (const __attribute__((address_space(4))) int32_t *)p.table;
+    const int blk = tbl[(int64_t)b * p.max_blocks + idx];
+    return (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+}
+
+// Position of a prefix key inside the paged cache: (block number in the sequence's
+// table, row inside the block).  Tiles advance by 32 keys, so positions are carried
+// forward by additions instead of divisions by the block size (a multiple of 16).
+struct Cursor {
+    int idx;
+    int slot;
+};
+
+__device__ __forceinline__ Cursor cursor_add(Cursor c, int n, int bs) {
+    c.slot += n;
+    while (c.slot >= bs) {  // n <= 32 and bs >= 16: at most two steps
+        c.slot -= bs;
+        ++c.idx;
+    }
+    return c;
+}
+
+// One 16-byte direct global->LDS load per lane: lane l's bytes land at LDS address
+// lds_base + 16 * l.  Written as inline assembly so that the compiler does not see an
+// LDS write it cannot disambiguate (it would then drain every load before each LDS
+// read); completion is tracked explicitly with vmcnt, and the stages a load writes
+// are ordered against their readers by the barriers (which carry memory clobbers).
+// M0 carries the LDS base; an SALU write of M0 needs one wait state before an
+// LDS-DMA instruction reads it.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "m0");
+}
+
+// Workgroup barrier for LDS traffic only (no wait on the tile loads in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wavefront's tile loads are still in flight (loads
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+// Block-table entries of a chunk, checked against the pool size (-1: out of range),
+// copied to LDS at kernel start when at most kTblMax of them; each wavefront then
+// reads them through a 64-entry window held one entry per lane, so a lookup is a lane
+// read, not a memory access.  Larger chunks read the table directly.
+struct BlockLookup {
+    const int *tbl;  // LDS copy, indexed relative to idx0
+    int idx0;        // first table entry of the chunk
+    int nent;        // entries the chunk touches
+    bool staged;     // tbl holds all of them
+    int win;         // lane i: relative entry wbase + i (-1 past the end)
+    int wbase;
+};
+
+__device__ __forceinline__ int lookup_entry(const MfmaParams &p, int b, BlockLookup &bl, int idx) {
+    if (!bl.staged) return table_entry(p, b, idx);
+    const int rel = idx - bl.idx0;
+    if (rel - bl.wbase >= 63) {  // lookups only move forward; keep rel and rel + 1 inside
+        bl.wbase = rel;
+        const int r = rel + (int)(threadIdx.x & 63);
+        bl.win = r < bl.nent ? bl.tbl[r] : -1;
+    }
+    return __builtin_amdgcn_readlane(bl.win, rel - bl.wbase);
+}
+
+// Cache blocks of the two 16-key groups of a prefix tile (group 1 falls back to group
+// 0 when it lies past the chunk end; an out-of-range entry reads block 0, whose keys
+// the score mask removes).  Looked up one tile before the loads that use them.
+struct TileBlocks {
+    int blk[2];
+    int slot[2];
+};
+
+__device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, BlockLookup &bl,
+                                                    Cursor c, int k0, int kend) {
+    TileBlocks tb;
+    const int e0 = lookup_entry(p, b, bl, c.idx);
+    tb.blk[0] = e0 < 0 ? 0 : e0;
+    tb.slot[0] = c.slot;
+    tb.blk[1] = tb.blk[0];
+    tb.slot[1] = c.slot;
+    if (k0 + 16 < kend) {
+        // c.slot is a multiple of 16 below the block size (also a multiple of 16)
+        if (c.slot + 16 < p.bs) {
+            tb.slot[1] = c.slot + 16;
+        } else {
+            const int e1 = lookup_entry(p, b, bl, c.idx + 1);
+            tb.blk[1] = e1 < 0 ? 0 : e1;
+            tb.slot[1] = 0;
+        }
+    }
+    return tb;
+}
+
+// One wavefront's share of a tile's loads: NI loads of 1 KB, load j filling LDS unit
+// (first unit + j) of the wavefront's tensor from row j (counted from each lane's first
+// row) of the source.  Prefix tiles are issued one load at a time between matrix
+// products of the tile before; tree tiles (rows past the last node clamped to it) and
+// the trailing repeat slots are issued whole when prepared.  Wavefronts 0-3 load K,
+// 4-7 load V, a quarter of the units each.
+struct TileLoad {
+    const unsigned char *src;   // per lane: its 16 bytes of the first row
+    int64_t step;               // bytes between successive rows
+    uint32_t lds;               // LDS address of the first unit
+    int ustride;                // bytes between units
+    bool spread;                // loads still to be issued one by one
+};
+
+__device__ __forceinline__ void load_unit(const TileLoad &t, int j) {
+    dma16(t.src + j * t.step, t.lds + j * t.ustride);
+}
+
+// Validity of the 32 keys of a prefix tile starting at cursor c (bit kk: key k0 + kk
+// exists and its block-table entry is in range).
+__device__ __forceinline__ uint32_t prefix_valid(const MfmaParams &p, int b, int k0, Cursor c,
+                                                 int kend, bool all_blocks_ok) {
+    if (all_blocks_ok && k0 + kKeyTile <= kend) return 0xffffffffu;
+    uint32_t v = 0;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+        const int pos = k0 + 16 * grp;
+        if (pos < kend) {
+            const int n = kend - pos < 16 ? kend - pos : 16;
+            uint32_t bits = (n == 16 ? 0xffffu : ((1u << n) - 1u)) << (16 * grp);
+            const int idx = c.idx + (c.slot + 16 * grp >= p.bs ? 1 : 0);
+            if (!all_blocks_ok && table_entry(p, b, idx) < 0) bits = 0;
+            v |= bits;
+        }
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t tree_valid(int k0, int T) {
+    const int n = T - k0;
+    return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
+}
+
+}  // namespace
+}  // namespace sv
