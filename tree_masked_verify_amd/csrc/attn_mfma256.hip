@@ -34,6 +34,13 @@ namespace {
 
 namespace w4 {
 
+#ifndef SV_W4_KD
+#define SV_W4_KD 5  // K fragments read ahead (k-steps)
+#endif
+#ifndef SV_W4_VD
+#define SV_W4_VD 4  // V fragments read ahead (d blocks)
+#endif
+
 constexpr int D = 256;
 constexpr int kW = 4;                    // wavefronts per workgroup
 constexpr int kRowsPerWave = 64;
@@ -123,16 +130,23 @@ __device__ __forceinline__ void tile_scores(const unsigned char *ks, const bf16x
                                             f32x16 (&sacc)[2], Hook &&hook) {
     const int lane = threadIdx.x & 63;
     const unsigned char *kb = ks + key_offset(lane & 31, KU) + (lane >> 5) * 16;
+    // K fragments are read KD k-steps ahead of their products; the reads sit before the
+    // tile loads the hook issues (which the compiler does not move reads across)
+    constexpr int KD = SV_W4_KD;
+    bf16x8 a[KD + 1];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) a[k] = *reinterpret_cast<const bf16x8 *>(kb + k * 32);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + k * 32);
+        if (k + KD < KS) a[(k + KD) % (KD + 1)] = *reinterpret_cast<const bf16x8 *>(kb + (k + KD) * 32);
         hook(k);
+        const bf16x8 &ak = a[k % (KD + 1)];
         if (k == 0) {
-            mfma_vgpr_first(sacc[0], a, qf[0][0]);
-            mfma_vgpr_first(sacc[1], a, qf[1][0]);
+            mfma_vgpr_first(sacc[0], ak, qf[0][0]);
+            mfma_vgpr_first(sacc[1], ak, qf[1][0]);
         } else {
-            mfma_vgpr(sacc[0], a, qf[0][k]);
-            mfma_vgpr(sacc[1], a, qf[1][k]);
+            mfma_vgpr(sacc[0], ak, qf[0][k]);
+            mfma_vgpr(sacc[1], ak, qf[1][k]);
         }
     }
     vgpr_read_guard(sacc[0], sacc[1]);
@@ -200,29 +214,43 @@ __device__ __forceinline__ void tile_probs(const f32x16 (&sacc)[2], int c, const
     }
 }
 
-// O^T += V^T P^T over key chunk c of a tile (keys 16c .. 16c+15): A = V^T (32 d x 16
+// O^T += V^T P^T over one 16-key chunk c of a tile (keys 16c .. 16c+15), whose V rows
+// start at vc = the tile's V + 512 c; pc[rb] is the chunk's P^T fragment.  A = V^T (32 d x 16
 // keys; lane l: d 32 db + l % 32, keys 16c + 4 (l / 32) + 0..3 and 16c + 8 + 4 (l / 32)
 // + 0..3, the P^T fragment's order).  The transposing read: in each 16-lane group G,
 // source lane 4r + q points at 4 consecutive d (32 db + 16 (G % 2) + 4q ..) of key
 // 16c + 4 (G / 2) + r; lane j of the group then receives d 32 db + 16 (G % 2) + j of
 // those 4 keys.
-__device__ __forceinline__ void pv_chunk(const unsigned char *vs, int c, const bf16x8 (&pf)[2][2],
-                                         f32x16 (&o)[2][DB]) {
+__device__ __forceinline__ void pv_one(const unsigned char *vc, const bf16x8 (&pc)[2], f32x16 (&o)[2][DB]) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4;
     const int r = (lane >> 2) & 3;
     const int q = lane & 3;
-    const unsigned char *vb = vs + ((G >> 1) * 4 + r) * VU + (G & 1) * 32 + q * 8 + c * 512;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    const unsigned char *vb = vc + ((G >> 1) * 4 + r) * VU + (G & 1) * 32 + q * 8;
+    // V^T fragments of the next VD d blocks are in flight while a block's products run
+    constexpr int VD = SV_W4_VD;
+    bf16x8 v[VD + 1];
+    auto read = [&](int db) {
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vb + db * 64));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (lds_bf16x4 *)(vb + 8 * VU + db * 64));
-        const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[0][c], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[1][c], o[1][db], 0, 0, 0);
+        v[db % (VD + 1)] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+#pragma unroll
+    for (int db = 0; db < VD; ++db) read(db);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        if (db + VD < DB) read(db + VD);
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db % (VD + 1)], pc[0], o[0][db], 0, 0, 0);
+        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db % (VD + 1)], pc[1], o[1][db], 0, 0, 0);
     }
+}
+
+__device__ __forceinline__ void pv_chunk(const unsigned char *vs, int c, const bf16x8 (&pf)[2][2],
+                                         f32x16 (&o)[2][DB]) {
+    const bf16x8 pc[2] = {pf[0][c], pf[1][c]};
+    pv_one(vs + c * 512, pc, o);
 }
 
 // x *= s for an accumulator element held in an AGPR, without giving it a VGPR home (a
@@ -425,19 +453,30 @@ void attn_w4_kernel(MfmaParams p) {
         if (k % every == 0 && tl.spread) load_unit(tl, k / every);
     };
 
-    // ---- one tile: scores, optional masking, softmax, PV product; the softmax of key
-    // chunk 1 runs between the matrix instructions of chunk 0's PV product
+    // ---- one tile.  The PV products run one half-tile behind the softmax: tile u's
+    // max and chunk-0 probabilities go between the matrix instructions of tile u-1's
+    // chunk-1 PV product, and tile u's chunk-1 probabilities between those of its own
+    // chunk-0 PV product.  Before the first tile the pending product adds zeros.
+    bf16x8 pprev[2];  // P^T fragments of the pending chunk-1 product
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pprev[rb][j] = (__bf16)0.0f;
+    const unsigned char *vprev = smem + KTILE;  // V of the pending product (tile 0 at first)
     auto compute = [&](int u, bool masked, uint32_t kvalid, bool tree, int k0, auto &&hook) {
         const unsigned char *stg = smem + (u & (NST - 1)) * STAGE_BYTES;
         tile_scores(stg, qf, sacc, hook);
         if (masked) mask_scores(sacc, kvalid, tree, k0, mrow);
+        pv_one(vprev, pprev, o);
         tile_max(sacc, mref, lsum, alpha, mneg, p.scale_log2);
         tile_probs(sacc, 0, mneg, lsum, pf, p.scale_log2);
         settle(pf, 0);
         rescale(o, alpha);
         pv_chunk(stg + KTILE, 0, pf, o);
         tile_probs(sacc, 1, mneg, lsum, pf, p.scale_log2);
-        pv_chunk(stg + KTILE, 1, pf, o);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) pprev[rb] = pf[rb][1];
+        vprev = stg + KTILE + 512;
     };
 
     for (int k = 0; k < LOOK; ++k) issue(k);  // ring prologue
@@ -490,6 +529,7 @@ void attn_w4_kernel(MfmaParams p) {
         }
         compute(u, tr || kvalid != 0xffffffffu, kvalid, tr, k0, load_in_scores);
     }
+    pv_one(vprev, pprev, o);  // the last tile's chunk-1 product
     wait_loads<0>();  // the trailing repeat loads
 
     // ---- partial results: O (unnormalised), reference max (log2 units) and sum per row;
