@@ -14,7 +14,8 @@
 //     registers (256 AGPRs), so every K and V fragment read from LDS serves 64 rows;
 //   * keys stream through a 4-deep ring of LDS stages, 32 keys of K and V per stage,
 //     filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KB per load)
-//     issued two tiles ahead between the matrix instructions; one barrier per tile;
+//     issued three tiles ahead between the score product's matrix instructions; one
+//     barrier per tile;
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (32 keys x 32 rows per block): a lane holds 16 keys of one row, and the other
 //     16 keys of that row sit in the lane 32 apart, so the row max is one lane swap;
@@ -22,8 +23,8 @@
 //     16-key chunks; the chunk's key order follows the score registers, so the P^T
 //     fragment is the score registers as they stand, and two transposing LDS reads
 //     (ds_read_b64_tr_b16) deliver V^T in exactly that order;
-//   * the softmax of tile u runs between the matrix instructions of the PV product of
-//     tile u-1, so the one wavefront of a SIMD keeps the matrix core busy by itself;
+//   * the probabilities of a tile's second 16-key chunk are computed between the
+//     matrix instructions of its first chunk's PV product;
 //   * the reference max only moves when a tile raises it by more than 2^8, so the
 //     accumulators are rarely rescaled (the merged result does not depend on the
 //     reference values used).
@@ -58,7 +59,7 @@ constexpr int VU = 1024 + 64;
 constexpr int KTILE = UNITS * KU;
 constexpr int STAGE_BYTES = UNITS * (KU + VU);
 constexpr int NST = 4;                   // ring depth
-constexpr int LOOK = 2;                  // tiles loaded ahead
+constexpr int LOOK = 3;                  // tiles loaded ahead (a stage is free once its PV is done)
 constexpr int NI = 2 * UNITS / kW;       // loads per wavefront per tile
 constexpr int VMWAIT = NI * (LOOK - 1);  // loads left in flight at a wait
 constexpr int kGrpMax = 2048;            // 16-key groups of one chunk in the LDS table
@@ -148,6 +149,8 @@ __device__ __forceinline__ void tile_scores(const unsigned char *ks, const bf16x
             mfma_vgpr(sacc[0], ak, qf[0][k]);
             mfma_vgpr(sacc[1], ak, qf[1][k]);
         }
+        // the loads the hook issues stay in their k-step
+        __builtin_amdgcn_sched_barrier(0);
     }
     vgpr_read_guard(sacc[0], sacc[1]);
 }
@@ -170,87 +173,109 @@ __device__ __forceinline__ void mask_scores(f32x16 (&sacc)[2], uint32_t kvalid, 
     }
 }
 
-// Online softmax in log2 units, first half: the row max over the tile; the reference
-// max of a row moves (to the tile max) only when the tile exceeds it by more than
-// kRescaleSlack, and alpha is the factor the row's earlier sums and accumulators must
-// take (1 when it did not move).  mneg = -reference (0 while a row has seen no valid key).
-__device__ __forceinline__ void tile_max(const f32x16 (&sacc)[2], float (&mref)[2], float (&lsum)[2],
-                                         float (&alpha)[2], float (&mneg)[2], float scale_log2) {
+// Online softmax in log2 units, taken in pieces so that a tile's softmax can run
+// between the matrix instructions of the next tile's score product.
+//
+// Row max over the tile of one row block (both lanes of a row), in log2 units.
+__device__ __forceinline__ float row_max(const f32x16 &sr, float scale_log2) {
+    float m8[8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        float m8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m8[j] = __builtin_fmaxf(sacc[rb][2 * j], sacc[rb][2 * j + 1]);
-        float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
-                                   __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
-        mt = max_over_halves(mt) * scale_log2;
-        const bool raise = mt > mref[rb] + kRescaleSlack;
-        const float mnew = raise ? mt : mref[rb];
-        alpha[rb] = raise ? __builtin_amdgcn_exp2f(mref[rb] - mnew) : 1.0f;  // 0 when nothing seen yet
-        mref[rb] = mnew;
-        mneg[rb] = mnew == kNegInf ? 0.0f : -mnew;
-        lsum[rb] *= alpha[rb];
-    }
+    for (int j = 0; j < 8; ++j) m8[j] = __builtin_fmaxf(sr[2 * j], sr[2 * j + 1]);
+    const float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
+                                     __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
+    return max_over_halves(mt) * scale_log2;
 }
 
-// Second half, for key chunk c: probabilities exp2(s * scale_log2 - mref) (a masked
-// score, -inf, gives 0) as the bf16 P^T fragment pf[rb][c] (element j = score element
-// 8c + j), and exactly those bf16 values added to the row sums.
-__device__ __forceinline__ void tile_probs(const f32x16 (&sacc)[2], int c, const float (&mneg)[2],
-                                           float (&lsum)[2], bf16x8 (&pf)[2][2], float scale_log2) {
+// Reference update of a row: the reference max moves (to the tile max mt) only when the
+// tile exceeds it by more than kRescaleSlack; alpha is the factor the row's earlier sum
+// and accumulators must take (1 when it did not move, 0 when nothing was seen before);
+// mneg = -reference (0 while the row has seen no valid key).
+__device__ __forceinline__ void ref_update(float mt, float &mref, float &lsum, float &alpha, float &mneg) {
+    const bool raise = mt > mref + kRescaleSlack;
+    const float mnew = raise ? mt : mref;
+    alpha = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
+    mref = mnew;
+    mneg = mnew == kNegInf ? 0.0f : -mnew;
+    lsum *= alpha;
+}
+
+// Probabilities of score elements e, e + 1 of a row block: exp2(s * scale_log2 - mref)
+// (a masked score, -inf, gives 0), rounded to bf16 into the P^T fragment (element j of
+// fragment c is score element 8c + j), and exactly those bf16 values added to the row sum.
+__device__ __forceinline__ void probs_pair(const f32x16 &sr, int e, float mneg, float &lsum, bf16x8 (&pr)[2],
+                                           float scale_log2) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sr[e], scale_log2, mneg));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sr[e + 1], scale_log2, mneg));
+    const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum, false);
+    pr[e >> 3][e & 7] = pk[0];
+    pr[e >> 3][(e & 7) + 1] = pk[1];
+}
+
+// The softmax of one tile (scores sp) in 16 pieces, piece k before step k of a PV
+// product: row maxima (pieces 0, 1), reference updates (2), then the 16 probability pairs
+// (two row blocks x 8 pairs, row blocks alternating) over pieces 3-14.
+struct RowState {
+    float mref[2], lsum[2], alpha[2], mneg[2], mt[2];
+};
+
+__device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowState &rs, bf16x8 (&pf)[2][2],
+                                              float scale_log2) {
+    if (k < 2) rs.mt[k] = row_max(sp[k], scale_log2);
+    if (k == 2) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb) ref_update(rs.mt[rb], rs.mref[rb], rs.lsum[rb], rs.alpha[rb], rs.mneg[rb]);
+    }
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * c + j], scale_log2, mneg[rb]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[rb][8 * c + j + 1], scale_log2, mneg[rb]));
-            const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-            lsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum[rb], false);
-            pf[rb][c][j] = pk[0];
-            pf[rb][c][j + 1] = pk[1];
+    for (int q = 0; q < 16; ++q) {
+        if (k == 3 + (3 * q) / 4) {
+            const int rb = q & 1;
+            probs_pair(sp[rb], 2 * (q >> 1), rs.mneg[rb], rs.lsum[rb], pf[rb], scale_log2);
         }
     }
 }
 
-// O^T += V^T P^T over one 16-key chunk c of a tile (keys 16c .. 16c+15), whose V rows
-// start at vc = the tile's V + 512 c; pc[rb] is the chunk's P^T fragment.  A = V^T (32 d x 16
+// O^T += V^T P^T over one tile (V at vs), in two 16-key chunks c (keys 16c .. 16c+15, V
+// rows from vs + 512 c) with P^T fragments pf[rb][c].  A = V^T (32 d x 16
 // keys; lane l: d 32 db + l % 32, keys 16c + 4 (l / 32) + 0..3 and 16c + 8 + 4 (l / 32)
 // + 0..3, the P^T fragment's order).  The transposing read: in each 16-lane group G,
 // source lane 4r + q points at 4 consecutive d (32 db + 16 (G % 2) + 4q ..) of key
 // 16c + 4 (G / 2) + r; lane j of the group then receives d 32 db + 16 (G % 2) + j of
 // those 4 keys.
-__device__ __forceinline__ void pv_one(const unsigned char *vc, const bf16x8 (&pc)[2], f32x16 (&o)[2][DB]) {
+template <class Hook>
+__device__ __forceinline__ void pv_tile(const unsigned char *vs, const bf16x8 (&pf)[2][2], f32x16 (&o)[2][DB],
+                                        Hook &&hook) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4;
     const int r = (lane >> 2) & 3;
     const int q = lane & 3;
-    const unsigned char *vb = vc + ((G >> 1) * 4 + r) * VU + (G & 1) * 32 + q * 8;
-    // V^T fragments of the next VD d blocks are in flight while a block's products run
+    const unsigned char *vb = vs + ((G >> 1) * 4 + r) * VU + (G & 1) * 32 + q * 8;
+    // V^T fragments of the next VD (chunk, d block) steps are in flight while a step's
+    // products run
     constexpr int VD = SV_W4_VD;
+    constexpr int NSTEP = 2 * DB;
     bf16x8 v[VD + 1];
-    auto read = [&](int db) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vb + db * 64));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4 *)(vb + 8 * VU + db * 64));
-        v[db % (VD + 1)] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    auto read = [&](int i) {
+        const unsigned char *a = vb + (i / DB) * 512 + (i % DB) * 64;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)a);
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a + 8 * VU));
+        v[i % (VD + 1)] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 #pragma unroll
-    for (int db = 0; db < VD; ++db) read(db);
+    for (int i = 0; i < VD; ++i) read(i);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        if (db + VD < DB) read(db + VD);
-        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db % (VD + 1)], pc[0], o[0][db], 0, 0, 0);
-        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[db % (VD + 1)], pc[1], o[1][db], 0, 0, 0);
+    for (int i = 0; i < NSTEP; ++i) {
+        if (i + VD < NSTEP) read(i + VD);
+        hook(i);
+        const int c = i / DB, db = i % DB;
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[i % (VD + 1)], pf[0][c], o[0][db], 0, 0, 0);
+        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[i % (VD + 1)], pf[1][c], o[1][db], 0, 0, 0);
+        // the hook's work stays in its step, in the shadow of that step's products
+        __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-__device__ __forceinline__ void pv_chunk(const unsigned char *vs, int c, const bf16x8 (&pf)[2][2],
-                                         f32x16 (&o)[2][DB]) {
-    const bf16x8 pc[2] = {pf[0][c], pf[1][c]};
-    pv_one(vs + c * 512, pc, o);
 }
 
 // x *= s for an accumulator element held in an AGPR, without giving it a VGPR home (a
@@ -264,11 +289,13 @@ __device__ __forceinline__ float scale_agpr(float x, float s) {
     return x;
 }
 
-// Keeps the probabilities of chunk c computed before the (rarely taken) rescale branch
-// rather than sunk past it, so that chunk 1's softmax stays between the matrix
-// instructions of chunk 0's PV product.
-__device__ __forceinline__ void settle(const bf16x8 (&pf)[2][2], int c) {
-    asm volatile("" ::"v"(pf[0][c]), "v"(pf[1][c]));
+// Keeps a tile's softmax where it was written, between the matrix instructions of the
+// PV product, rather than sunk past the (rarely taken) rescale branch into the next
+// iteration.
+__device__ __forceinline__ void settle(const bf16x8 (&pf)[2][2], const RowState &rs) {
+    asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
+    asm volatile("" ::"v"(rs.lsum[0]), "v"(rs.lsum[1]), "v"(rs.mneg[0]), "v"(rs.mneg[1]), "v"(rs.mref[0]),
+                 "v"(rs.mref[1]));
 }
 
 // O *= alpha per row block, when any lane's reference max moved.  The accumulator
@@ -313,6 +340,7 @@ void attn_w4_kernel(MfmaParams p) {
     const int ntp = end > start ? (end - start + kKeyTile - 1) / kKeyTile : 0;
     const int ntt = s == 0 ? (p.T + kKeyTile - 1) / kKeyTile : 0;
     const int nt = ntp + ntt;
+    if (nt == 0) return;  // no rows (the host launches nothing for an empty tree)
 
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -395,20 +423,36 @@ void attn_w4_kernel(MfmaParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.0f;
-    float mref[2] = {kNegInf, kNegInf};
-    float lsum[2] = {0.0f, 0.0f};
-    float alpha[2], mneg[2];
-    bf16x8 pf[2][2];
-    f32x16 sacc[2];
+    RowState rs;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        rs.mref[rb] = kNegInf;
+        rs.lsum[rb] = 0.0f;
+    }
+    f32x16 sc[2];  // scores of the current tile
+    // P^T fragments of even (set 0) and odd (set 1) tiles; set 1 starts as those of
+    // "tile -1", zero, whose PV product adds nothing
+    bf16x8 pf[2][2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pf[1][rb][c][j] = (__bf16)0.0f;
 
     // ---- tile loads.  Wavefront w loads tensor w / 2 (K, V), units (w % 2) * 8 + j of a
-    // tile; lanes 0-31 carry key p of unit p, lanes 32-63 key p + 16.  Every tile slot
-    // k < nt + LOOK issues exactly NI loads per wavefront (slots past the last tile repeat
-    // the last tile's sources into a free stage), so "tile u has landed" is always the
+    // tile; lanes 0-31 carry key p of unit p, lanes 32-63 key p + 16.  Iteration u of the
+    // tile loop computes the scores of tile u and the PV product of tile u - 1, so K is
+    // needed one iteration before V: in iteration u the K wavefronts load tile u + 3 and
+    // the V wavefronts tile u + 2, both landing three iterations before their use.  Every
+    // iteration (and the three of the prologue) issues exactly NI loads per wavefront
+    // (past the last tile they repeat the last sources into a free stage; before tile 0
+    // the V wavefronts read tile 0), so "iteration u's operands have landed" is always the
     // same vmcnt, and the ring drains before exit.
     const uint32_t smem0 = lds_addr(smem);
     const int wq = uni(w & 1);
     const int tensor = uni(w >> 1);
+    const int ahead = tensor ? 2 : 3;
     const int half = h;
     const int ustride = tensor ? VU : KU;
     const uint32_t lds_w = (tensor ? KTILE : 0) + wq * NI * ustride;
@@ -419,8 +463,9 @@ void attn_w4_kernel(MfmaParams p) {
     const int64_t lane_off = (int64_t)(8 * wq) * step + (lane & 31) * 16;
     TileLoad tl;
     tl.ustride = ustride;
-    auto prepare = [&](int k) {  // any tile slot
+    auto prepare = [&](int k) {  // this wavefront's share of tile k (k >= -1)
         const uint32_t stage = smem0 + (k & (NST - 1)) * STAGE_BYTES;
+        k = k < 0 ? 0 : k;
         if (k < ntp) {
             const int k0 = start + k * kKeyTile;
             int64_t off0, off1;
@@ -441,80 +486,81 @@ void attn_w4_kernel(MfmaParams p) {
             tl.spread = true;
         }
     };
-    auto issue = [&](int k) {
-        prepare(k);
-        if (tl.spread)
-#pragma unroll
-            for (int j = 0; j < NI; ++j) load_unit(tl, j);
-    };
     // the NI loads of the prepared tile go between the k-steps of the score product
     auto load_in_scores = [&](int k) {
         constexpr int every = KS / NI;
         if (k % every == 0 && tl.spread) load_unit(tl, k / every);
     };
 
-    // ---- one tile.  The PV products run one half-tile behind the softmax: tile u's
-    // max and chunk-0 probabilities go between the matrix instructions of tile u-1's
-    // chunk-1 PV product, and tile u's chunk-1 probabilities between those of its own
-    // chunk-0 PV product.  Before the first tile the pending product adds zeros.
-    bf16x8 pprev[2];  // P^T fragments of the pending chunk-1 product
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pprev[rb][j] = (__bf16)0.0f;
-    const unsigned char *vprev = smem + KTILE;  // V of the pending product (tile 0 at first)
-    auto compute = [&](int u, bool masked, uint32_t kvalid, bool tree, int k0, auto &&hook) {
-        const unsigned char *stg = smem + (u & (NST - 1)) * STAGE_BYTES;
-        tile_scores(stg, qf, sacc, hook);
-        if (masked) mask_scores(sacc, kvalid, tree, k0, mrow);
-        pv_one(vprev, pprev, o);
-        tile_max(sacc, mref, lsum, alpha, mneg, p.scale_log2);
-        tile_probs(sacc, 0, mneg, lsum, pf, p.scale_log2);
-        settle(pf, 0);
-        rescale(o, alpha);
-        pv_chunk(stg + KTILE, 0, pf, o);
-        tile_probs(sacc, 1, mneg, lsum, pf, p.scale_log2);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) pprev[rb] = pf[rb][1];
-        vprev = stg + KTILE + 512;
+    // ---- iteration u: the score product of tile u (the hook issues loads between its
+    // k-steps), its mask, then the PV product of tile u - 1 with the softmax of tile u in
+    // pieces between its steps, and the rescale when a reference moved (after the PV
+    // product of tile u - 1, before that of tile u).  Tile u's probabilities go to set
+    // u % 2, a template constant, so the loops below run two iterations per trip.
+    auto iteration = [&](auto cur_c, int u, auto &&loads, bool masked, uint32_t kvalid, bool tree, int k0) {
+        constexpr int cur = decltype(cur_c)::value;
+        tile_scores(smem + (u & (NST - 1)) * STAGE_BYTES, qf, sc, loads);
+        if (masked) mask_scores(sc, kvalid, tree, k0, mrow);
+        pv_tile(smem + ((u - 1) & (NST - 1)) * STAGE_BYTES + KTILE, pf[cur ^ 1], o,
+                [&](int i) { softmax_piece(i, sc, rs, pf[cur], p.scale_log2); });
+        settle(pf[cur], rs);
+        rescale(o, rs.alpha);
     };
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1>;
 
-    for (int k = 0; k < LOOK; ++k) issue(k);  // ring prologue
+    for (int k = -3; k < 0; ++k) {  // ring prologue
+        prepare(k + ahead);
+        if (tl.spread)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) load_unit(tl, j);
+    }
     int u = 0;
     if (staged && all_ok) {
-        // full prefix tiles whose loads LOOK tiles ahead are full prefix tiles too: group
-        // offsets read one tile early, no masking, no branches around the loads
-        const int nfast = (end - start) / kKeyTile - LOOK;
-        uint32_t gnext = nfast > 0 ? gtab[2 * LOOK + half] : 0;
-        for (; u < nfast; ++u) {
+        // full prefix tiles whose loads (up to 3 tiles ahead) are full prefix tiles too:
+        // group offsets read one iteration early, no masking, no branches around the
+        // loads; an even count, two iterations per trip
+        const int nfull = (end - start) / kKeyTile;
+        const int nfast = nfull > 3 ? (nfull - 3) & ~1 : 0;
+        uint32_t gnext = nfast > 0 ? gtab[2 * ahead + half] : 0;
+        auto fast = [&](auto cur_c, int uu) {
             wait_loads<VMWAIT>();
-            lds_barrier();  // tile u visible to all; stage of tile u - 2 free for reuse
+            lds_barrier();  // operands of iteration uu visible to all; load targets free
             const uint32_t g = gnext;
-            gnext = gtab[min(2 * (u + LOOK + 1) + half, kGrpMax - 1)];
+            gnext = gtab[min(2 * (uu + 1 + ahead) + half, kGrpMax - 1)];
             TileLoad f;
             f.src = pool_w + (int64_t)g * 16 + lane_off;
             f.step = step;
-            f.lds = smem0 + ((u + LOOK) & (NST - 1)) * STAGE_BYTES + lds_w;
+            f.lds = smem0 + ((uu + ahead) & (NST - 1)) * STAGE_BYTES + lds_w;
             f.ustride = ustride;
-            compute(u, false, 0u, false, 0, [&](int k) {
-                constexpr int every = KS / NI;
-                if (k % every == 0) load_unit(f, k / every);
-            });
+            iteration(
+                cur_c, uu,
+                [&](int k) {
+                    constexpr int every = KS / NI;
+                    if (k % every == 0) load_unit(f, k / every);
+                },
+                false, 0u, false, 0);
+        };
+        for (; u < nfast; u += 2) {
+            fast(Set0{}, u);
+            fast(Set1{}, u + 1);
         }
         tl = TileLoad{pool_w + lane_off, step, 0u, ustride, true};  // repeat-slot source
     }
-    for (; u < nt; ++u) {
+    auto generic = [&](auto cur_c, int uu) {
         wait_loads<VMWAIT>();
         lds_barrier();
-        prepare(u + LOOK);
-        const bool tr = u >= ntp;
-        int k0;
-        uint32_t kvalid;
-        if (tr) {
-            k0 = (u - ntp) * kKeyTile;
+        prepare(uu + ahead);
+        const bool tr = uu >= ntp && uu < nt;
+        int k0 = 0;
+        uint32_t kvalid = 0;
+        if (uu >= nt) {
+            // past the last tile: all keys masked
+        } else if (tr) {
+            k0 = (uu - ntp) * kKeyTile;
             kvalid = tree_valid(k0, p.T);
         } else {
-            k0 = start + u * kKeyTile;
+            k0 = start + uu * kKeyTile;
             kvalid = 0;
 #pragma unroll
             for (int grp = 0; grp < 2; ++grp) {
@@ -522,21 +568,28 @@ void attn_w4_kernel(MfmaParams p) {
                 if (pos < end) {
                     int64_t off;
                     const int nk = end - pos < 16 ? end - pos : 16;
-                    if (group_off(2 * u + grp, off))
+                    if (group_off(2 * uu + grp, off))
                         kvalid |= (nk == 16 ? 0xffffu : ((1u << nk) - 1u)) << (16 * grp);
                 }
             }
         }
-        compute(u, tr || kvalid != 0xffffffffu, kvalid, tr, k0, load_in_scores);
+        iteration(cur_c, uu, load_in_scores, tr || kvalid != 0xffffffffu, kvalid, tr, k0);
+    };
+    // iterations up to nt (the PV product of the last tile), two per trip from an even u;
+    // iterations past the last tile compute the scores of repeat-slot data with every key
+    // masked, so that their probabilities are zero and their PV products add nothing
+    const int nit = (nt + 2) & ~1;
+    for (; u < nit; u += 2) {
+        generic(Set0{}, u);
+        generic(Set1{}, u + 1);
     }
-    pv_one(vprev, pprev, o);  // the last tile's chunk-1 product
     wait_loads<0>();  // the trailing repeat loads
 
     // ---- partial results: O (unnormalised), reference max (log2 units) and sum per row;
     //      accumulator element r of block (rb, db) is d = 32 db + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float ltot = lsum[rb] + __shfl_xor(lsum[rb], 32, 64);
+        const float ltot = rs.lsum[rb] + __shfl_xor(rs.lsum[rb], 32, 64);
         const int row = row_base + rb * 32;
         if (row < p.R) {
             const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
@@ -549,7 +602,7 @@ void attn_w4_kernel(MfmaParams p) {
                         f32x4{o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2],
                               o[rb][db][4 * g4 + 3]};
             if (h == 0) {
-                p.ws_ml[base * 2 + 0] = mref[rb];
+                p.ws_ml[base * 2 + 0] = rs.mref[rb];
                 p.ws_ml[base * 2 + 1] = ltot;
             }
         }
