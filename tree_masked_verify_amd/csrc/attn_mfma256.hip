@@ -173,66 +173,82 @@ __device__ __forceinline__ void mask_scores(f32x16 (&sacc)[2], uint32_t kvalid, 
     }
 }
 
-// Online softmax in log2 units, taken in pieces so that a tile's softmax can run
-// between the matrix instructions of the next tile's score product.
-//
-// Row max over the tile of one row block (both lanes of a row), in log2 units.
-__device__ __forceinline__ float row_max(const f32x16 &sr, float scale_log2) {
-    float m8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m8[j] = __builtin_fmaxf(sr[2 * j], sr[2 * j + 1]);
-    const float mt = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), __builtin_fmaxf(m8[2], m8[3])),
-                                     __builtin_fmaxf(__builtin_fmaxf(m8[4], m8[5]), __builtin_fmaxf(m8[6], m8[7])));
-    return max_over_halves(mt) * scale_log2;
-}
+// Online softmax in log2 units, taken in 16 pieces that run between the steps of a PV
+// product.  A single wavefront issues in order, so an operation that waits for the
+// result of the one before it also holds up the next matrix instruction; the pieces are
+// therefore arranged so that each one only uses results of earlier pieces (one step,
+// two matrix instructions, apart):
+//   0-2  row maxima of both row blocks: three levels of max3/max, then the lane swap
+//        (the other 16 keys of a row sit in the lane 32 apart) and the log2 scaling;
+//   3    reference updates: the reference max of a row moves (to the tile max) only
+//        when the tile exceeds it by more than kRescaleSlack; alpha = exp2(old - new) is
+//        the factor the row's earlier sum and accumulators must take, exactly 1 when the
+//        reference did not move.  A row that has seen no valid key holds the finite
+//        reference kNoRef (its sum and accumulators are 0), so that alpha needs no
+//        special case;
+//   4-15 probabilities exp2(s * scale_log2 - mref) of 16 element pairs (one pair of each
+//        row block per piece), in five stages one piece apart: the fma, the exp2, the
+//        rounding to bf16 into the P^T fragment (element j of fragment c is score element
+//        8c + j), the sum of exactly those two bf16 values (widened by bit shifts), and
+//        its addition to the row sum.  A masked score (-inf) gives 0.
+constexpr float kNoRef = -1.0e30f;
 
-// Reference update of a row: the reference max moves (to the tile max mt) only when the
-// tile exceeds it by more than kRescaleSlack; alpha is the factor the row's earlier sum
-// and accumulators must take (1 when it did not move, 0 when nothing was seen before);
-// mneg = -reference (0 while the row has seen no valid key).
-__device__ __forceinline__ void ref_update(float mt, float &mref, float &lsum, float &alpha, float &mneg) {
-    const bool raise = mt > mref + kRescaleSlack;
-    const float mnew = raise ? mt : mref;
-    alpha = raise ? __builtin_amdgcn_exp2f(mref - mnew) : 1.0f;
-    mref = mnew;
-    mneg = mnew == kNegInf ? 0.0f : -mnew;
-    lsum *= alpha;
-}
-
-// Probabilities of score elements e, e + 1 of a row block: exp2(s * scale_log2 - mref)
-// (a masked score, -inf, gives 0), rounded to bf16 into the P^T fragment (element j of
-// fragment c is score element 8c + j), and exactly those bf16 values added to the row sum.
-__device__ __forceinline__ void probs_pair(const f32x16 &sr, int e, float mneg, float &lsum, bf16x8 (&pr)[2],
-                                           float scale_log2) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sr[e], scale_log2, mneg));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sr[e + 1], scale_log2, mneg));
-    const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-    lsum = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, lsum, false);
-    pr[e >> 3][e & 7] = pk[0];
-    pr[e >> 3][(e & 7) + 1] = pk[1];
-}
-
-// The softmax of one tile (scores sp) in 16 pieces, piece k before step k of a PV
-// product: row maxima (pieces 0, 1), reference updates (2), then the 16 probability pairs
-// (two row blocks x 8 pairs, row blocks alternating) over pieces 3-14.
 struct RowState {
-    float mref[2], lsum[2], alpha[2], mneg[2], mt[2];
+    float mref[2], lsum[2], alpha[2];
+    bool raised[2];
 };
 
-__device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowState &rs, bf16x8 (&pf)[2][2],
-                                              float scale_log2) {
-    if (k < 2) rs.mt[k] = row_max(sp[k], scale_log2);
-    if (k == 2) {
+struct SoftTmp {
+    float m6[2][6], m2[2][2], mt[2];
+    float x[16][2], y[16][2], t[16];
+};
+
+__device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowState &rs, SoftTmp &t,
+                                              bf16x8 (&pf)[2][2], float scale_log2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) ref_update(rs.mt[rb], rs.mref[rb], rs.lsum[rb], rs.alpha[rb], rs.mneg[rb]);
-    }
+    for (int rb = 0; rb < 2; ++rb) {
+        const f32x16 &sr = sp[rb];
+        if (k == 0) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        if (k == 3 + (3 * q) / 4) {
-            const int rb = q & 1;
-            probs_pair(sp[rb], 2 * (q >> 1), rs.mneg[rb], rs.lsum[rb], pf[rb], scale_log2);
+            for (int j = 0; j < 5; ++j)
+                t.m6[rb][j] = __builtin_fmaxf(__builtin_fmaxf(sr[3 * j], sr[3 * j + 1]), sr[3 * j + 2]);
+            t.m6[rb][5] = sr[15];
+        }
+        if (k == 1) {
+            t.m2[rb][0] = __builtin_fmaxf(__builtin_fmaxf(t.m6[rb][0], t.m6[rb][1]), t.m6[rb][2]);
+            t.m2[rb][1] = __builtin_fmaxf(__builtin_fmaxf(t.m6[rb][3], t.m6[rb][4]), t.m6[rb][5]);
+        }
+        if (k == 2) t.mt[rb] = max_over_halves(__builtin_fmaxf(t.m2[rb][0], t.m2[rb][1])) * scale_log2;
+        if (k == 3) {
+            rs.raised[rb] = t.mt[rb] > rs.mref[rb] + kRescaleSlack;
+            const float mnew = rs.raised[rb] ? t.mt[rb] : rs.mref[rb];
+            rs.alpha[rb] = __builtin_amdgcn_exp2f(rs.mref[rb] - mnew);
+            rs.mref[rb] = mnew;
+            rs.lsum[rb] *= rs.alpha[rb];
+        }
+        // pair q = 2 i + rb (i = 0..7): elements 2i, 2i + 1 of row block rb
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = 2 * i + rb;
+            if (k == 4 + i) {
+                t.x[q][0] = fmaf(sr[2 * i], scale_log2, -rs.mref[rb]);
+                t.x[q][1] = fmaf(sr[2 * i + 1], scale_log2, -rs.mref[rb]);
+            }
+            if (k == 5 + i) {
+                t.y[q][0] = __builtin_amdgcn_exp2f(t.x[q][0]);
+                t.y[q][1] = __builtin_amdgcn_exp2f(t.x[q][1]);
+            }
+            if (k == 6 + i) {
+                pf[rb][i >> 2][2 * (i & 3)] = (__bf16)t.y[q][0];
+                pf[rb][i >> 2][2 * (i & 3) + 1] = (__bf16)t.y[q][1];
+            }
+            if (k == 7 + i) {
+                const bf16x2 pk = {pf[rb][i >> 2][2 * (i & 3)], pf[rb][i >> 2][2 * (i & 3) + 1]};
+                const uint32_t wv = __builtin_bit_cast(uint32_t, pk);
+                t.t[q] = __uint_as_float(wv << 16) + __uint_as_float(wv & 0xffff0000u);
+            }
+            if (k == 8 + i) rs.lsum[rb] += t.t[q];
         }
     }
 }
@@ -294,15 +310,14 @@ __device__ __forceinline__ float scale_agpr(float x, float s) {
 // iteration.
 __device__ __forceinline__ void settle(const bf16x8 (&pf)[2][2], const RowState &rs) {
     asm volatile("" ::"v"(pf[0][0]), "v"(pf[0][1]), "v"(pf[1][0]), "v"(pf[1][1]));
-    asm volatile("" ::"v"(rs.lsum[0]), "v"(rs.lsum[1]), "v"(rs.mneg[0]), "v"(rs.mneg[1]), "v"(rs.mref[0]),
-                 "v"(rs.mref[1]));
+    asm volatile("" ::"v"(rs.lsum[0]), "v"(rs.lsum[1]), "v"(rs.mref[0]), "v"(rs.mref[1]));
 }
 
 // O *= alpha per row block, when any lane's reference max moved.  The accumulator
 // reads are in assembly the compiler does not look into, so the 18 wait states after
 // the last matrix instruction are given here, fenced against rescheduling.
-__device__ __forceinline__ void rescale(f32x16 (&o)[2][DB], const float (&alpha)[2]) {
-    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+__device__ __forceinline__ void rescale(f32x16 (&o)[2][DB], const RowState &rs) {
+    if (__any(rs.raised[0] || rs.raised[1])) {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -311,7 +326,7 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[2][DB], const float (&alpha)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[rb][db][r] = scale_agpr(o[rb][db][r], alpha[rb]);
+                for (int r = 0; r < 16; ++r) o[rb][db][r] = scale_agpr(o[rb][db][r], rs.alpha[rb]);
         // and 2 wait states before a matrix instruction reads what a VALU op wrote
         asm volatile("s_nop 1" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
@@ -426,7 +441,7 @@ void attn_w4_kernel(MfmaParams p) {
     RowState rs;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        rs.mref[rb] = kNegInf;
+        rs.mref[rb] = kNoRef;
         rs.lsum[rb] = 0.0f;
     }
     f32x16 sc[2];  // scores of the current tile
@@ -501,10 +516,11 @@ void attn_w4_kernel(MfmaParams p) {
         constexpr int cur = decltype(cur_c)::value;
         tile_scores(smem + (u & (NST - 1)) * STAGE_BYTES, qf, sc, loads);
         if (masked) mask_scores(sc, kvalid, tree, k0, mrow);
+        SoftTmp tmp;
         pv_tile(smem + ((u - 1) & (NST - 1)) * STAGE_BYTES + KTILE, pf[cur ^ 1], o,
-                [&](int i) { softmax_piece(i, sc, rs, pf[cur], p.scale_log2); });
+                [&](int i) { softmax_piece(i, sc, rs, tmp, pf[cur], p.scale_log2); });
         settle(pf[cur], rs);
-        rescale(o, rs.alpha);
+        rescale(o, rs);
     };
     using Set0 = std::integral_constant<int, 0>;
     using Set1 = std::integral_constant<int, 1>;
@@ -602,7 +618,7 @@ void attn_w4_kernel(MfmaParams p) {
                         f32x4{o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2],
                               o[rb][db][4 * g4 + 3]};
             if (h == 0) {
-                p.ws_ml[base * 2 + 0] = rs.mref[rb];
+                p.ws_ml[base * 2 + 0] = rs.mref[rb] == kNoRef ? kNegInf : rs.mref[rb];
                 p.ws_ml[base * 2 + 1] = ltot;
             }
         }
