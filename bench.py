@@ -128,6 +128,64 @@ def counter_traffic(workload):
     return int(fields["hbm_bytes_per_call"])
 
 
+def _smi_sample():
+    """(socket power W, graphics clock MHz) from one `amd-smi metric -p -c` reading, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=10)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    d = d[0] if isinstance(d, list) else d
+    if isinstance(d, dict) and "gpu_data" in d:
+        d = d["gpu_data"][0]
+
+    def val(x):
+        x = x.get("value") if isinstance(x, dict) else x
+        try:
+            return float(x)
+        except (TypeError, ValueError):
+            return None
+    clk = d.get("clock", {})
+    gfx = clk.get("gfx_0", clk.get("gfx", {}))
+    return val(d.get("power", {}).get("socket_power")), val(gfx.get("clk") if isinstance(gfx, dict) else gfx)
+
+
+def power_probe(st, seconds):
+    """The attention call back to back for `seconds` while amd-smi samples the board's socket
+    power and graphics clock (the first second of samples is dropped as ramp-up)."""
+    import statistics
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.time()
+        while not stop.is_set():
+            v = _smi_sample()
+            if v is not None and time.time() - t0 > 1.0:
+                samples.append(v)
+            time.sleep(0.25)
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0, n = time.time(), 0
+    while time.time() - t0 < seconds:
+        for _ in range(50):
+            st.attention()
+        torch.cuda.synchronize()
+        n += 50
+    dt = time.time() - t0
+    stop.set()
+    th.join()
+    pw = [p for p, _ in samples if p is not None]
+    ck = [c for _, c in samples if c is not None]
+    return {"attention_us": round(dt / n * 1e6, 1), "calls": n, "samples": len(samples),
+            "socket_power_w_median": statistics.median(pw) if pw else None,
+            "socket_power_w_max": max(pw) if pw else None,
+            "gfx_clock_mhz_median": statistics.median(ck) if ck else None}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +195,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="only loop the attention call this long while sampling board power "
+                         "and graphics clock with amd-smi; prints one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of this many MiB --steps "
                          "times (reference for the HBM byte counters)")
@@ -167,6 +228,14 @@ def main():
     st = VerifyStep.from_inputs(inp, num_splits=args.splits)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
+    if args.power > 0:
+        st.build_mask()
+        for _ in range(3):
+            st.attention()
+        torch.cuda.synchronize()
+        log(f"[bench] power probe, {args.power} s of attention calls")
+        print(json.dumps({"workload": w.name, **power_probe(st, args.power)}), flush=True)
+        return
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         st.run()

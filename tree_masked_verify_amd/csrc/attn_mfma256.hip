@@ -438,10 +438,13 @@ void attn_w4_kernel(MfmaParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[rb][db][r] = 0.0f;
+    // Rows past the last query row get the reference +inf: their probabilities are 0 (the
+    // PV products then multiply zeros, which costs the matrix cores less energy), and
+    // their sums and accumulators, never stored, may hold NaN.
     RowState rs;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        rs.mref[rb] = kNoRef;
+        rs.mref[rb] = row_base + rb * 32 < p.R ? kNoRef : __builtin_huge_valf();
         rs.lsum[rb] = 0.0f;
     }
     f32x16 sc[2];  // scores of the current tile
