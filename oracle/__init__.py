@@ -50,11 +50,14 @@ def _declare(lib):
     lib.oracle_argmax.argtypes = [_f32p, _i64, _i64, _i32p, _int]
     lib.oracle_accept_longest_path.argtypes = [
         _f32p, _i32p, _i32p, _i32p, _int, _int, _i64, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_accept_sampled.argtypes = [
+        _f32p, _i32p, _i32p, _i32p, _f32p, _f32p, ctypes.c_double, _int, _int, _i64, _i32p,
+        _i32p, _i32p]
     lib.oracle_kv_commit.argtypes = [
         _vp, _vp, _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64,
         _int, _i32p, _int, _i32p, _int, _int, _int, _int]
     for f in ("oracle_build_tree_mask", "oracle_tree_verify_attention", "oracle_argmax",
-              "oracle_accept_longest_path", "oracle_kv_commit"):
+              "oracle_accept_longest_path", "oracle_accept_sampled", "oracle_kv_commit"):
         getattr(lib, f).restype = _int
     return lib
 
@@ -170,6 +173,28 @@ class Oracle:
             V, _p(am, _i32p), _p(L, _i32p), _p(nodes, _i32p), _p(toks, _i32p))
         assert rc == 0
         return am, L, nodes, toks
+
+    def accept_sampled(self, logits, draft, parents, u_accept, u_sample, temperature,
+                       tree_err=None):
+        """Sampled acceptance; returns (accepted_len, accepted_nodes, out_tokens)."""
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        draft = np.ascontiguousarray(draft, dtype=np.int32)
+        parents = np.ascontiguousarray(parents, dtype=np.int32)
+        u_accept = np.ascontiguousarray(u_accept, dtype=np.float32)
+        u_sample = np.ascontiguousarray(u_sample, dtype=np.float32)
+        B, T = parents.shape
+        V = logits.shape[-1]
+        if tree_err is not None:
+            tree_err = np.ascontiguousarray(tree_err, dtype=np.int32)
+        L = np.zeros((B,), np.int32)
+        nodes = np.zeros((B, T), np.int32)
+        toks = np.zeros((B, T), np.int32)
+        rc = self.lib.oracle_accept_sampled(
+            _p(logits, _f32p), _p(draft, _i32p), _p(parents, _i32p), _p(tree_err, _i32p),
+            _p(u_accept, _f32p), _p(u_sample, _f32p), float(temperature), B, T, V, _p(L, _i32p),
+            _p(nodes, _i32p), _p(toks, _i32p))
+        assert rc == 0
+        return L, nodes, toks
 
     def kv_commit(self, k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: Cache,
                   prefix_len, max_prefix_len, new_prefix_len=True):

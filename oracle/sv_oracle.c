@@ -27,10 +27,13 @@
  *  [ANE]  "Speculative decoding verify batches to amortize ANE dispatch"
  *         (llms-explorer): Facts on the commit rule (argmax decides, longest
  *         matching prefix plus one bonus token, accept(k) commits only the
- *         accepted prefix) and on delayed KV write-through.
+ *         accepted prefix), on delayed KV write-through, and on Forge's sampled
+ *         verification (a proposal is accepted with its target probability; on
+ *         rejection the target distribution is sampled with it excluded).
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC sv_oracle.c -lm
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -310,6 +313,118 @@ int oracle_accept_longest_path(const float *logits, const int32_t *draft, const 
         accepted_len[b] = L;
     }
     free(a); free(dep); free(match); free(path);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sampled acceptance ([ANE] Facts: Forge treats the drafted path as given,    */
+/* accepts a proposal with its target probability, and on rejection samples   */
+/* the target distribution with that proposal excluded).                       */
+/* Target distribution of node v: p_v(x) = exp(l_v(x) / tau) / sum_y          */
+/* exp(l_v(y) / tau) over logits row v (NaN and -inf entries have p = 0, +inf */
+/* counts as the largest finite float; a row with no finite entry has p = 0   */
+/* everywhere).                                                                */
+/* Reading for a tree (the pages state the rule for one proposal): starting  */
+/* at the root, the children of the current node v are tried in increasing    */
+/* node index, each as one proposal from what is left of p_v.  With E the      */
+/* tokens already rejected at v and R = 1 - sum_{x in E} p_v(x), child c with  */
+/* token x is accepted when u_accept[c] * R < p_v(x) (x in E or outside the    */
+/* vocabulary: p = 0); an accepted child becomes the current node.  When no    */
+/* child is accepted (or v is a leaf), the emitted token is drawn from p_v     */
+/* restricted to tokens outside E by inverse CDF: the smallest token y outside */
+/* E with sum_{z <= y, z not in E} p_v(z) > u_sample[v] * R (token 0 if no     */
+/* token outside E has probability).  Path and tokens: root..final node,       */
+/* L = path length, out_tokens = the accepted children's draft tokens, then    */
+/* the drawn token.  An invalid tree accepts nothing (L = 0, -1 entries).       */
+static double logit_at(const float *row, int64_t y) {
+    const float x = row[y];
+    if (isnan(x)) return -INFINITY;
+    if (isinf(x) && x > 0) return (double)FLT_MAX;
+    return (double)x;
+}
+
+int oracle_accept_sampled(const float *logits, const int32_t *draft, const int32_t *parents,
+                          const int32_t *tree_err, const float *u_accept, const float *u_sample,
+                          double tau, int B, int T, int64_t V, int32_t *accepted_len,
+                          int32_t *accepted_nodes, int32_t *out_tokens) {
+    if (B < 0 || T < 1 || V < 1 || !(tau > 0)) return -1;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    unsigned char *excl = (unsigned char *)malloc((size_t)V);
+    int32_t *path = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    if (!p || !excl || !path) {
+        free(p); free(excl); free(path);
+        return -2;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (int64_t)b * T;
+        const int32_t *drf = draft + (int64_t)b * T;
+        int32_t *nodes = accepted_nodes + (int64_t)b * T;
+        int32_t *toks = out_tokens + (int64_t)b * T;
+        for (int j = 0; j < T; ++j) nodes[j] = toks[j] = -1;
+        if ((tree_err && tree_err[b] != 0) || tree_status(par, T) != OR_TREE_OK) {
+            accepted_len[b] = 0;
+            continue;
+        }
+        int v = 0, L = 0;
+        path[L++] = 0;
+        for (;;) {
+            /* p_v */
+            const float *row = logits + ((int64_t)b * T + v) * V;
+            double m = -INFINITY;
+            for (int64_t y = 0; y < V; ++y) {
+                const double l = logit_at(row, y);
+                if (l > m) m = l;
+            }
+            double Z = 0.0;
+            for (int64_t y = 0; y < V; ++y) {
+                const double l = logit_at(row, y);
+                p[y] = l == -INFINITY ? 0.0 : exp((l - m) / tau);
+                Z += p[y];
+            }
+            for (int64_t y = 0; y < V; ++y) p[y] = Z > 0.0 ? p[y] / Z : 0.0;
+            memset(excl, 0, (size_t)V);
+            /* children of v in increasing index */
+            double R = 1.0;
+            int next = -1;
+            for (int c = v + 1; c < T && next < 0; ++c) {
+                if (par[c] != v) continue;
+                const int32_t x = drf[c];
+                const int in_vocab = x >= 0 && (int64_t)x < V;
+                const double px = (in_vocab && !excl[x]) ? p[x] : 0.0;
+                if ((double)u_accept[(int64_t)b * T + c] * R < px) {
+                    next = c;
+                } else if (in_vocab && !excl[x]) {
+                    excl[x] = 1;
+                    R -= px;
+                }
+            }
+            if (next >= 0) {
+                toks[L - 1] = drf[next];
+                path[L++] = next;
+                v = next;
+                continue;
+            }
+            /* draw from p_v without E */
+            const double target = (double)u_sample[(int64_t)b * T + v] * R;
+            double acc = 0.0;
+            int32_t tok = -1;
+            for (int64_t y = 0; y < V && tok < 0; ++y) {
+                if (excl[y] || p[y] <= 0.0) continue;
+                acc += p[y];
+                if (acc > target) tok = (int32_t)y;
+            }
+            if (tok < 0) { /* rounding or no probability left: last eligible token, else 0 */
+                tok = 0;
+                for (int64_t y = V - 1; y >= 0; --y)
+                    if (!excl[y] && p[y] > 0.0) { tok = (int32_t)y; break; }
+            }
+            toks[L - 1] = tok;
+            break;
+        }
+        for (int j = 0; j < L; ++j) nodes[j] = path[j];
+        accepted_len[b] = L;
+    }
+    free(p); free(excl); free(path);
     return 0;
 }
 

@@ -455,6 +455,183 @@ def pin_accept_expected_tokens_closed_form(orc):
         assert abs(L.mean() - want) <= 5 * sigma + 1e-9, (K, p, L.mean(), want)
 
 
+# =========================================================================== sampled accept pins
+def _p64(row, tau):
+    """Target distribution of one logits row in fp64 (numpy; -inf entries give 0)."""
+    l = np.asarray(row, np.float64) / tau
+    e = np.exp(l - l.max())
+    return e / e.sum()
+
+
+def pin_sampled_worked_examples(orc):
+    """Hand-derived cases of the rule: proposals tried in node order, a rejected
+    token is excluded and the rest renormalised, strict comparison u * R < p."""
+    lg = np.log(np.array([[0.5, 0.3, 0.2], [1, 1, 1], [1, 1, 1], [0.1, 0.1, 0.8]],
+                         np.float32))[None]
+    par = np.array([[-1, 0, 0, 0]], np.int32)
+    drf = np.array([[0, 0, 0, 1]], np.int32)
+    us = np.array([[0.0, 0.0, 0.0, 0.15]], np.float32)
+    # node 1 (token 0): 0.6 >= 0.5, rejected, R = 0.5; node 2 repeats token 0: p = 0;
+    # node 3 (token 1): 0.59 * 0.5 < 0.3, accepted; leaf: cumulative 0.1, 0.2 > 0.15
+    L, nodes, toks = orc.accept_sampled(lg, drf, par, np.array([[0, 0.6, 0.0, 0.59]], np.float32),
+                                        us, 1.0)
+    assert L[0] == 2 and list(nodes[0]) == [0, 3, -1, -1] and list(toks[0]) == [1, 1, -1, -1]
+    # 0.61 * 0.5 >= 0.3: every proposal rejected, E = {0, 1}, R = 0.2; only token 2 is left
+    us2 = np.array([[0.99, 0.0, 0.0, 0.15]], np.float32)
+    L, nodes, toks = orc.accept_sampled(lg, drf, par, np.array([[0, 0.6, 0.0, 0.61]], np.float32),
+                                        us2, 1.0)
+    assert L[0] == 1 and nodes[0, 0] == 0 and toks[0, 0] == 2 and np.all(toks[0, 1:] == -1)
+    # equal logits give p = 0.5 exactly: u = 0.5 rejects (strict), the next float below accepts
+    lg2 = np.zeros((1, 2, 2), np.float32)
+    par2 = np.array([[-1, 0]], np.int32)
+    drf2 = np.array([[0, 0]], np.int32)
+    half = np.float32(0.5)
+    L, _, toks = orc.accept_sampled(lg2, drf2, par2, np.array([[0, half]], np.float32),
+                                    np.array([[0.3, 0.3]], np.float32), 1.0)
+    assert L[0] == 1 and toks[0, 0] == 1            # token 0 excluded: token 1 is drawn
+    below = np.nextafter(half, np.float32(0))
+    L, _, toks = orc.accept_sampled(lg2, drf2, par2, np.array([[0, below]], np.float32),
+                                    np.array([[0.3, 0.3]], np.float32), 1.0)
+    assert L[0] == 2 and list(toks[0]) == [0, 0]     # row 1: cumulative 0.5 > 0.3 at token 0
+    # temperature: logits (0, ln 3) give p = (1/4, 3/4) at tau 1 and (1/10, 9/10) at tau 1/2
+    lg3 = np.zeros((1, 2, 2), np.float32)
+    lg3[0, :, 1] = np.float32(math.log(3.0))
+    ua = np.array([[0, 0.2]], np.float32)
+    assert orc.accept_sampled(lg3, drf2, par2, ua, np.array([[0.5, 0.5]], np.float32), 1.0)[0][0] == 2
+    assert orc.accept_sampled(lg3, drf2, par2, ua, np.array([[0.5, 0.5]], np.float32), 0.5)[0][0] == 1
+    # a row with no finite logit: every proposal has p = 0 and token 0 is emitted
+    lg4 = np.full((1, 2, 3), -np.inf, np.float32)
+    L, _, toks = orc.accept_sampled(lg4, np.array([[0, 2]], np.int32), par2,
+                                    np.array([[0, 0.0]], np.float32),
+                                    np.array([[0.7, 0.7]], np.float32), 1.0)
+    assert L[0] == 1 and toks[0, 0] == 0
+    # NaN entries have probability 0: row (NaN, 0, 0) is (0, 1/2, 1/2)
+    lg5 = np.zeros((1, 2, 3), np.float32)
+    lg5[0, 0, 0] = np.nan
+    L, _, toks = orc.accept_sampled(lg5, np.array([[0, 0]], np.int32), par2,
+                                    np.array([[0, 0.0]], np.float32),
+                                    np.array([[0.6, 0.6]], np.float32), 1.0)
+    assert L[0] == 1 and toks[0, 0] == 2
+    # an invalid tree accepts nothing
+    L, nodes, toks = orc.accept_sampled(lg, drf, par, np.zeros((1, 4), np.float32), us, 1.0,
+                                        np.array([1], np.int32))
+    assert L[0] == 0 and np.all(nodes == -1) and np.all(toks == -1)
+
+
+def pin_sampled_expected_tokens_golden(orc):
+    """A K-draft chain whose every row gives its child's draft token probability p:
+    each position is accepted with probability p, so the mean burst length is the
+    pages' 1 + p + p^2 + p^3 (K = 3: 1.42 at 30%, 1.88 at 50%)."""
+    with open(os.path.join(GOLDEN, "expected_tokens_per_burst.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    for K, p, printed in rows:
+        K, p, printed = int(K), float(p), float(printed)
+        n, T, V = 200_000, K + 1, 4
+        rng = np.random.Generator(np.random.PCG64(int(p * 1000) + 17))
+        tok = rng.integers(0, V, size=(n, T)).astype(np.int32)   # draft token of each node
+        lg = np.full((n, T, V), np.float32(math.log((1 - p) / (V - 1))), np.float32)
+        nxt = np.concatenate([tok[:, 1:], tok[:, :1]], axis=1)      # row i favours node i+1's token
+        lg[np.arange(n)[:, None], np.arange(T)[None], nxt] = np.float32(math.log(p))
+        par = np.tile(np.array(wl.chain_tree(T), np.int32), (n, 1))
+        ua, us = wl.make_uniforms(n, T, seed=K)
+        L, _, _ = orc.accept_sampled(lg, tok, par, ua, us, 1.0)
+        L = L.astype(np.float64)
+        sigma = L.std() / math.sqrt(n)
+        assert abs(L.mean() - printed) <= 0.005 + 5 * sigma, (K, p, L.mean(), printed)
+
+
+def pin_sampled_preserves_target(orc):
+    """Monte Carlo: the first emitted token follows the root's target distribution,
+    and after an accepted child the next one follows that child's (the property the
+    rule exists for).  Node 2 repeats node 1's token, so it is never accepted."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    par1 = np.array([-1, 0, 0, 0, 1, 1, 3], np.int32)
+    drf1 = np.array([0, 2, 2, 4, 0, 3, 1], np.int32)
+    T, V, tau, n = len(par1), 5, 0.7, 60_000
+    rows = rng.normal(0.0, 1.0, size=(T, V)).astype(np.float32)
+    lg = np.tile(rows[None], (n, 1, 1))
+    par = np.tile(par1[None], (n, 1))
+    drf = np.tile(drf1[None], (n, 1))
+    ua, us = wl.make_uniforms(n, T, seed=99)
+    L, nodes, toks = orc.accept_sampled(lg, drf, par, ua, us, tau)
+
+    def check(sel, want, what):
+        m = int(sel.sum())
+        assert m > 2000, (what, m)
+        got = np.bincount(toks[sel, 0 if what == "root" else 1], minlength=V)[:V] / m
+        sig = np.sqrt(want * (1 - want) / m)
+        assert np.all(np.abs(got - want) <= 5 * sig + 1e-12), (what, got, want)
+    check(np.ones(n, bool), _p64(rows[0], tau), "root")
+    # after child 1 (token 2) is accepted the next token follows row 1; after child 3
+    # (token 4) row 3
+    for c in (1, 3):
+        sel = (L >= 2) & (nodes[:, 1] == c)
+        m = int(sel.sum())
+        assert m > 2000, (c, m)
+        got = np.bincount(toks[sel, 1], minlength=V)[:V] / m
+        want = _p64(rows[c], tau)
+        sig = np.sqrt(want * (1 - want) / m)
+        assert np.all(np.abs(got - want) <= 5 * sig + 1e-12), (c, got, want)
+    assert not np.any(nodes == 2)
+    # acceptance rates: node 1 with p_root(2); node 3 after both token-2 proposals fail
+    p0 = _p64(rows[0], tau)
+    r1 = np.mean(nodes[:, 1] == 1)
+    assert abs(r1 - p0[2]) <= 5 * math.sqrt(p0[2] * (1 - p0[2]) / n)
+
+
+def pin_sampled_low_temperature_is_greedy(orc):
+    """As the temperature goes to 0 the target distribution is the argmax: with
+    distinct sibling tokens and well-separated maxima the sampled rule accepts
+    exactly the greedy longest matching path and emits the same tokens."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    for trial in range(40):
+        T = int(rng.integers(1, 24))
+        V = int(rng.integers(4, 40))
+        par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, T)], np.int32)
+        top = rng.integers(0, V, size=T)
+        lg = rng.uniform(-1.0, 0.0, size=(T, V)).astype(np.float32)
+        lg[np.arange(T), top] = 1.0                      # maxima 1 apart from the rest
+        drf = np.zeros(T, np.int32)
+        kids_of = [[c for c in range(T) if par[c] == v] for v in range(T)]
+        if max(len(k) for k in kids_of) > V:
+            continue
+        for v in range(T):
+            toks = rng.permutation(V)[:len(kids_of[v])]          # distinct sibling tokens
+            if len(toks) and top[v] not in toks and rng.random() < 0.7:
+                toks[0] = top[v]                                 # one child proposes the argmax
+            for c, t in zip(kids_of[v], toks):
+                drf[c] = t
+        ua, us = wl.make_uniforms(1, T, seed=trial)
+        _, Lg, ng, tg = orc.accept_longest_path(lg[None], drf[None], par[None])
+        Ls, ns, ts = orc.accept_sampled(lg[None], drf[None], par[None], ua, us, 1e-3)
+        assert Ls[0] == Lg[0] and np.array_equal(ns, ng) and np.array_equal(ts, tg), trial
+
+
+def pin_sampled_invariants(orc):
+    """On workload-shaped inputs: the path is a root path, the emitted tokens are the
+    accepted children's draft tokens then one drawn token, and the drawn token is
+    none of the final node's children's tokens (all of them were rejected)."""
+    for name, seed in (("tiny", 3), ("parity512", 4), ("batched8k", 5)):
+        kw = {"V": 2048} if name == "batched8k" else {}
+        if name == "batched8k":
+            kw.update(B=3, prefix=(16, 32))
+        inp = small_inputs(name, seed, **kw)
+        lg, drf, par = to_np(inp.logits), to_np(inp.draft), to_np(inp.parents)
+        B, T = par.shape
+        ua, us = wl.make_uniforms(B, T, seed)
+        L, nodes, toks = orc.accept_sampled(lg, drf, par, ua, us, inp.w.temperature)
+        for b in range(B):
+            assert 1 <= L[b] <= T
+            path = list(nodes[b, :L[b]])
+            assert path[0] == 0 and np.all(nodes[b, L[b]:] == -1) and np.all(toks[b, L[b]:] == -1)
+            for j in range(1, L[b]):
+                assert par[b, path[j]] == path[j - 1] and toks[b, j - 1] == drf[b, path[j]]
+            last = path[-1]
+            rejected = {int(drf[b, c]) for c in range(T) if par[b, c] == last}
+            assert int(toks[b, L[b] - 1]) not in rejected
+            assert 0 <= toks[b, L[b] - 1] < lg.shape[-1]
+
+
 # =========================================================================== commit pins
 def _commit_case(orc, name, seed, **kw):
     inp = small_inputs(name, seed, **kw)
@@ -561,6 +738,8 @@ ALL_PINS = [
     pin_argmax_numpy, pin_argmax_special_values, pin_argmax_planted,
     pin_accept_bruteforce, pin_accept_edge_cases, pin_accept_expected_tokens_golden,
     pin_accept_expected_tokens_closed_form,
+    pin_sampled_worked_examples, pin_sampled_expected_tokens_golden, pin_sampled_preserves_target,
+    pin_sampled_low_temperature_is_greedy, pin_sampled_invariants,
     pin_commit_invariants, pin_commit_single_root, pin_commit_refusals,
     pin_commit_chain_equals_serial,
 ]

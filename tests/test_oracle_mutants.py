@@ -43,6 +43,23 @@ MUTANTS = [
     ("accept_ties_to_largest", "match[i] && dep[i] > dep[best]",
      "match[i] && dep[i] >= dep[best]", 0),
     ("accept_ignores_tree_err", "(tree_err && tree_err[b] != 0) ||", "0 ||", 0),
+    ("sampled_no_renormalise", "R -= px;", "", 0),
+    ("sampled_rejected_token_drawn", "if (excl[y] || p[y] <= 0.0) continue;",
+     "if (p[y] <= 0.0) continue;", 0),
+    ("sampled_repeated_token_retried", "const double px = (in_vocab && !excl[x]) ? p[x] : 0.0;",
+     "const double px = in_vocab ? p[x] : 0.0;", 0),
+    ("sampled_compare_le", "* R < px) {", "* R <= px) {", 0),
+    ("sampled_root_row_only", "const float *row = logits + ((int64_t)b * T + v) * V;",
+     "const float *row = logits + ((int64_t)b * T) * V;", 0),
+    ("sampled_temperature_ignored", "exp((l - m) / tau)", "exp(l - m)", 0),
+    ("sampled_children_reversed", "for (int c = v + 1; c < T && next < 0; ++c) {",
+     "for (int c = T - 1; c > v && next < 0; --c) {", 0),
+    ("sampled_emits_parent_token", "toks[L - 1] = drf[next];", "toks[L - 1] = drf[v];", 0),
+    ("sampled_uniform_of_parent", "u_accept[(int64_t)b * T + c]", "u_accept[(int64_t)b * T + v]", 0),
+    ("sampled_draw_not_scaled", "const double target = (double)u_sample[(int64_t)b * T + v] * R;",
+     "const double target = (double)u_sample[(int64_t)b * T + v];", 0),
+    ("sampled_nan_counts", "if (isnan(x)) return -INFINITY;", "", 0),
+    ("sampled_ignores_tree_err", "(tree_err && tree_err[b] != 0) ||", "0 ||", 1),
     ("commit_copies_node_j", "* T + nodes[j]) * D;", "* T + j) * D;", 0),
     ("commit_v_from_k", "memcpy((char *)v_cache + dst * esz, (const char *)v_tree",
      "memcpy((char *)v_cache + dst * esz, (const char *)k_tree", 0),

@@ -50,6 +50,7 @@ class Workload:
     topk: int = 0                          # eagle2 trees
     capacity: int = 0                      # contiguous caches: rows per sequence
     qkv_std: float = 1.0
+    temperature: float = 0.3               # sampled acceptance: target softmax temperature
     notes: str = field(default="", compare=False)
 
 
@@ -300,6 +301,15 @@ def make_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu",
         k_pool=k_pool, v_pool=v_pool, block_table=t(table), block_size=bs,
         prefix_len=t(prefix), max_prefix_len=max_p, logits=logits,
         planted_argmax=t(top_np), draft=t(draft), scale=1.0 / math.sqrt(w.D))
+
+
+def make_uniforms(B: int, T: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """The random numbers sampled acceptance consumes, drawn up front: float32 in
+    [0, 1), u_accept[b][c] for trying node c as a proposal and u_sample[b][v] for
+    drawing the emitted token at node v (numpy PCG64, its own stream per seed)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 0x5A3D]))
+    u = rng.random((2, B, T), dtype=np.float32)
+    return np.ascontiguousarray(u[0]), np.ascontiguousarray(u[1])
 
 
 def scaled(w: Workload, **kw) -> Workload:
