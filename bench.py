@@ -259,10 +259,14 @@ def main():
     ms_step = ev[0].elapsed_time(ev[1]) / args.steps
     ms_attn = sum(a.elapsed_time(b) for a, b in ea) / args.steps
 
-    # per-stage split (separate pass, one call type at a time)
+    # per-stage split (separate pass, one call type at a time); the sampled acceptance
+    # (the alternative to the greedy accept stage) is timed here as well
+    ua, us = wl.make_uniforms(w.B, w.T, args.seed)
+    ua, us = torch.from_numpy(ua).to(dev), torch.from_numpy(us).to(dev)
     stages = {}
     for name, fn in (("mask", st.build_mask), ("attention", st.attention),
-                     ("accept", st.accept), ("commit", st.commit)):
+                     ("accept", st.accept), ("commit", st.commit),
+                     ("accept_sampled", lambda: st.accept_sampled(ua, us, w.temperature))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -287,7 +291,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "prefix": list(w.prefix), "tree_nodes": w.T,
                    "tree": w.tree, "vocab": w.V, "paged_block": w.block_size,
-                   "num_splits": args.splits, "seed": args.seed},
+                   "num_splits": args.splits, "seed": args.seed,
+                   "sampled_temperature": w.temperature},
         "roofline": {"bound": "hbm", "kernel": "tree-verify attention (split + merge kernels)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name),
@@ -297,6 +302,9 @@ def main():
         "stages_us": stages,
         "accepted_tokens_per_step": int(st.accepted_len.sum()),
         "argmax_gbs": round(bytes_argmax / (stages["accept"] * 1e-6) / 1e9, 1),
+        # sampled acceptance: one read of every logit row (the walk and the draw touch a
+        # few more bytes per sequence, not counted)
+        "accept_sampled_gbs": round(bytes_argmax / (stages["accept_sampled"] * 1e-6) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

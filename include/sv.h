@@ -9,6 +9,8 @@
  *                                ancestors (split-KV, GQA, log-sum-exp merge)
  *   3. sv_accept_longest_path    vocab argmax per row -> longest matching root path
  *                                -> accepted nodes and emitted tokens
+ *      (or sv_accept_sampled      target softmax per row -> proposals accepted with
+ *                                their target probability, emitted token drawn)
  *   4. sv_kv_commit              copy only the accepted rows' K/V into the cache
  *
  * Sources (web pages, by title and section):
@@ -22,7 +24,8 @@
  *     bother" (greedy longest-matching-prefix verification) and "What's not
  *     implemented" item 1 (ancestor-only tree attention, per-path argmax).
  *   "Speculative decoding verify batches to amortize ANE dispatch"
- *     (llms-explorer): Facts on the commit rule and on delayed KV write-through.
+ *     (llms-explorer): Facts on the commit rule, on delayed KV write-through and on
+ *     Forge's sampled verification.
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is device memory owned by the caller.  The library
@@ -194,6 +197,49 @@ int sv_accept_longest_path(const float *logits, const int32_t *draft, const int3
                            int32_t *argmax_out, int32_t *accepted_len, int32_t *accepted_nodes,
                            int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* Bytes of workspace sv_accept_sampled needs (0 when the shape is invalid). */
+size_t sv_accept_sampled_workspace_size(int32_t B, int32_t T, int64_t V);
+
+/*
+ * Sampled acceptance (temperature > 0), an alternative to sv_accept_longest_path
+ * with the same outputs, for sv_kv_commit to consume.
+ * Defined by: llms-explorer page Facts on Forge's sampled verification (the drafted
+ * path is treated as given; a proposal is accepted with its target probability; on
+ * rejection the target distribution is sampled with that proposal excluded, which
+ * keeps the target distribution).  The pages state the rule for one proposal; for a
+ * tree the children of a node are tried one after another as proposals from what is
+ * left.
+ *
+ *   logits  float32 [B][T][V]; row v gives node v's target distribution
+ *           p_v(x) = exp(l_v(x) / temperature) / sum_y exp(l_v(y) / temperature)
+ *           (NaN and -inf entries have probability 0, +inf counts as FLT_MAX; a row
+ *           without a finite entry has probability 0 everywhere)
+ *   draft, parents, tree_err: as for sv_accept_longest_path
+ *   u_accept float32 [B][T] in [0, 1): the draw for trying node c as a proposal
+ *   u_sample float32 [B][T] in [0, 1): the draw for the emitted token at node v
+ *           (the caller draws both; the library draws no random numbers)
+ *   temperature > 0 and finite
+ *   accepted_len, accepted_nodes, out_tokens: as for sv_accept_longest_path
+ * Walk: start at the root.  At the current node v the children are tried in
+ * increasing node index; with E the tokens rejected so far at v and
+ * R = 1 - sum_{x in E} p_v(x), child c with token x is accepted when
+ * u_accept[b][c] * R < p_v(x) (p = 0 for x in E or outside [0, V)) and becomes the
+ * current node; a rejected token joins E.  When no child is accepted (or v is a
+ * leaf) the emitted token is the smallest y not in E whose cumulative probability
+ * over tokens not in E exceeds u_sample[b][v] * R (token 0 when no probability is
+ * left).  out_tokens: the accepted children's draft tokens, then the emitted token.
+ * Precision: fp32 (the row sums in chunks); a decision within a few 1e-7 of its
+ * boundary can go either way, compared with an exact evaluation.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, V < 1, temperature not positive and
+ * finite), SV_ERR_TREE_SIZE, SV_ERR_OVERFLOW, SV_ERR_WORKSPACE, SV_ERR_ALIGN,
+ * SV_ERR_HIP.
+ */
+int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *parents,
+                      const int32_t *tree_err, const float *u_accept, const float *u_sample,
+                      float temperature, int32_t B, int32_t T, int64_t V, int32_t *accepted_len,
+                      int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Delayed KV write-through: commit only the accepted rows.

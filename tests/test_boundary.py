@@ -120,6 +120,27 @@ def test_accept_validation(lib):
     assert sv.sv_accept_longest_path_workspace_size(2, 0, 1000) == 0
 
 
+def test_accept_sampled_validation(lib):
+    f = lib.sv_accept_sampled
+    args = lambda B=2, T=8, V=1000, lg=FAKE, ua=FAKE, tau=0.5, ws=FAKE, wsb=1 << 30: (
+        lg, FAKE, FAKE, None, ua, FAKE, tau, B, T, V, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert f(*args(V=0)) == -2
+    assert f(*args(B=-3)) == -2
+    assert f(*args(tau=0.0)) == -2 and f(*args(tau=-1.0)) == -2
+    assert f(*args(tau=float("inf"))) == -2 and f(*args(tau=float("nan"))) == -2
+    assert f(*args(T=0)) == -6 and f(*args(T=65)) == -6
+    assert f(*args(V=1 << 31)) == -8
+    assert f(*args(lg=None)) == -1 and f(*args(ua=None)) == -1
+    assert f(*args(lg=FAKE + 2)) == -11
+    assert f(*args(wsb=8)) == -9
+    assert f(*args(ws=None)) == -9
+    assert f(*args(B=0)) == 0
+    assert sv.sv_accept_sampled_workspace_size(2, 8, 1000) > 0
+    assert sv.sv_accept_sampled_workspace_size(2, 0, 1000) == 0
+    # chunks of at most 65536 elements: (max, sum) per row and chunk
+    assert sv.sv_accept_sampled_workspace_size(1, 1, 151936) >= 3 * 8
+
+
 def test_commit_validation(lib):
     f = lib.sv_kv_commit
     def call(c=None, Hkv=2, T=8, D=256, maxp=100, kt=FAKE, B=2):

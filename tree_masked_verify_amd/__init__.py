@@ -23,7 +23,8 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -10: "SV_ERR_HIP", -11: "SV_ERR_ALIGN"}
 ENTRY_POINTS = ("sv_build_tree_mask", "sv_tree_verify_attention_workspace_size",
                 "sv_tree_verify_attention", "sv_accept_longest_path_workspace_size",
-                "sv_accept_longest_path", "sv_kv_commit", "sv_status_string")
+                "sv_accept_longest_path", "sv_accept_sampled_workspace_size",
+                "sv_accept_sampled", "sv_kv_commit", "sv_status_string")
 
 
 class SvError(RuntimeError):
@@ -63,12 +64,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sv_accept_longest_path_workspace_size.restype = sz
     lib.sv_accept_longest_path.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, vp, vp,
                                            sz, vp]
+    lib.sv_accept_sampled_workspace_size.argtypes = [i32, i32, i64]
+    lib.sv_accept_sampled_workspace_size.restype = sz
+    lib.sv_accept_sampled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i64, vp,
+                                      vp, vp, vp, sz, vp]
     lib.sv_kv_commit.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp,
                                  i32, i32, i32, i32, vp]
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
     for f in ("sv_build_tree_mask", "sv_tree_verify_attention", "sv_accept_longest_path",
-              "sv_kv_commit"):
+              "sv_accept_sampled", "sv_kv_commit"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -152,6 +157,22 @@ def sv_accept_longest_path(logits, draft, parents, tree_err, argmax_out, accepte
         workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream))
     _check("sv_accept_longest_path", rc)
+
+
+def sv_accept_sampled_workspace_size(B, T, V) -> int:
+    return int(load_library().sv_accept_sampled_workspace_size(B, T, V))
+
+
+def sv_accept_sampled(logits, draft, parents, tree_err, u_accept, u_sample, temperature,
+                      accepted_len, accepted_nodes, out_tokens, workspace, stream=None) -> None:
+    B, T = parents.shape
+    V = logits.shape[-1]
+    rc = load_library().sv_accept_sampled(
+        _ptr(logits), _ptr(draft), _ptr(parents), _ptr(tree_err), _ptr(u_accept), _ptr(u_sample),
+        float(temperature), B, T, V, _ptr(accepted_len), _ptr(accepted_nodes), _ptr(out_tokens),
+        _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None
+        else 0, _stream(stream))
+    _check("sv_accept_sampled", rc)
 
 
 def sv_kv_commit(k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: sv_kv_cache,

@@ -237,6 +237,37 @@ int sv_accept_longest_path(const float *logits, const int32_t *draft, const int3
                                     accepted_len, accepted_nodes, out_tokens, stream));
 }
 
+size_t sv_accept_sampled_workspace_size(int32_t B, int32_t T, int64_t V) {
+    if (B < 0 || T < 1 || T > 64 || V < 1 || V > INT_MAX) return 0;
+    ArgmaxPlan p;
+    if (make_sample_plan((int64_t)B * T, V, &p) != 0) return 0;
+    return round256(p.ws_bytes);
+}
+
+int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *parents,
+                      const int32_t *tree_err, const float *u_accept, const float *u_sample,
+                      float temperature, int32_t B, int32_t T, int64_t V, int32_t *accepted_len,
+                      int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    if (B < 0 || V < 1) return SV_ERR_SHAPE;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf())) return SV_ERR_SHAPE;
+    int64_t tmp;
+    if (V > INT_MAX || !prod_ok({(int64_t)B, T, V, 4}, &tmp)) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!logits || !draft || !parents || !u_accept || !u_sample || !accepted_len ||
+        !accepted_nodes || !out_tokens)
+        return SV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return SV_ERR_ALIGN;
+    ArgmaxPlan p;
+    if (make_sample_plan((int64_t)B * T, V, &p) != 0) return SV_ERR_SHAPE;
+    if (!workspace || workspace_bytes < p.ws_bytes) return SV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SV_ERR_ALIGN;
+    return hip_status(launch_accept_sampled(logits, draft, parents, tree_err, u_accept, u_sample,
+                                            temperature, B, T, V, p, workspace, accepted_len,
+                                            accepted_nodes, out_tokens, stream));
+}
+
 int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                  const int32_t *accepted_nodes, const int32_t *tree_err,
                  const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,

@@ -91,6 +91,15 @@ hipError_t launch_accept(const void *ws, const ArgmaxPlan &p, const int32_t *dra
                          int32_t *argmax_out, int32_t *accepted_len, int32_t *accepted_nodes,
                          int32_t *out_tokens, hipStream_t stream);
 
+// Sampled acceptance: per-chunk (max, sum) pairs [rows][chunks] in the workspace.
+int make_sample_plan(int64_t rows, int64_t V, ArgmaxPlan *p);
+hipError_t launch_accept_sampled(const float *logits, const int32_t *draft,
+                                 const int32_t *parents, const int32_t *tree_err,
+                                 const float *u_accept, const float *u_sample, float temperature,
+                                 int B, int T, int64_t V, const ArgmaxPlan &p, void *ws,
+                                 int32_t *accepted_len, int32_t *accepted_nodes,
+                                 int32_t *out_tokens, hipStream_t stream);
+
 hipError_t launch_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                             const int32_t *accepted_nodes, const int32_t *tree_err,
                             void *k_cache, void *v_cache, const CacheView &c,

@@ -2,14 +2,16 @@
 
 Allocation (outputs, workspaces) happens once in the constructor through torch; run()
 only enqueues sv_build_tree_mask -> sv_tree_verify_attention ->
-sv_accept_longest_path -> sv_kv_commit on one stream.
+sv_accept_longest_path -> sv_kv_commit on one stream.  accept_sampled() enqueues the
+sampled acceptance instead of the greedy one (same outputs, which commit() reads).
 """
 from __future__ import annotations
 
 import torch
 
 from . import (dtype_code, make_cache, sv_accept_longest_path,
-               sv_accept_longest_path_workspace_size, sv_build_tree_mask, sv_kv_commit,
+               sv_accept_longest_path_workspace_size, sv_accept_sampled,
+               sv_accept_sampled_workspace_size, sv_build_tree_mask, sv_kv_commit,
                sv_tree_verify_attention, sv_tree_verify_attention_workspace_size, workspace)
 
 
@@ -40,6 +42,7 @@ class VerifyStep:
         self.attn_ws = workspace(sv_tree_verify_attention_workspace_size(
             B, Hq, Hkv, T, D, self.max_prefix_len, dtype_code(q), self.num_splits), dev)
         self.acc_ws = workspace(sv_accept_longest_path_workspace_size(B, T, V), dev)
+        self.smp_ws = workspace(sv_accept_sampled_workspace_size(B, T, V), dev)
 
     @classmethod
     def from_inputs(cls, inp, num_splits=0, new_prefix_len=None):
@@ -59,6 +62,11 @@ class VerifyStep:
         sv_accept_longest_path(self.logits, self.draft, self.parents, self.tree_err,
                                self.argmax, self.accepted_len, self.accepted_nodes,
                                self.out_tokens, self.acc_ws, stream)
+
+    def accept_sampled(self, u_accept, u_sample, temperature, stream=None):
+        sv_accept_sampled(self.logits, self.draft, self.parents, self.tree_err, u_accept,
+                          u_sample, temperature, self.accepted_len, self.accepted_nodes,
+                          self.out_tokens, self.smp_ws, stream)
 
     def commit(self, stream=None):
         sv_kv_commit(self.k_tree, self.v_tree, self.accepted_len, self.accepted_nodes,
