@@ -53,11 +53,14 @@ def _declare(lib):
     lib.oracle_accept_sampled.argtypes = [
         _f32p, _i32p, _i32p, _i32p, _f32p, _f32p, ctypes.c_double, _int, _int, _i64, _i32p,
         _i32p, _i32p]
+    lib.oracle_rope_tree.argtypes = [_vp, _vp, _i32p, _i32p, _int, _int, _int, _int, _int, _int,
+                                     ctypes.c_double]
     lib.oracle_kv_commit.argtypes = [
         _vp, _vp, _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64,
         _int, _i32p, _int, _i32p, _int, _int, _int, _int]
     for f in ("oracle_build_tree_mask", "oracle_tree_verify_attention", "oracle_argmax",
-              "oracle_accept_longest_path", "oracle_accept_sampled", "oracle_kv_commit"):
+              "oracle_accept_longest_path", "oracle_accept_sampled", "oracle_rope_tree",
+              "oracle_kv_commit"):
         getattr(lib, f).restype = _int
     return lib
 
@@ -195,6 +198,21 @@ class Oracle:
             _p(nodes, _i32p), _p(toks, _i32p))
         assert rc == 0
         return L, nodes, toks
+
+    def rope_tree(self, q, k_tree, prefix_len, depth, theta, dtype):
+        """Returns rotated copies of q [B, Hq, T, D] and k_tree [B, Hkv, T, D] (float32
+        arrays, or uint16 bf16 bit patterns with dtype BF16)."""
+        q = np.array(q, copy=True, order="C")
+        k = np.array(k_tree, copy=True, order="C")
+        prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        depth = np.ascontiguousarray(depth, dtype=np.int32)
+        B, Hq, T, D = q.shape
+        Hkv = k.shape[1]
+        rc = self.lib.oracle_rope_tree(q.ctypes.data, k.ctypes.data, _p(prefix_len, _i32p),
+                                       _p(depth, _i32p), B, Hq, Hkv, T, D, int(dtype),
+                                       float(theta))
+        assert rc == 0
+        return q, k
 
     def kv_commit(self, k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: Cache,
                   prefix_len, max_prefix_len, new_prefix_len=True):

@@ -16,7 +16,8 @@
  *  [ADR]  "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status
  *         table rows E1.1-E1.5 (tree attention parity ladder, output layout
  *         [q_seq_len, num_heads, head_dim]), E4a (build_tree_mask from the
- *         parent array), E4b.10a (smaller token wins ties), E5a (tree-walk
+ *         parent array), E4b.5b (NeoX RoPE at base position + tree depth, over
+ *         the whole head), E4b.10a (smaller token wins ties), E5a (tree-walk
  *         accept), E6 v2 (mask selects ancestors + self); section 4 Phase E1
  *         (dynamic tree mask, apply_tree_attention) and Phase E5 (longest
  *         matching path from root; full accept picks the deepest).
@@ -425,6 +426,61 @@ int oracle_accept_sampled(const float *logits, const int32_t *draft, const int32
         accepted_len[b] = L;
     }
     free(p); free(excl); free(path);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tree-position RoPE ([ADR] row E4b.5b: positions base_pos + tree depth, NeoX  */
+/* style, the rotation covers the whole head).  For node i of sequence b,       */
+/* pos = prefix_len[b] + depth[b][i]; for j < D/2 with f_j = theta^(-2j/D) and  */
+/* a = pos * f_j:                                                               */
+/*   x'[j]       = x[j] cos a - x[j + D/2] sin a                                */
+/*   x'[j + D/2] = x[j + D/2] cos a + x[j] sin a                                */
+/* applied in place to every head of Q [B][Hq][T][D] and of the tree keys       */
+/* [B][Hkv][T][D]; each result is rounded to the tensor's type (to fp32 by     */
+/* round-to-nearest-even, then to bf16 by round-to-nearest-even).              */
+static void store_elem(void *base, int dtype, int64_t idx, double v) {
+    float f = (float)v;
+    if (dtype == OR_F32) {
+        ((float *)base)[idx] = f;
+        return;
+    }
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    if ((bits & 0x7f800000u) == 0x7f800000u && (bits & 0x007fffffu)) {
+        ((uint16_t *)base)[idx] = (uint16_t)((bits >> 16) | 0x40u);  /* NaN stays NaN */
+        return;
+    }
+    const uint32_t lsb = (bits >> 16) & 1u;
+    bits += 0x7fffu + lsb;                                             /* nearest, ties to even */
+    ((uint16_t *)base)[idx] = (uint16_t)(bits >> 16);
+}
+
+static void rope_rows(void *x, int dtype, int64_t nheads, const int32_t *prefix_len,
+                      const int32_t *depth, int B, int T, int D, double theta) {
+    const int half = D / 2;
+    for (int b = 0; b < B; ++b)
+        for (int64_t h = 0; h < nheads; ++h)
+            for (int i = 0; i < T; ++i) {
+                const double pos = (double)prefix_len[b] + (double)depth[(int64_t)b * T + i];
+                const int64_t row = (((int64_t)b * nheads + h) * T + i) * D;
+                for (int j = 0; j < half; ++j) {
+                    const double f = pow(theta, -2.0 * (double)j / (double)D);
+                    const double a = pos * f;
+                    const double c = cos(a), sn = sin(a);
+                    const double x1 = elem(x, dtype, row + j), x2 = elem(x, dtype, row + j + half);
+                    store_elem(x, dtype, row + j, x1 * c - x2 * sn);
+                    store_elem(x, dtype, row + j + half, x2 * c + x1 * sn);
+                }
+            }
+}
+
+int oracle_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t *depth,
+                     int B, int Hq, int Hkv, int T, int D, int dtype, double theta) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || T < 1 || D < 2 || (D & 1) || !(theta > 0) || isinf(theta))
+        return -1;
+    rope_rows(q, dtype, Hq, prefix_len, depth, B, T, D, theta);
+    rope_rows(k_tree, dtype, Hkv, prefix_len, depth, B, T, D, theta);
     return 0;
 }
 

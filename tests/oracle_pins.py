@@ -632,6 +632,94 @@ def pin_sampled_invariants(orc):
             assert 0 <= toks[b, L[b] - 1] < lg.shape[-1]
 
 
+# =========================================================================== RoPE pins
+def _bf16_to_f64(a):
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_rope_worked_examples(orc):
+    """D = 4, theta = 100: frequencies 1 and 100^(-1/2) = 0.1 (hand-derived); position
+    = prefix + depth; position 0 leaves the vector unchanged bit for bit."""
+    q = np.zeros((1, 1, 3, 4), np.float32)
+    q[0, 0, :, 0] = 1.0                                   # e0 on every node
+    k = np.zeros((1, 1, 3, 4), np.float32)
+    k[0, 0, :, 1] = 2.0                                   # 2 e1
+    depth = np.array([[0, 1, 2]], np.int32)
+    qo, ko = orc.rope_tree(q, k, np.array([5], np.int32), depth, 100.0, O.F32)
+    for i, pos in enumerate((5, 6, 7)):
+        want_q = [math.cos(pos), 0.0, math.sin(pos), 0.0]
+        want_k = [0.0, 2 * math.cos(0.1 * pos), 0.0, 2 * math.sin(0.1 * pos)]
+        assert np.allclose(qo[0, 0, i], want_q, atol=1e-7), (i, qo[0, 0, i], want_q)
+        assert np.allclose(ko[0, 0, i], want_k, atol=2e-7), (i, ko[0, 0, i], want_k)
+    rng = np.random.Generator(np.random.PCG64(3))
+    x = rng.standard_normal((2, 3, 4, 8)).astype(np.float32)
+    y = rng.standard_normal((2, 1, 4, 8)).astype(np.float32)
+    x0, y0 = orc.rope_tree(x, y, np.zeros(2, np.int32), np.zeros((2, 4), np.int32), 1e4, O.F32)
+    assert np.array_equal(x0, x) and np.array_equal(y0, y)
+
+
+def pin_rope_relative_position(orc):
+    """Rotary embeddings make <R(q, m), R(k, n)> depend on m - n only: shifting every
+    position by the same amount (through the prefix) keeps all query-key dot products."""
+    rng = np.random.Generator(np.random.PCG64(4))
+    B, Hq, Hkv, T, D = 1, 2, 1, 6, 64
+    q = rng.standard_normal((B, Hq, T, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    depth = np.array([[0, 1, 1, 2, 3, 2]], np.int32)
+    dots = []
+    for P in (0, 37, 1000):
+        qo, ko = orc.rope_tree(q, k, np.array([P], np.int32), depth, 1e4, O.F32)
+        dots.append(np.einsum("hid,jd->hij", qo[0].astype(np.float64), ko[0, 0].astype(np.float64)))
+    assert np.allclose(dots[0], dots[1], atol=2e-4) and np.allclose(dots[0], dots[2], atol=2e-4)
+    # while rotating one side only does change them
+    qo, _ = orc.rope_tree(q, k, np.array([37], np.int32), depth, 1e4, O.F32)
+    plain = np.einsum("hid,jd->hij", qo[0].astype(np.float64), k[0, 0].astype(np.float64))
+    assert not np.allclose(plain, dots[0], atol=1e-2)
+
+
+def pin_rope_pairs_and_tree(orc):
+    """NeoX pairs (j, j + D/2) keep their norms; a tree node is rotated like the chain
+    node at its depth (position = prefix + depth), so siblings with equal inputs agree."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    T, D = 7, 16
+    v = rng.standard_normal(D).astype(np.float32)
+    q = np.tile(v, (1, 1, T, 1)).astype(np.float32)
+    k = np.tile(v, (1, 2, T, 1)).astype(np.float32)
+    tree_depth = np.array([[0, 1, 1, 2, 2, 3, 1]], np.int32)
+    chain_depth = np.arange(T, dtype=np.int32)[None]
+    qt, kt = orc.rope_tree(q, k, np.array([100], np.int32), tree_depth, 500.0, O.F32)
+    qc, _ = orc.rope_tree(q, k, np.array([100], np.int32), chain_depth, 500.0, O.F32)
+    for i in range(T):
+        assert np.array_equal(qt[0, 0, i], qc[0, 0, tree_depth[0, i]]), i
+        assert np.array_equal(kt[0, 1, i], qt[0, 0, i]), i
+    n_in = v[:D // 2].astype(np.float64) ** 2 + v[D // 2:].astype(np.float64) ** 2
+    for i in range(T):
+        r = qt[0, 0, i].astype(np.float64)
+        n_out = r[:D // 2] ** 2 + r[D // 2:] ** 2
+        assert np.allclose(n_out, n_in, rtol=1e-6, atol=1e-7), i
+
+
+def pin_rope_bf16_rounding(orc):
+    """bf16 tensors: the result is the fp32 result rounded to nearest-even bf16 (the bits
+    of the fp32 value's top half, rounded), checked against numpy's own rounding."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    B, Hq, Hkv, T, D = 2, 2, 1, 5, 32
+    qf = rng.standard_normal((B, Hq, T, D)).astype(np.float32)
+    kf = rng.standard_normal((B, Hkv, T, D)).astype(np.float32)
+    to_bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)   # exact: bf16 inputs
+    qb = to_bits(qf)
+    kb = to_bits(kf)
+    P = np.array([3, 900], np.int32)
+    depth = np.array([[0, 1, 1, 2, 3], [0, 1, 2, 3, 4]], np.int32)
+    q32, k32 = orc.rope_tree(_bf16_to_f64(qb).astype(np.float32), _bf16_to_f64(kb).astype(np.float32),
+                             P, depth, 1e4, O.F32)
+    qo, ko = orc.rope_tree(qb, kb, P, depth, 1e4, O.BF16)
+    t = torch.from_numpy(q32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(qo, t)
+    t = torch.from_numpy(k32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ko, t)
+
+
 # =========================================================================== commit pins
 def _commit_case(orc, name, seed, **kw):
     inp = small_inputs(name, seed, **kw)
@@ -740,6 +828,8 @@ ALL_PINS = [
     pin_accept_expected_tokens_closed_form,
     pin_sampled_worked_examples, pin_sampled_expected_tokens_golden, pin_sampled_preserves_target,
     pin_sampled_low_temperature_is_greedy, pin_sampled_invariants,
+    pin_rope_worked_examples, pin_rope_relative_position, pin_rope_pairs_and_tree,
+    pin_rope_bf16_rounding,
     pin_commit_invariants, pin_commit_single_root, pin_commit_refusals,
     pin_commit_chain_equals_serial,
 ]

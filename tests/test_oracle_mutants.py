@@ -60,6 +60,16 @@ MUTANTS = [
      "const double target = (double)u_sample[(int64_t)b * T + v];", 0),
     ("sampled_nan_counts", "if (isnan(x)) return -INFINITY;", "", 0),
     ("sampled_ignores_tree_err", "(tree_err && tree_err[b] != 0) ||", "0 ||", 1),
+    ("rope_gptj_pairs", "const double x1 = elem(x, dtype, row + j), x2 = elem(x, dtype, row + j + half);",
+     "const double x1 = elem(x, dtype, row + (2 * j) % D), x2 = elem(x, dtype, row + (2 * j + 1) % D);", 0),
+    ("rope_frequency_exponent", "pow(theta, -2.0 * (double)j / (double)D)", "pow(theta, -(double)j / (double)D)", 0),
+    ("rope_sign", "x1 * c - x2 * sn", "x1 * c + x2 * sn", 0),
+    ("rope_position_is_index", "(double)prefix_len[b] + (double)depth[(int64_t)b * T + i]",
+     "(double)prefix_len[b] + (double)i", 0),
+    ("rope_prefix_ignored", "(double)prefix_len[b] + (double)depth[(int64_t)b * T + i]",
+     "(double)depth[(int64_t)b * T + i]", 0),
+    ("rope_keys_not_rotated", "    rope_rows(k_tree, dtype, Hkv, prefix_len, depth, B, T, D, theta);\n", "", 0),
+    ("rope_bf16_truncates", "bits += 0x7fffu + lsb;", "(void)lsb;", 0),
     ("commit_copies_node_j", "* T + nodes[j]) * D;", "* T + j) * D;", 0),
     ("commit_v_from_k", "memcpy((char *)v_cache + dst * esz, (const char *)v_tree",
      "memcpy((char *)v_cache + dst * esz, (const char *)k_tree", 0),
