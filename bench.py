@@ -263,10 +263,15 @@ def main():
     # (the alternative to the greedy accept stage) is timed here as well
     ua, us = wl.make_uniforms(w.B, w.T, args.seed)
     ua, us = torch.from_numpy(ua).to(dev), torch.from_numpy(us).to(dev)
+    # and the tree-position rotary embedding (in place on Q and the tree keys; last, so
+    # that the other stages are timed on the unrotated inputs)
+    from tree_masked_verify_amd import sv_rope_tree
     stages = {}
     for name, fn in (("mask", st.build_mask), ("attention", st.attention),
                      ("accept", st.accept), ("commit", st.commit),
-                     ("accept_sampled", lambda: st.accept_sampled(ua, us, w.temperature))):
+                     ("accept_sampled", lambda: st.accept_sampled(ua, us, w.temperature)),
+                     ("rope", lambda: sv_rope_tree(st.q, st.k_tree, st.prefix_len, st.depth,
+                                                   1e4))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -305,6 +310,9 @@ def main():
         # sampled acceptance: one read of every logit row (the walk and the draw touch a
         # few more bytes per sequence, not counted)
         "accept_sampled_gbs": round(bytes_argmax / (stages["accept_sampled"] * 1e-6) / 1e9, 1),
+        # rotary embedding: Q and tree keys read and written once
+        "rope_gbs": round(2 * w.B * (w.Hq + w.Hkv) * w.T * w.D * (2 if w.dtype == "bf16" else 4)
+                          / (stages["rope"] * 1e-6) / 1e9, 1),
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

@@ -11,13 +11,16 @@
  *                                -> accepted nodes and emitted tokens
  *      (or sv_accept_sampled      target softmax per row -> proposals accepted with
  *                                their target probability, emitted token drawn)
+ *   sv_rope_tree (before 2, when the caller's Q and tree keys are not yet rotated):
+ *                                rotary embedding at base position + tree depth
  *   4. sv_kv_commit              copy only the accepted rows' K/V into the cache
  *
  * Sources (web pages, by title and section):
  *   "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status rows
  *     E1.1-E1.5 (tree attention; output layout [q_seq_len, num_heads, head_dim];
  *     head_dim 256/512), E1 review gate (dtype and byte-length validation), E4a
- *     (build_tree_mask from the parent array, checked overflow), E5a (tree-walk
+ *     (build_tree_mask from the parent array, checked overflow), E4b.5b
+ *     (tree-position RoPE), E5a (tree-walk
  *     accept), E6 (zero-head guard before the GQA modulo), E6 v2 (ancestors +
  *     self); section 4, Phases E1 and E5.
  *   "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs): "Why
@@ -240,6 +243,32 @@ int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *
                       float temperature, int32_t B, int32_t T, int64_t V, int32_t *accepted_len,
                       int32_t *accepted_nodes, int32_t *out_tokens, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Tree-position rotary embedding of the queries and tree keys, in place.
+ * Defined by: ADR-037 Phase status row E4b.5b (RoPE on Q/K with tree positions
+ * base position + tree depth, NeoX style, the rotation covers the whole head; rope
+ * theta finite, head_dim even).
+ *
+ *   q       [B][Hq][T][D], k_tree [B][Hkv][T][D], float32 or bf16 (dtype), rotated
+ *           in place
+ *   prefix_len int32 [B]: base position of each sequence's root
+ *   depth   int32 [B][T]: tree depth of each node (sv_build_tree_mask's output)
+ *   theta   > 0 and finite (e.g. 10000)
+ * Node i of sequence b sits at position prefix_len[b] + depth[b][i] (siblings share
+ * a position; a chain gets consecutive ones).  For j < D/2, with
+ * a = position * theta^(-2j/D):
+ *   x[j] <- x[j] cos a - x[j + D/2] sin a,   x[j + D/2] <- x[j + D/2] cos a + x[j] sin a.
+ * Angles, their cosines and sines and the rotation are evaluated in fp64 (an angle is
+ * within about position * 2^-52 rad of exact, ~5e-7 at 2^31), each result is rounded
+ * once to the tensor's type.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, Hq or Hkv < 1, D odd or outside
+ * [2, 1024], theta not positive and finite), SV_ERR_TREE_SIZE, SV_ERR_DTYPE,
+ * SV_ERR_OVERFLOW, SV_ERR_ALIGN, SV_ERR_HIP.
+ */
+int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t *depth,
+                 int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, int32_t dtype,
+                 double theta, hipStream_t stream);
 
 /*
  * Delayed KV write-through: commit only the accepted rows.

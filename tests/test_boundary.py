@@ -141,6 +141,21 @@ def test_accept_sampled_validation(lib):
     assert sv.sv_accept_sampled_workspace_size(1, 1, 151936) >= 3 * 8
 
 
+def test_rope_validation(lib):
+    f = lib.sv_rope_tree
+    args = lambda B=2, Hq=4, Hkv=2, T=8, D=128, dt=sv.SV_BF16, th=1e4, q=FAKE: (
+        q, FAKE, FAKE, FAKE, B, Hq, Hkv, T, D, dt, th, None)
+    assert f(*args(D=127)) == -2 and f(*args(D=0)) == -2 and f(*args(D=2048)) == -2
+    assert f(*args(th=0.0)) == -2 and f(*args(th=-1.0)) == -2
+    assert f(*args(th=float("inf"))) == -2 and f(*args(th=float("nan"))) == -2
+    assert f(*args(Hq=0)) == -2 and f(*args(Hkv=0)) == -2 and f(*args(B=-1)) == -2
+    assert f(*args(T=0)) == -6 and f(*args(T=65)) == -6
+    assert f(*args(dt=3)) == -3
+    assert f(*args(q=None)) == -1
+    assert f(*args(q=FAKE + 1)) == -11 and f(*args(q=FAKE + 2, dt=sv.SV_F32)) == -11
+    assert f(*args(B=0)) == 0
+
+
 def test_commit_validation(lib):
     f = lib.sv_kv_commit
     def call(c=None, Hkv=2, T=8, D=256, maxp=100, kt=FAKE, B=2):

@@ -24,7 +24,7 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
 ENTRY_POINTS = ("sv_build_tree_mask", "sv_tree_verify_attention_workspace_size",
                 "sv_tree_verify_attention", "sv_accept_longest_path_workspace_size",
                 "sv_accept_longest_path", "sv_accept_sampled_workspace_size",
-                "sv_accept_sampled", "sv_kv_commit", "sv_status_string")
+                "sv_accept_sampled", "sv_rope_tree", "sv_kv_commit", "sv_status_string")
 
 
 class SvError(RuntimeError):
@@ -68,12 +68,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sv_accept_sampled_workspace_size.restype = sz
     lib.sv_accept_sampled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, i32, i32, i64, vp,
                                       vp, vp, vp, sz, vp]
+    lib.sv_rope_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_double,
+                                 vp]
     lib.sv_kv_commit.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp,
                                  i32, i32, i32, i32, vp]
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
     for f in ("sv_build_tree_mask", "sv_tree_verify_attention", "sv_accept_longest_path",
-              "sv_accept_sampled", "sv_kv_commit"):
+              "sv_accept_sampled", "sv_rope_tree", "sv_kv_commit"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +175,14 @@ def sv_accept_sampled(logits, draft, parents, tree_err, u_accept, u_sample, temp
         _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None
         else 0, _stream(stream))
     _check("sv_accept_sampled", rc)
+
+
+def sv_rope_tree(q, k_tree, prefix_len, depth, theta, stream=None) -> None:
+    B, Hq, T, D = q.shape
+    Hkv = k_tree.shape[1]
+    rc = load_library().sv_rope_tree(_ptr(q), _ptr(k_tree), _ptr(prefix_len), _ptr(depth), B, Hq,
+                                     Hkv, T, D, dtype_code(q), float(theta), _stream(stream))
+    _check("sv_rope_tree", rc)
 
 
 def sv_kv_commit(k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: sv_kv_cache,

@@ -268,6 +268,24 @@ int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *
                                             accepted_nodes, out_tokens, stream));
 }
 
+int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t *depth,
+                 int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, int32_t dtype,
+                 double theta, hipStream_t stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || D < 2 || D > 1024 || (D & 1)) return SV_ERR_SHAPE;
+    if (!(theta > 0.0) || !(theta < __builtin_huge_val())) return SV_ERR_SHAPE;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+    int64_t tmp;
+    if (!prod_ok({(int64_t)B, (int64_t)Hq + Hkv, T, D, 4}, &tmp)) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!q || !k_tree || !prefix_len || !depth) return SV_ERR_NULL;
+    const uintptr_t al = dtype == SV_BF16 ? 1u : 3u;
+    if ((reinterpret_cast<uintptr_t>(q) & al) || (reinterpret_cast<uintptr_t>(k_tree) & al))
+        return SV_ERR_ALIGN;
+    return hip_status(launch_rope_tree(q, k_tree, prefix_len, depth, B, Hq, Hkv, T, D, dtype,
+                                       theta, stream));
+}
+
 int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                  const int32_t *accepted_nodes, const int32_t *tree_err,
                  const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,

@@ -100,6 +100,10 @@ hipError_t launch_accept_sampled(const float *logits, const int32_t *draft,
                                  int32_t *accepted_len, int32_t *accepted_nodes,
                                  int32_t *out_tokens, hipStream_t stream);
 
+hipError_t launch_rope_tree(void *q, void *k_tree, const int32_t *prefix_len,
+                            const int32_t *depth, int B, int Hq, int Hkv, int T, int D, int dtype,
+                            double theta, hipStream_t stream);
+
 hipError_t launch_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                             const int32_t *accepted_nodes, const int32_t *tree_err,
                             void *k_cache, void *v_cache, const CacheView &c,
