@@ -121,7 +121,10 @@ def counter_traffic(workload):
             fields[k.strip()] = v.strip()
     h = hashlib.sha256()
     for name in fields.get("sources", "").split():
-        with open(os.path.join(ROOT, "tree_masked_verify_amd", "csrc", name), "rb") as f:
+        path = os.path.join(ROOT, "tree_masked_verify_amd", "csrc", name)
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as f:
             h.update(f.read())
     if not fields.get("sources") or h.hexdigest() != fields.get("sources_sha256"):
         return None

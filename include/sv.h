@@ -18,7 +18,8 @@
  * Sources (web pages, by title and section):
  *   "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status rows
  *     E1.1-E1.5 (tree attention; output layout [q_seq_len, num_heads, head_dim];
- *     head_dim 256/512), E1 review gate (dtype and byte-length validation), E4a
+ *     head_dim 256/512), E4b.6 (the head_dim-128 retrofit of the tree attention),
+ *     E1 review gate (dtype and byte-length validation), E4a
  *     (build_tree_mask from the parent array, checked overflow), E4b.5b
  *     (tree-position RoPE), E5a (tree-walk
  *     accept), E6 (zero-head guard before the GQA modulo), E6 v2 (ancestors +
@@ -61,7 +62,7 @@ typedef enum sv_status {
     SV_ERR_SHAPE = -2,      /* a size is negative/zero where not allowed, or inconsistent */
     SV_ERR_DTYPE = -3,      /* unknown dtype, or dtype not supported for this call */
     SV_ERR_GQA = -4,        /* Hkv <= 0, Hq <= 0 or Hq not a multiple of Hkv */
-    SV_ERR_HEAD_DIM = -5,   /* head_dim not 256 or 512 */
+    SV_ERR_HEAD_DIM = -5,   /* head_dim not 128, 256 or 512 */
     SV_ERR_TREE_SIZE = -6,  /* T outside [1, 64] */
     SV_ERR_CAPACITY = -7,   /* max_prefix_len + T exceeds the rows the block table reserves */
     SV_ERR_OVERFLOW = -8,   /* a byte size does not fit in 64 bits / an index in 32 bits */

@@ -71,7 +71,7 @@ def test_attention_validation(lib):
     assert attn(lib, Hkv=0) == -4
     assert attn(lib, Hq=0) == -4
     assert attn(lib, Hq=6, Hkv=4) == -4
-    assert attn(lib, D=128) == -5
+    assert attn(lib, D=64) == -5 and attn(lib, D=100) == -5 and attn(lib, D=1024) == -5
     assert attn(lib, T=0) == -6 and attn(lib, T=65) == -6
     assert attn(lib, B=-1) == -2 and attn(lib, maxp=-1) == -2 and attn(lib, splits=-2) == -2
     assert attn(lib, c=cache(dtype=9)) == -3
@@ -99,7 +99,8 @@ def test_attention_workspace_size(lib):
     assert a > 0 and b > 0
     assert b >= 16 * 8 * 4 * 240 * 256 * 4            # 4 chunks of fp32 partials per row
     assert f(16, 32, 0, 60, 256, 32768, sv.SV_BF16) == 0
-    assert f(16, 32, 8, 60, 128, 32768, sv.SV_BF16) == 0
+    assert f(16, 32, 8, 60, 64, 32768, sv.SV_BF16) == 0
+    assert f(16, 32, 8, 60, 128, 32768, sv.SV_BF16) > 0   # head_dim 128 is supported
     assert f(1, 1, 1, 1, 256, 0, sv.SV_F32) > 0
 
 

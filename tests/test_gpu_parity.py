@@ -122,3 +122,27 @@ def test_fp32_gqa(orc):
 
 def test_unaligned_vocab(orc):
     run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="v1001", V=1001, B=3), 11)
+
+
+# ----------------------------------------------------------------- head_dim 128
+@pytest.mark.parametrize("seed", [0, 1])
+def test_parity512_head_dim_128(orc, seed):
+    """Matrix-core path (bf16, 64 rows per kv head) at head_dim 128."""
+    run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], D=128, name="parity512-d128"), seed)
+
+
+def test_tiny_head_dim_128(orc):
+    """VALU path (fp32) at head_dim 128."""
+    run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], D=128, name="tiny-d128"), 0)
+
+
+def test_batched8k_head_dim_128(orc):
+    """Paged, shuffled, variable prefix, 512 rows per kv head (two row groups)."""
+    w = wl.scaled(wl.WORKLOADS["batched8k"], D=128, B=6, name="batched8k-d128")
+    run_case(orc, w, 5, rows=sample_rows(w, 200, 5))
+
+
+def test_long32k_head_dim_128_full_size(orc):
+    """The 32K shape at head_dim 128, full size, sampled rows against the oracle."""
+    w = wl.WORKLOADS["long32k_d128"]
+    run_case(orc, w, 0, rows=sample_rows(w, 120, 9))

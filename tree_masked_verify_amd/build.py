@@ -23,10 +23,10 @@ FLAGS = [
     # no packed fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Per-file additions.  The head_dim-256 attention kernel handles finite scores and -inf
+# Per-file additions.  The head_dim-128/256 attention kernel handles finite scores and -inf
 # (masked keys) only; without NaN semantics its row maxima need no canonicalising
 # moves before each v_max.
-FILE_FLAGS = {"attn_mfma256.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"attn_mfma_w4.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra: list[str], obj_dir: str) -> str:

@@ -552,8 +552,9 @@ hipError_t launch_d(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
+    if (a.D == 128) return launch_attn_w4(a, pl, stream);
 #ifndef SV_ATTN_LEGACY256
-    if (a.D == 256) return launch_attn_mfma256(a, pl, stream);
+    if (a.D == 256) return launch_attn_w4(a, pl, stream);
 #endif
     return a.D == 256 ? launch_d<256>(a, pl, stream) : launch_d<512>(a, pl, stream);
 }

@@ -1,8 +1,8 @@
-// attn_mfma256.hip -- tree-masked split-KV attention for head_dim 256 on the gfx950
-// matrix cores, one wavefront per SIMD.
+// attn_mfma_w4.hip -- tree-masked split-KV attention for head_dim 128 and 256 on the
+// gfx950 matrix cores, one wavefront per SIMD.
 //
-// What is computed (ADR-037 Phase status rows E1.1-E1.5, section 4 Phase E1;
-// Medusa/EAGLE-2 page "What's not implemented" 1(c)): every query row (q head g of
+// What is computed (ADR-037 Phase status rows E1.1-E1.5, section 4 Phase E1, and row
+// E4b.6 for head_dim 128; Medusa/EAGLE-2 page "What's not implemented" 1(c)): every query row (q head g of
 // kv head kvh, tree node i) attends to the cached prefix of its sequence and to
 // the tree rows its ancestor mask selects.  One workgroup covers one
 // (sequence, kv head, prefix chunk, row group); it leaves an unnormalised partial
@@ -10,10 +10,10 @@
 //
 // Organisation (4 wavefronts per workgroup, one per SIMD, one workgroup per CU):
 //   * a wavefront owns 64 query rows as two 32-row blocks; their Q fragments stay in
-//     registers (128 VGPRs) and their output accumulators in the accumulation
-//     registers (256 AGPRs), so every K and V fragment read from LDS serves 64 rows;
+//     registers (D / 2 VGPRs) and their output accumulators in the accumulation
+//     registers (D AGPRs), so every K and V fragment read from LDS serves 64 rows;
 //   * keys stream through a 4-deep ring of LDS stages, 32 keys of K and V per stage,
-//     filled by direct global->LDS loads (global_load_lds_dwordx4, 1 KB per load)
+//     filled by direct global->LDS loads (global_load_lds_dwordx4, two key rows per load)
 //     issued three tiles ahead between the score product's matrix instructions; one
 //     barrier per tile;
 //   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
@@ -42,53 +42,78 @@ namespace w4 {
 #define SV_W4_VD 4  // V fragments read ahead (d blocks)
 #endif
 
-constexpr int D = 256;
 constexpr int kW = 4;                    // wavefronts per workgroup
 constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerWG = kW * kRowsPerWave;
-constexpr int KS = D / 16;               // 16-wide k-steps of S^T = K Q^T
-constexpr int DB = D / 32;               // 32-wide d blocks of O^T
-// LDS tile: 16 units of 1 KB per tensor, unit p holding keys p and p + 16 side by side
-// (one wavefront-wide direct load each).  K units are padded by 16 bytes (the K
-// fragment read, 16 lanes x 16 bytes per LDS cycle, then touches 64 distinct banks),
-// V units by 64 bytes (the transposing read, 32 lanes x 8 bytes per cycle over four
-// units, likewise).
-constexpr int UNITS = 16;
-constexpr int KU = 1024 + 16;
-constexpr int VU = 1024 + 64;
-constexpr int KTILE = UNITS * KU;
-constexpr int STAGE_BYTES = UNITS * (KU + VU);
+constexpr int UNITS = 16;                // LDS units per tensor and tile
 constexpr int NST = 4;                   // ring depth
 constexpr int LOOK = 3;                  // tiles loaded ahead (a stage is free once its PV is done)
 constexpr int NI = 2 * UNITS / kW;       // loads per wavefront per tile
 constexpr int VMWAIT = NI * (LOOK - 1);  // loads left in flight at a wait
 constexpr int kGrpMax = 2048;            // 16-key groups of one chunk in the LDS table
-constexpr int GTAB_OFF = NST * STAGE_BYTES;
-constexpr int MASK_OFF = GTAB_OFF + kGrpMax * 4;
 constexpr uint32_t kNoGroup = 0xffffffffu;  // group table: block entry out of range
-constexpr int SMEM = MASK_OFF + kRowsPerWG * 8;
-static_assert(SMEM <= 160 * 1024, "LDS budget");
+
+// LDS tile geometry for head_dim D: 16 units per tensor, unit p holding keys p and p + 16
+// side by side, each unit filled by one direct load (D = 256: 1 KB, all 64 lanes; D = 128:
+// 512 bytes, lanes 0-31).  K units are padded by 16 bytes (the K fragment read, 16 lanes
+// x 16 bytes per LDS cycle, then touches 64 distinct banks: unit u starts at bank offset
+// 16u mod 256), V units by 64 bytes (the transposing read, 32 lanes x 8 bytes per cycle
+// over four units at bank offsets 0, 64, 128, 192, likewise).
+template <int D>
+struct Geo {
+    static constexpr int KS = D / 16;            // 16-wide k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;            // 32-wide d blocks of O^T
+    static constexpr int KEYB = 2 * D;           // bytes of one key row
+    static constexpr int LPK = KEYB / 16;        // lanes of a load per key row
+    static constexpr int UNIT = 2 * KEYB;
+    static constexpr int KU = UNIT + 16;
+    static constexpr int VU = UNIT + 64;
+    static constexpr int KTILE = UNITS * KU;
+    static constexpr int STAGE_BYTES = UNITS * (KU + VU);
+    static constexpr int GTAB_OFF = NST * STAGE_BYTES;
+    static constexpr int MASK_OFF = GTAB_OFF + kGrpMax * 4;
+    static constexpr int SMEM = MASK_OFF + kRowsPerWG * 8;
+    static_assert(D == 128 || D == 256, "head_dim 128 or 256");
+    static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert((KU % 256) == 16 && (VU % 256) == 64, "bank offsets");
+};
 
 // LDS offset of key r of a tile (K or V unit stride u).
-__device__ __forceinline__ int key_offset(int r, int u) { return (r & 15) * u + (r >> 4) * 512; }
+template <int D>
+__device__ __forceinline__ int key_offset(int r, int u) { return (r & 15) * u + (r >> 4) * Geo<D>::KEYB; }
+
+// A unit load: every lane of the wavefront with D = 256, lanes 0-31 with D = 128 (the
+// others would write past the unit).
+template <int D>
+__device__ __forceinline__ void unit_load(const unsigned char *src, uint32_t lds) {
+    if (Geo<D>::LPK == 32 || (threadIdx.x & 63) < 2 * Geo<D>::LPK) dma16(src, lds);
+}
+
+template <int D>
+__device__ __forceinline__ void load_unit_d(const TileLoad &t, int j) {
+    unit_load<D>(t.src + j * t.step, t.lds + j * t.ustride);
+}
 
 // Issues the whole tree tile (rows past the last node read the last node, masked); the
 // returned descriptor re-reads the last node (for repeat slots).
+template <int D>
 __device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int k0,
                                                uint32_t stage) {
+    using G = Geo<D>;
     const int w = uni(threadIdx.x >> 6);
     const int tensor = w >> 1;
     const int q = w & 1;
-    const int half = (int)((threadIdx.x & 63) >> 5);
+    const int lane = threadIdx.x & 63;
+    const int half = (lane / G::LPK) & 1;
     const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
-                                ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + (threadIdx.x & 31) * 16;
+                                ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + (lane % G::LPK) * 16;
     const int row = k0 + 8 * q + 16 * half;
     TileLoad t;
-    t.ustride = tensor ? VU : KU;
-    t.lds = stage + (tensor ? KTILE : 0) + q * NI * t.ustride;
+    t.ustride = tensor ? G::VU : G::KU;
+    t.lds = stage + (tensor ? G::KTILE : 0) + q * NI * t.ustride;
 #pragma unroll
     for (int j = 0; j < NI; ++j)
-        dma16(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
+        unit_load<D>(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
     t.src = base + (int64_t)(p.T - 1) * (D * 2);
     t.step = 0;
     t.spread = false;
@@ -126,11 +151,12 @@ __device__ __forceinline__ void vgpr_read_guard(f32x16 &x, f32x16 &y) {
 // S^T = K Q^T for one tile: A = K (32 keys x 16 d; lane: key l % 32, d 16 ks + 8 (l / 32)
 // .. +8), B = Q^T (lane: row l % 32, same d).  sacc[rb] element r: row rb*32 + l % 32,
 // key (r / 4) * 8 + (l / 32) * 4 + r % 4.  hook(ks) runs before each k-step's products.
-template <class Hook>
-__device__ __forceinline__ void tile_scores(const unsigned char *ks, const bf16x8 (&qf)[2][KS],
+template <int D, class Hook>
+__device__ __forceinline__ void tile_scores(const unsigned char *ks, const bf16x8 (&qf)[2][Geo<D>::KS],
                                             f32x16 (&sacc)[2], Hook &&hook) {
+    constexpr int KS = Geo<D>::KS;
     const int lane = threadIdx.x & 63;
-    const unsigned char *kb = ks + key_offset(lane & 31, KU) + (lane >> 5) * 16;
+    const unsigned char *kb = ks + key_offset<D>(lane & 31, Geo<D>::KU) + (lane >> 5) * 16;
     // K fragments are read KD k-steps ahead of their products; the reads sit before the
     // tile loads the hook issues (which the compiler does not move reads across)
     constexpr int KD = SV_W4_KD;
@@ -260,9 +286,10 @@ __device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowS
 // source lane 4r + q points at 4 consecutive d (32 db + 16 (G % 2) + 4q ..) of key
 // 16c + 4 (G / 2) + r; lane j of the group then receives d 32 db + 16 (G % 2) + j of
 // those 4 keys.
-template <class Hook>
-__device__ __forceinline__ void pv_tile(const unsigned char *vs, const bf16x8 (&pf)[2][2], f32x16 (&o)[2][DB],
-                                        Hook &&hook) {
+template <int D, class Hook>
+__device__ __forceinline__ void pv_tile(const unsigned char *vs, const bf16x8 (&pf)[2][2],
+                                        f32x16 (&o)[2][Geo<D>::DB], Hook &&hook) {
+    constexpr int DB = Geo<D>::DB, VU = Geo<D>::VU;
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4;
@@ -275,7 +302,7 @@ __device__ __forceinline__ void pv_tile(const unsigned char *vs, const bf16x8 (&
     constexpr int NSTEP = 2 * DB;
     bf16x8 v[VD + 1];
     auto read = [&](int i) {
-        const unsigned char *a = vb + (i / DB) * 512 + (i % DB) * 64;
+        const unsigned char *a = vb + (i / DB) * Geo<D>::KEYB + (i % DB) * 64;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)a);
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(a + 8 * VU));
         v[i % (VD + 1)] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -316,7 +343,9 @@ __device__ __forceinline__ void settle(const bf16x8 (&pf)[2][2], const RowState 
 // O *= alpha per row block, when any lane's reference max moved.  The accumulator
 // reads are in assembly the compiler does not look into, so the 18 wait states after
 // the last matrix instruction are given here, fenced against rescheduling.
-__device__ __forceinline__ void rescale(f32x16 (&o)[2][DB], const RowState &rs) {
+template <int D>
+__device__ __forceinline__ void rescale(f32x16 (&o)[2][Geo<D>::DB], const RowState &rs) {
+    constexpr int DB = Geo<D>::DB;
     if (__any(rs.raised[0] || rs.raised[1])) {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
@@ -333,9 +362,13 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[2][DB], const RowState &rs) 
     }
 }
 
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_w4_kernel(MfmaParams p) {
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    using G = Geo<D>;
+    constexpr int KS = G::KS, DB = G::DB, KU = G::KU, VU = G::VU, KTILE = G::KTILE;
+    constexpr int STAGE_BYTES = G::STAGE_BYTES, GTAB_OFF = G::GTAB_OFF, MASK_OFF = G::MASK_OFF;
 
     const int logical = xcd_logical_id();
     if (logical >= p.total) return;
@@ -471,14 +504,14 @@ void attn_w4_kernel(MfmaParams p) {
     const int wq = uni(w & 1);
     const int tensor = uni(w >> 1);
     const int ahead = tensor ? 2 : 3;
-    const int half = h;
+    const int half = (lane / G::LPK) & 1;  // the load's key row: p (0) or p + 16 (1)
     const int ustride = tensor ? VU : KU;
     const uint32_t lds_w = (tensor ? KTILE : 0) + wq * NI * ustride;
     const unsigned char *pool_w = reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
                                   (int64_t)kvh * p.hstride * 2;
     const int64_t step = p.rstride * 2;
     // per lane: its 16 bytes of the wavefront's first row inside a group
-    const int64_t lane_off = (int64_t)(8 * wq) * step + (lane & 31) * 16;
+    const int64_t lane_off = (int64_t)(8 * wq) * step + (lane % G::LPK) * 16;
     TileLoad tl;
     tl.ustride = ustride;
     auto prepare = [&](int k) {  // this wavefront's share of tile k (k >= -1)
@@ -498,7 +531,7 @@ void attn_w4_kernel(MfmaParams p) {
             tl.lds = stage + lds_w;
             tl.spread = true;
         } else if (k < nt) {
-            tl = issue_tree(p, b, kvh, (k - ntp) * kKeyTile, stage);
+            tl = issue_tree<D>(p, b, kvh, (k - ntp) * kKeyTile, stage);
         } else {
             tl.lds = stage + lds_w;
             tl.spread = true;
@@ -507,7 +540,7 @@ void attn_w4_kernel(MfmaParams p) {
     // the NI loads of the prepared tile go between the k-steps of the score product
     auto load_in_scores = [&](int k) {
         constexpr int every = KS / NI;
-        if (k % every == 0 && tl.spread) load_unit(tl, k / every);
+        if (k % every == 0 && tl.spread) load_unit_d<D>(tl, k / every);
     };
 
     // ---- iteration u: the score product of tile u (the hook issues loads between its
@@ -517,13 +550,17 @@ void attn_w4_kernel(MfmaParams p) {
     // u % 2, a template constant, so the loops below run two iterations per trip.
     auto iteration = [&](auto cur_c, int u, auto &&loads, bool masked, uint32_t kvalid, bool tree, int k0) {
         constexpr int cur = decltype(cur_c)::value;
-        tile_scores(smem + (u & (NST - 1)) * STAGE_BYTES, qf, sc, loads);
+        tile_scores<D>(smem + (u & (NST - 1)) * STAGE_BYTES, qf, sc, loads);
         if (masked) mask_scores(sc, kvalid, tree, k0, mrow);
         SoftTmp tmp;
-        pv_tile(smem + ((u - 1) & (NST - 1)) * STAGE_BYTES + KTILE, pf[cur ^ 1], o,
-                [&](int i) { softmax_piece(i, sc, rs, tmp, pf[cur], p.scale_log2); });
+        pv_tile<D>(smem + ((u - 1) & (NST - 1)) * STAGE_BYTES + KTILE, pf[cur ^ 1], o, [&](int i) {
+            // the softmax's 16 pieces over the product's 2 DB steps
+            constexpr int per = 16 / (2 * DB);
+#pragma unroll
+            for (int r = 0; r < per; ++r) softmax_piece(i * per + r, sc, rs, tmp, pf[cur], p.scale_log2);
+        });
         settle(pf[cur], rs);
-        rescale(o, rs);
+        rescale<D>(o, rs);
     };
     using Set0 = std::integral_constant<int, 0>;
     using Set1 = std::integral_constant<int, 1>;
@@ -532,7 +569,7 @@ void attn_w4_kernel(MfmaParams p) {
         prepare(k + ahead);
         if (tl.spread)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) load_unit(tl, j);
+            for (int j = 0; j < NI; ++j) load_unit_d<D>(tl, j);
     }
     int u = 0;
     if (staged && all_ok) {
@@ -556,7 +593,7 @@ void attn_w4_kernel(MfmaParams p) {
                 cur_c, uu,
                 [&](int k) {
                     constexpr int every = KS / NI;
-                    if (k % every == 0) load_unit(f, k / every);
+                    if (k % every == 0) load_unit_d<D>(f, k / every);
                 },
                 false, 0u, false, 0);
         };
@@ -632,10 +669,12 @@ void attn_w4_kernel(MfmaParams p) {
 
 }  // namespace
 
-hipError_t launch_attn_mfma256(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
+namespace {
+template <int D>
+hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     using namespace w4;
-    if (a.B == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)attn_w4_kernel,
+    constexpr int SMEM = Geo<D>::SMEM;
+    hipError_t e = hipFuncSetAttribute((const void *)attn_w4_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;
     MfmaParams p;
@@ -668,8 +707,14 @@ hipError_t launch_attn_mfma256(const AttnArgs &a, const AttnPlan &pl, hipStream_
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
     const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
-    hipLaunchKernelGGL(attn_w4_kernel, dim3(grid), dim3(64 * kW), SMEM, stream, p);
+    hipLaunchKernelGGL(attn_w4_kernel<D>, dim3(grid), dim3(64 * kW), SMEM, stream, p);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
+    if (a.B == 0) return hipSuccess;
+    return a.D == 128 ? launch_w4<128>(a, pl, stream) : launch_w4<256>(a, pl, stream);
 }
 
 }  // namespace sv

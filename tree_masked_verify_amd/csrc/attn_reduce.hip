@@ -21,7 +21,8 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
                                                           int max_P, int B, int Hq, int Hkv,
                                                           int T, int R, int S, int C,
                                                           float *__restrict__ out) {
-    constexpr int VPL = D / 64 / 4;  // float4 vectors per lane
+    constexpr int NV4 = D / 4;                 // float4 vectors per row
+    constexpr int VPL = (NV4 + 63) / 64;       // per lane (lanes past NV4 idle at D = 128)
     const int lane = threadIdx.x & 63;
     const int64_t x = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t nrows = (int64_t)B * T * Hq;
@@ -52,11 +53,13 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
         const float wgt = m == kNegInfR ? 0.0f : exp2f(m - M);
         L += wgt * l;
         const f32x4 *src = reinterpret_cast<const f32x4 *>(ws_o + base * D);
-        for (int v = 0; v < VPL; ++v) acc[v] += wgt * src[lane + 64 * v];
+        for (int v = 0; v < VPL; ++v)
+            if (lane + 64 * v < NV4) acc[v] += wgt * src[lane + 64 * v];
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     f32x4 *dst = reinterpret_cast<f32x4 *>(out + (((int64_t)b * T + i) * Hq + h) * D);
-    for (int v = 0; v < VPL; ++v) dst[lane + 64 * v] = acc[v] * inv;
+    for (int v = 0; v < VPL; ++v)
+        if (lane + 64 * v < NV4) dst[lane + 64 * v] = acc[v] * inv;
 }
 
 }  // namespace
@@ -66,7 +69,11 @@ hipError_t launch_attn_reduce(const AttnArgs &a, const AttnPlan &pl, hipStream_t
     if (nrows == 0) return hipSuccess;
     const int per = 4;
     dim3 grid((unsigned)((nrows + per - 1) / per));
-    if (a.D == 256)
+    if (a.D == 128)
+        hipLaunchKernelGGL(attn_reduce_kernel<128>, grid, dim3(64 * per), 0, stream, a.ws_o,
+                           a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
+                           pl.R, pl.S, pl.C, a.out);
+    else if (a.D == 256)
         hipLaunchKernelGGL(attn_reduce_kernel<256>, grid, dim3(64 * per), 0, stream, a.ws_o,
                            a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
                            pl.R, pl.S, pl.C, a.out);

@@ -216,6 +216,7 @@ hipError_t launch_attn_valu(const AttnArgs &a, const AttnPlan &pl, int dtype,
                             hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     const bool bf = dtype == SV_BF16;
+    if (a.D == 128) return bf ? launch_v<128, true>(a, pl, stream) : launch_v<128, false>(a, pl, stream);
     if (a.D == 256) return bf ? launch_v<256, true>(a, pl, stream) : launch_v<256, false>(a, pl, stream);
     return bf ? launch_v<512, true>(a, pl, stream) : launch_v<512, false>(a, pl, stream);
 }

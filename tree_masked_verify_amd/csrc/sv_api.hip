@@ -67,7 +67,7 @@ int check_attn_shape(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, i
     if (B < 0 || max_prefix_len < 0 || num_splits < 0) return SV_ERR_SHAPE;
     if (Hkv <= 0 || Hq <= 0) return SV_ERR_GQA;  // before the modulo
     if (Hq % Hkv != 0) return SV_ERR_GQA;
-    if (D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    if (D != 128 && D != 256 && D != 512) return SV_ERR_HEAD_DIM;
     if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
     int64_t tmp;
@@ -86,8 +86,9 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     p->R = R;
     p->mfma = dtype == SV_BF16 && R >= 16;
     if (p->mfma) {
-        // 32-row blocks, each shared by D/256 wavefronts; at most 8 wavefronts
-        const int dsplit = D / 256;
+        // 32-row blocks, each shared by D/256 wavefronts (one below 256); at most 8
+        // wavefronts
+        const int dsplit = D >= 256 ? D / 256 : 1;
         const int blocks = (R + 31) / 32;
         int nw = blocks * dsplit;
         nw = nw > kAttnMaxWaves ? kAttnMaxWaves : nw;
@@ -132,7 +133,7 @@ const char *sv_status_string(int status) {
         case SV_ERR_SHAPE: return "invalid or inconsistent size";
         case SV_ERR_DTYPE: return "unsupported or mismatched dtype";
         case SV_ERR_GQA: return "head counts must be positive with Hq a multiple of Hkv";
-        case SV_ERR_HEAD_DIM: return "head_dim must be 256 or 512";
+        case SV_ERR_HEAD_DIM: return "head_dim must be 128, 256 or 512";
         case SV_ERR_TREE_SIZE: return "tree size T must be in [1, 64]";
         case SV_ERR_CAPACITY: return "max_prefix_len + T exceeds the cache rows reserved per sequence";
         case SV_ERR_OVERFLOW: return "a size overflows";
@@ -295,7 +296,7 @@ int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted
     if (B < 0 || max_prefix_len < 0) return SV_ERR_SHAPE;
     if (Hkv <= 0) return SV_ERR_GQA;
     if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
-    if (D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    if (D != 128 && D != 256 && D != 512) return SV_ERR_HEAD_DIM;
     const int dtype = cache->dtype;
     const int es = esize_of(dtype);
     if (es == 0) return SV_ERR_DTYPE;

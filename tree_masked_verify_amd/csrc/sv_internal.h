@@ -71,8 +71,8 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
 hipError_t launch_tree_mask(const int32_t *parents, int B, int T, uint64_t *mask,
                             int32_t *depth, int32_t *tree_err, hipStream_t stream);
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
-// head_dim 256, one wavefront per SIMD (called by launch_attn_mfma)
-hipError_t launch_attn_mfma256(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
+// head_dim 128 and 256, one wavefront per SIMD (called by launch_attn_mfma)
+hipError_t launch_attn_w4(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs &a, const AttnPlan &p, int dtype,
                             hipStream_t stream);
 hipError_t launch_attn_reduce(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);

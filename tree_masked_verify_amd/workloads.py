@@ -81,6 +81,13 @@ WORKLOADS: dict[str, Workload] = {
         block_size=16, shuffled=True,
         notes="16 sequences, prefix 32768, 60-node random tree (8 levels, 1-4 children), "
               "paged cache with shuffled block table"),
+    # head_dim 128 (the head size of the Qwen target the pages retrofit the tree attention
+    # for), otherwise the 32K shape
+    "long32k_d128": Workload(
+        name="long32k_d128", B=16, Hq=32, Hkv=8, D=128, dtype="bf16", prefix=(32768, 32768),
+        T=60, tree="random", max_levels=8, max_children=4, V=151936, logit_std=2.0,
+        draft_p=0.6, block_size=16, shuffled=True,
+        notes="long32k with head_dim 128"),
 }
 
 
