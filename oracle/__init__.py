@@ -58,9 +58,13 @@ def _declare(lib):
     lib.oracle_kv_commit.argtypes = [
         _vp, _vp, _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64,
         _int, _i32p, _int, _i32p, _int, _int, _int, _int]
+    _f64p = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_topk_logprobs.argtypes = [_f32p, _i64, _i64, _int, _i32p, _f64p, _int]
+    lib.oracle_draft_tree.argtypes = [_f32p, _i32p, _int, _int, _i64, _int, _int, _i32p, _i32p,
+                                      _f64p]
     for f in ("oracle_build_tree_mask", "oracle_tree_verify_attention", "oracle_argmax",
               "oracle_accept_longest_path", "oracle_accept_sampled", "oracle_rope_tree",
-              "oracle_kv_commit"):
+              "oracle_kv_commit", "oracle_topk_logprobs", "oracle_draft_tree"):
         getattr(lib, f).restype = _int
     return lib
 
@@ -198,6 +202,39 @@ class Oracle:
             _p(nodes, _i32p), _p(toks, _i32p))
         assert rc == 0
         return L, nodes, toks
+
+    def topk_logprobs(self, logits, K, nthreads: int = 0):
+        """Top-K of each row's log-softmax: (tokens int32 [..., K], logp float64 [..., K]),
+        best first, ties to the smaller token."""
+        logits = np.ascontiguousarray(logits, dtype=np.float32)
+        V = logits.shape[-1]
+        flat = logits.reshape(-1, V)
+        tok = np.zeros((flat.shape[0], K), np.int32)
+        lp = np.zeros((flat.shape[0], K), np.float64)
+        rc = self.lib.oracle_topk_logprobs(_p(flat, _f32p), flat.shape[0], V, int(K),
+                                           _p(tok, _i32p),
+                                           _p(lp, ctypes.POINTER(ctypes.c_double)),
+                                           int(nthreads))
+        assert rc == 0, rc
+        return tok.reshape(*logits.shape[:-1], K), lp.reshape(*logits.shape[:-1], K)
+
+    def draft_tree(self, drafter_logits, root_tokens, K, max_levels):
+        """Best-first tree expansion over drafter rows [B, T, V] (row i: the drafter's
+        output for the node admitted i-th).  Returns (parents int32 [B, T], tokens int32
+        [B, T], cum float64 [B, T]); raises ValueError when the shape is refused."""
+        dl = np.ascontiguousarray(drafter_logits, dtype=np.float32)
+        root_tokens = np.ascontiguousarray(root_tokens, dtype=np.int32)
+        B, T, V = dl.shape
+        par = np.zeros((B, T), np.int32)
+        tok = np.zeros((B, T), np.int32)
+        cum = np.zeros((B, T), np.float64)
+        rc = self.lib.oracle_draft_tree(_p(dl, _f32p), _p(root_tokens, _i32p), B, T, V, int(K),
+                                        int(max_levels), _p(par, _i32p), _p(tok, _i32p),
+                                        _p(cum, ctypes.POINTER(ctypes.c_double)))
+        if rc == -1:
+            raise ValueError("draft_tree: shape refused")
+        assert rc == 0, rc
+        return par, tok, cum
 
     def rope_tree(self, q, k_tree, prefix_len, depth, theta, dtype):
         """Returns rotated copies of q [B, Hq, T, D] and k_tree [B, Hkv, T, D] (float32

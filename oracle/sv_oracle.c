@@ -16,15 +16,20 @@
  *  [ADR]  "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status
  *         table rows E1.1-E1.5 (tree attention parity ladder, output layout
  *         [q_seq_len, num_heads, head_dim]), E4a (build_tree_mask from the
- *         parent array), E4b.5b (NeoX RoPE at base position + tree depth, over
- *         the whole head), E4b.10a (smaller token wins ties), E5a (tree-walk
- *         accept), E6 v2 (mask selects ancestors + self); section 4 Phase E1
- *         (dynamic tree mask, apply_tree_attention) and Phase E5 (longest
- *         matching path from root; full accept picks the deepest).
+ *         parent array; global best-first expansion through one queue of
+ *         pending candidates keyed by the fp64 cumulative log-probability),
+ *         E4b.5b (NeoX RoPE at base position + tree depth, over the whole
+ *         head), E4b.10a (top-K of the log-softmax, smaller token wins ties),
+ *         E5a (tree-walk accept), E6 v2 (mask selects ancestors + self);
+ *         section 4 Phase E1 (dynamic tree mask, apply_tree_attention), Phase
+ *         E4 (expansion by cumulative log-probability up to a node budget) and
+ *         Phase E5 (longest matching path from root; full accept picks the
+ *         deepest).
  *  [HEADS] "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs):
  *         "Why bother" (greedy verify accepts the longest matching argmax
- *         prefix), "What's not implemented" item 1(c) (each tree node attends
- *         only to its ancestors).
+ *         prefix), "Mechanism comparison" (EAGLE-2's dynamic candidate tree),
+ *         "What's not implemented" item 1(c) (each tree node attends only to
+ *         its ancestors).
  *  [ANE]  "Speculative decoding verify batches to amortize ANE dispatch"
  *         (llms-explorer): Facts on the commit rule (argmax decides, longest
  *         matching prefix plus one bonus token, accept(k) commits only the
@@ -526,4 +531,150 @@ int oracle_kv_commit(const void *k_tree, const void *v_tree, const int32_t *acce
         if (new_prefix_len) new_prefix_len[b] = ok ? P + L : P;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-K of a log-softmax row ([ADR] row E4b.10a: log_softmax of the row,   */
+/* the K largest log-probabilities with the smaller token winning ties, and  */
+/* the choice made on the unclamped values).  With l(y) = logit_at(row, y)   */
+/* (NaN and -inf: -inf; +inf: the largest finite float), m = max_y l(y) and  */
+/* Z = sum over finite l(y) of exp(l(y) - m):                                 */
+/*   logp(y) = (l(y) - m) - log Z,  -inf where l(y) = -inf (and everywhere   */
+/*   when the row has no finite entry).                                       */
+/* logp increases strictly with l, so the K largest log-probabilities are     */
+/* found by comparing l itself, which no rounding can merge: K times, the     */
+/* token not chosen yet with the largest l, the smaller token on a tie.       */
+/* Outputs are in that order (best first).                                    */
+static void topk_row(const float *row, int64_t V, int K, int32_t *tok, double *logp,
+                     unsigned char *taken) {
+    double m = -INFINITY;
+    for (int64_t y = 0; y < V; ++y) {
+        const double l = logit_at(row, y);
+        if (l > m) m = l;
+    }
+    double Z = 0.0;
+    for (int64_t y = 0; y < V; ++y) {
+        const double l = logit_at(row, y);
+        if (l > -INFINITY) Z += exp(l - m);
+    }
+    memset(taken, 0, (size_t)V);
+    for (int k = 0; k < K; ++k) {
+        int64_t best = -1;
+        double bl = 0.0;
+        for (int64_t y = 0; y < V; ++y) {
+            if (taken[y]) continue;
+            const double l = logit_at(row, y);
+            if (best < 0 || l > bl) {
+                best = y;
+                bl = l;
+            }
+        }
+        taken[best] = 1;
+        tok[k] = (int32_t)best;
+        logp[k] = (bl == -INFINITY || Z == 0.0) ? -INFINITY : (bl - m) - log(Z);
+    }
+}
+
+int oracle_topk_logprobs(const float *logits, int64_t R, int64_t V, int K, int32_t *tok,
+                         double *logp, int nthreads) {
+    if (R < 0 || V < 1 || K < 1 || (int64_t)K > V) return -1;
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    int fail = 0;
+#pragma omp parallel
+    {
+        unsigned char *taken = (unsigned char *)malloc((size_t)V);
+        if (!taken) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic)
+        for (int64_t r = 0; r < R; ++r)
+            if (taken) topk_row(logits + r * V, V, K, tok + r * K, logp + r * K, taken);
+        free(taken);
+    }
+    return fail ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* EAGLE-2 global best-first tree expansion ([ADR] row E4a: one queue of     */
+/* pending candidates keyed by the fp64 cumulative log-probability, admitted */
+/* one node at a time, so that a grandchild of A can beat a sibling of A;     */
+/* section 4 Phase E4: expand by cumulative log-probability until the node   */
+/* budget is reached; [HEADS] "Mechanism comparison", EAGLE-2's dynamic      */
+/* tree).  Per sequence b:                                                    */
+/*   node 0 is the root: token root_token[b], cumulative log-prob 0, level 1. */
+/*   Admitting node i runs the drafter on it.  The synthetic drafter's output */
+/*   for the node admitted i-th is row i of drafter_logits[b]; its top-K     */
+/*   (topk_row) offers K candidate children (token, key cum(i) + logp), best */
+/*   first.  A node on level max_levels offers none, and neither does the    */
+/*   node that completes the tree (so row T-1 is never read).                 */
+/*   The pending candidate with the largest key is admitted next as node n:   */
+/*   parent, token, cum(n) = key, level = parent's level + 1.  Ties go to the */
+/*   candidate offered first (earlier parent, then better rank).             */
+/*   Expansion stops at T nodes.                                              */
+/* T must not exceed the nodes of a full K-ary tree of max_levels levels; the */
+/* queue then never runs dry.                                                 */
+int oracle_draft_tree(const float *drafter_logits, const int32_t *root_token, int B, int T,
+                      int64_t V, int K, int max_levels, int32_t *parents, int32_t *tokens,
+                      double *cum) {
+    if (B < 0 || T < 1 || V < 1 || K < 1 || (int64_t)K > V || max_levels < 1) return -1;
+    /* capacity: 1 + K + K^2 + ... over max_levels levels */
+    int64_t cap = 0, width = 1;
+    for (int lv = 0; lv < max_levels && cap < T; ++lv) {
+        cap += width;
+        width = width * K > T ? T : width * K;
+    }
+    if (cap < T) return -1;
+    const int64_t np = (int64_t)T * K;
+    double *ckey = (double *)malloc(sizeof(double) * (size_t)np);
+    int32_t *cpar = (int32_t *)malloc(sizeof(int32_t) * (size_t)np);
+    int32_t *ctok = (int32_t *)malloc(sizeof(int32_t) * (size_t)np);
+    unsigned char *used = (unsigned char *)malloc((size_t)np);
+    int32_t *level = (int32_t *)malloc(sizeof(int32_t) * (size_t)T);
+    int32_t *ktok = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    double *klp = (double *)malloc(sizeof(double) * (size_t)K);
+    unsigned char *taken = (unsigned char *)malloc((size_t)V);
+    int rc = 0;
+    if (!ckey || !cpar || !ctok || !used || !level || !ktok || !klp || !taken) rc = -2;
+    for (int b = 0; b < B && rc == 0; ++b) {
+        const float *rows = drafter_logits + (int64_t)b * T * V;
+        int32_t *par = parents + (int64_t)b * T;
+        int32_t *tk = tokens + (int64_t)b * T;
+        double *cm = cum + (int64_t)b * T;
+        int64_t npend = 0;
+        int n = 1;
+        par[0] = -1;
+        tk[0] = root_token[b];
+        cm[0] = 0.0;
+        level[0] = 1;
+        int last = 0; /* the node admitted last, to be offered next */
+        for (;;) {
+            if (n < T && level[last] < max_levels) { /* the drafter runs on node `last` */
+                topk_row(rows + (int64_t)last * V, V, K, ktok, klp, taken);
+                for (int r = 0; r < K; ++r) {
+                    ckey[npend] = cm[last] + klp[r];
+                    cpar[npend] = last;
+                    ctok[npend] = ktok[r];
+                    used[npend] = 0;
+                    ++npend;
+                }
+            }
+            if (n == T) break;
+            int64_t best = -1;
+            for (int64_t q = 0; q < npend; ++q)
+                if (!used[q] && (best < 0 || ckey[q] > ckey[best])) best = q;
+            if (best < 0) {
+                rc = -3;
+                break;
+            }
+            used[best] = 1;
+            par[n] = cpar[best];
+            tk[n] = ctok[best];
+            cm[n] = ckey[best];
+            level[n] = level[cpar[best]] + 1;
+            last = n++;
+        }
+    }
+    free(ckey); free(cpar); free(ctok); free(used); free(level); free(ktok); free(klp); free(taken);
+    return rc;
 }

@@ -818,6 +818,176 @@ def pin_commit_chain_equals_serial(orc):
     assert np.array_equal(c1.k, c2.k) and np.array_equal(c1.v, c2.v)
 
 
+
+# ======================================================= top-K and best-first expansion
+F32MAX = float(np.finfo(np.float32).max)
+
+
+def pin_topk_worked_examples(orc):
+    """Hand-derived rows: the pages' ordering case [0, -3e38, -2e38] (ADR-037 row
+    E4b.10a: choosing on clamped values would merge the two tails), ties to the smaller
+    token, NaN / +inf / -inf handling, a row without a finite entry, and K = V."""
+    tok, lp = orc.topk_logprobs(np.array([[0.0, -3e38, -2e38]], np.float32), 3)
+    assert tok[0].tolist() == [0, 2, 1]
+    assert lp[0, 0] == 0.0 and lp[0, 1] == float(np.float32(-2e38))
+    assert lp[0, 2] == float(np.float32(-3e38))
+    # three tokens at 7, two at 5: p(7) = 1 / (3 + 2 e^-2)
+    tok, lp = orc.topk_logprobs(np.array([[5, 7, 7, 5, 7]], np.float32), 4)
+    assert tok[0].tolist() == [1, 2, 4, 0]
+    top = -math.log(3.0 + 2.0 * math.exp(-2.0))
+    assert np.allclose(lp[0], [top, top, top, top - 2.0], rtol=0, atol=1e-15)
+    # NaN and -inf have probability 0; +inf counts as the largest finite float
+    tok, lp = orc.topk_logprobs(
+        np.array([[np.nan, 1.0, np.inf, -np.inf, np.inf]], np.float32), 5)
+    assert tok[0].tolist() == [2, 4, 1, 0, 3]
+    assert lp[0, 0] == lp[0, 1] and abs(lp[0, 0] + math.log(2.0)) < 1e-15
+    assert abs(lp[0, 2] - ((1.0 - F32MAX) - math.log(2.0))) <= 1e-15 * F32MAX
+    assert lp[0, 3] == -np.inf and lp[0, 4] == -np.inf
+    # no finite entry: every log-probability is -inf, the smallest tokens come first
+    tok, lp = orc.topk_logprobs(np.array([[np.nan, -np.inf, np.nan, -np.inf]], np.float32), 3)
+    assert tok[0].tolist() == [0, 1, 2] and np.all(lp == -np.inf)
+    # K = V: a permutation whose probabilities sum to 1
+    row = np.random.default_rng(3).normal(0, 3, size=(1, 40)).astype(np.float32)
+    tok, lp = orc.topk_logprobs(row, 40)
+    assert sorted(tok[0].tolist()) == list(range(40))
+    assert abs(math.fsum(np.exp(lp[0]).tolist()) - 1.0) < 1e-14
+    assert np.all(np.diff(lp[0]) <= 0)
+
+
+def pin_topk_vs_library(orc):
+    """Random rows (on a coarse grid, so that ties occur) against scipy's log_softmax in
+    fp64 and a stable descending argsort (ties keep the smaller index)."""
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(17)
+    for V, K in ((1000, 8), (37, 37), (5000, 1), (300, 64)):
+        x = (np.round(rng.normal(0, 2, size=(6, V)) * 4) / 4).astype(np.float32)
+        tok, lp = orc.topk_logprobs(x, K)
+        ref = log_softmax(x.astype(np.float64), axis=-1)
+        for r in range(x.shape[0]):
+            order = np.argsort(-x[r].astype(np.float64), kind="stable")[:K]
+            assert tok[r].tolist() == order.tolist()
+            assert np.allclose(lp[r], ref[r, order], rtol=0, atol=1e-12)
+
+
+def _draft_rows():
+    """Rows of the worked best-first example (V = 3, K = 2)."""
+    ninf = -np.inf
+    return np.array([[[0.0, -0.375, ninf],    # node 0 (root)
+                      [-2.0, ninf, 0.0],      # node 1
+                      [0.0, 0.0, ninf],       # node 2
+                      [-1.0, 0.0, 1.0],       # node 3
+                      [-9.0, -9.0, -9.0],     # node 4
+                      [np.nan] * 3]],         # node 5 completes the tree: never read
+                    np.float32)
+
+
+def pin_draft_tree_worked_example(orc):
+    """Global best-first expansion worked by hand (ADR-037 row E4a: a grandchild of A
+    is admitted before a sibling of A when its cumulative log-probability is higher).
+
+    Root offers token 0 (c1 = -log(1 + e^-0.375)) and token 1 (c3 = -0.375 + c1).  Node 1
+    (token 0) offers token 2 at c1 - log(1 + e^-2), which beats the root's token 1, so
+    node 2 is that grandchild.  Node 2 offers tokens 0 and 1 at c2 - log 2 (a tie).
+    Node 3 is the root's token 1; it offers token 2 at c3 + 1 - log(e^-1 + 1 + e), which
+    beats the tie, so node 4 is that; node 5 is the first-offered side of the tie."""
+    rows = _draft_rows()
+    par, tok, cum = orc.draft_tree(rows, np.array([77], np.int32), K=2, max_levels=4)
+    assert par[0].tolist() == [-1, 0, 1, 0, 3, 2]
+    assert tok[0].tolist() == [77, 0, 2, 1, 2, 0]
+    c1 = -math.log1p(math.exp(-0.375))
+    c2 = c1 - math.log1p(math.exp(-2.0))
+    c3 = -0.375 + c1
+    c4 = c3 + 1.0 - math.log(math.exp(-1.0) + 1.0 + math.exp(1.0))
+    c5 = c2 - math.log(2.0)
+    assert np.allclose(cum[0], [0.0, c1, c2, c3, c4, c5], rtol=0, atol=1e-14)
+    # a level limit of 2: only the root offers candidates, three nodes at most
+    par, tok, _ = orc.draft_tree(rows[:, :3], np.array([5], np.int32), K=2, max_levels=2)
+    assert par[0].tolist() == [-1, 0, 0] and tok[0].tolist() == [5, 0, 1]
+    for T, K, lv in ((4, 2, 2), (2, 4, 3), (2, 1, 1)):
+        try:
+            orc.draft_tree(np.zeros((1, T, 3), np.float32), np.zeros(1, np.int32), K=K,
+                           max_levels=lv)
+        except ValueError:
+            continue
+        raise AssertionError(f"T={T} K={K} max_levels={lv} must be refused")
+
+
+def pin_draft_tree_bruteforce(orc):
+    """With every drafter row the same the candidate tree is fixed, and best-first
+    admits exactly its T - 1 best non-root nodes (brute force over all rank sequences
+    with scipy's log-softmax); admission order never raises the cumulative log-prob."""
+    from itertools import product
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(23)
+    V, K, levels = 6, 3, 4
+    for trial in range(4):
+        row = rng.normal(0, 1.5, size=V).astype(np.float32)
+        lp = log_softmax(row.astype(np.float64))
+        order = np.argsort(-row.astype(np.float64), kind="stable")[:K]
+        paths = []
+        for d in range(1, levels):
+            for seq in product(range(K), repeat=d):
+                paths.append((sum(lp[order[r]] for r in seq),
+                              tuple(int(order[r]) for r in seq)))
+        paths.sort(key=lambda t: -t[0])
+        # a budget whose cut is not inside a group of (near-)equal sums
+        cuts = [n for n in range(4, len(paths)) if paths[n - 1][0] - paths[n][0] > 1e-9]
+        n = cuts[trial]
+        T = n + 1
+        rows = np.tile(row[None, None], (1, T, 1))
+        par, tok, cum = orc.draft_tree(rows, np.array([9], np.int32), K=K, max_levels=levels)
+        got = set()
+        for i in range(1, T):
+            seq, j = [], i
+            while j > 0:
+                seq.append(int(tok[0, j]))
+                j = par[0, j]
+            got.add(tuple(reversed(seq)))
+        assert got == {p for _, p in paths[:n]}
+        assert np.all(np.diff(cum[0, 1:]) <= 0)
+        sums = {p: c for c, p in paths}
+        for i in range(1, T):
+            seq, j = [], i
+            while j > 0:
+                seq.append(int(tok[0, j]))
+                j = par[0, j]
+            assert abs(cum[0, i] - sums[tuple(reversed(seq))]) < 1e-12
+
+
+def pin_draft_tree_structure(orc):
+    """K = 1 gives a chain of each row's argmax (numpy); a two-level limit gives a star
+    of the root row's top-K (stable argsort); T = 1 reads no row; every child comes
+    from the top-K of the row of its parent's admission index, and keys never rise."""
+    rng = np.random.default_rng(31)
+    rows = rng.normal(0, 2, size=(2, 12, 50)).astype(np.float32)
+    roots = np.array([4, 8], np.int32)
+    par, tok, _ = orc.draft_tree(rows, roots, K=1, max_levels=12)
+    for b in range(2):
+        assert par[b].tolist() == [-1] + list(range(11))
+        assert tok[b, 1:].tolist() == [int(np.argmax(rows[b, i])) for i in range(11)]
+    par, tok, _ = orc.draft_tree(rows[:, :5], roots, K=4, max_levels=2)
+    for b in range(2):
+        assert par[b].tolist() == [-1, 0, 0, 0, 0]
+        assert tok[b, 1:].tolist() == np.argsort(-rows[b, 0], kind="stable")[:4].tolist()
+    par, tok, cum = orc.draft_tree(np.full((2, 1, 50), np.nan, np.float32), roots, K=3,
+                                   max_levels=3)
+    assert par.tolist() == [[-1], [-1]] and tok[:, 0].tolist() == [4, 8] and np.all(cum == 0)
+    par, tok, cum = orc.draft_tree(rows, roots, K=5, max_levels=4)
+    for b in range(2):
+        assert par[b, 0] == -1 and tok[b, 0] == roots[b] and cum[b, 0] == 0.0
+        assert np.all(np.diff(cum[b, 1:]) <= 0)
+        depth = [0] * 12
+        for c in range(1, 12):
+            p = int(par[b, c])
+            assert 0 <= p < c
+            depth[c] = depth[p] + 1
+            assert depth[c] <= 3
+            top = np.argsort(-rows[b, p], kind="stable")[:5].tolist()
+            assert int(tok[b, c]) in top
+        # no token offered twice by one parent
+        pairs = [(int(par[b, c]), int(tok[b, c])) for c in range(1, 12)]
+        assert len(set(pairs)) == len(pairs)
+
 ALL_PINS = [
     pin_mask_worked_example, pin_mask_closed_forms, pin_mask_bruteforce, pin_mask_invalid,
     pin_attn_decode_T1, pin_attn_chain_causal, pin_attn_tree_vs_sdpa, pin_attn_prefix_zero,
@@ -830,6 +1000,8 @@ ALL_PINS = [
     pin_sampled_low_temperature_is_greedy, pin_sampled_invariants,
     pin_rope_worked_examples, pin_rope_relative_position, pin_rope_pairs_and_tree,
     pin_rope_bf16_rounding,
+    pin_topk_worked_examples, pin_topk_vs_library, pin_draft_tree_worked_example,
+    pin_draft_tree_bruteforce, pin_draft_tree_structure,
     pin_commit_invariants, pin_commit_single_root, pin_commit_refusals,
     pin_commit_chain_equals_serial,
 ]

@@ -76,6 +76,21 @@ MUTANTS = [
     ("commit_length_short", "new_prefix_len[b] = ok ? P + L : P;",
      "new_prefix_len[b] = ok ? P + L - 1 : P;", 0),
     ("commit_ignores_tree_err", "int ok = !(tree_err && tree_err[b] != 0);", "int ok = 1;", 0),
+    ("topk_ties_to_larger_token", "if (best < 0 || l > bl) {", "if (best < 0 || l >= bl) {", 0),
+    ("topk_not_normalised", "(bl - m) - log(Z);", "(bl - m);", 0),
+    ("topk_sum_not_shifted", "if (l > -INFINITY) Z += exp(l - m);",
+     "if (l > -INFINITY) Z += exp(l);", 0),
+    ("draft_key_not_cumulative", "ckey[npend] = cm[last] + klp[r];", "ckey[npend] = klp[r];", 0),
+    ("draft_ties_to_later_offer", "ckey[q] > ckey[best]", "ckey[q] >= ckey[best]", 0),
+    ("draft_row_of_parent", "topk_row(rows + (int64_t)last * V,",
+     "topk_row(rows + (int64_t)(last ? par[last] : 0) * V,", 0),
+    ("draft_level_off_by_one", "level[last] < max_levels", "level[last] <= max_levels", 0),
+    ("draft_only_best_child", "for (int r = 0; r < K; ++r) {\n                    ckey",
+     "for (int r = 0; r < 1; ++r) {\n                    ckey", 0),
+    ("draft_token_of_parent", "tk[n] = ctok[best];", "tk[n] = tk[cpar[best]];", 0),
+    ("draft_cum_in_f32", "cm[n] = ckey[best];", "cm[n] = (float)ckey[best];", 0),
+    ("draft_prefers_last_parent", "if (!used[q] && (best < 0 || ckey[q] > ckey[best])) best = q;",
+     "if (!used[q] && (best < 0 || ckey[q] > ckey[best] || (cpar[q] == last && cpar[best] != last))) best = q;", 0),
 ]
 
 
