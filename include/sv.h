@@ -15,18 +15,23 @@
  *                                rotary embedding at base position + tree depth
  *   4. sv_kv_commit              copy only the accepted rows' K/V into the cache
  *
+ * Before the step, sv_draft_tree builds the draft tree itself from the drafter's
+ * logits (top-K of each row's log-softmax, then EAGLE-2 global best-first
+ * expansion); sv_topk_logprobs is its top-K on its own.
+ *
  * Sources (web pages, by title and section):
  *   "ADR-037 -- EAGLE-3 with dynamic tree port" (hf2q docs): Phase status rows
  *     E1.1-E1.5 (tree attention; output layout [q_seq_len, num_heads, head_dim];
  *     head_dim 256/512), E4b.6 (the head_dim-128 retrofit of the tree attention),
  *     E1 review gate (dtype and byte-length validation), E4a
- *     (build_tree_mask from the parent array, checked overflow), E4b.5b
- *     (tree-position RoPE), E5a (tree-walk
- *     accept), E6 (zero-head guard before the GQA modulo), E6 v2 (ancestors +
- *     self); section 4, Phases E1 and E5.
+ *     (build_tree_mask from the parent array, checked overflow; best-first tree
+ *     expansion), E4b.5b (tree-position RoPE), E4b.10a (top-K extraction), E5a
+ *     (tree-walk accept), E6 (zero-head guard before the GQA modulo), E6 v2
+ *     (ancestors + self); section 4, Phases E1, E4 and E5.
  *   "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs): "Why
- *     bother" (greedy longest-matching-prefix verification) and "What's not
- *     implemented" item 1 (ancestor-only tree attention, per-path argmax).
+ *     bother" (greedy longest-matching-prefix verification), "Mechanism
+ *     comparison" (EAGLE-2's dynamic tree) and "What's not implemented" item 1
+ *     (ancestor-only tree attention, per-path argmax).
  *   "Speculative decoding verify batches to amortize ANE dispatch"
  *     (llms-explorer): Facts on the commit rule, on delayed KV write-through and on
  *     Forge's sampled verification.
@@ -270,6 +275,64 @@ int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *
 int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t *depth,
                  int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t D, int32_t dtype,
                  double theta, hipStream_t stream);
+
+/*
+ * Top-K of the log-softmax of each row.
+ * Defined by: ADR-037 Phase status row E4b.10a (log_softmax of the row, the K
+ * largest log-probabilities, the smaller token winning ties, the choice made on
+ * unclamped values).
+ *
+ *   logits     float32 [R][V] (4-byte aligned)
+ *   top_tokens int32 [R][K], top_logp float64 [R][K] (8-byte aligned): best first
+ * With l(y) the logit (NaN and -inf read as -inf, +inf as FLT_MAX), m = max l and
+ * Z = sum over finite l of exp(l - m): logp(y) = (l(y) - m) - log Z, evaluated in
+ * fp64 (-inf where l is -inf, and for every token of a row without a finite
+ * entry).  The K tokens are chosen by comparing l itself (logp increases strictly
+ * with l), ties to the smaller token, so the tokens are exact; the log-probs
+ * agree with an exact evaluation to about 1e-15 relative.
+ * 1 <= K <= min(V, 64).  R = 0 is a no-op.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (R < 0, V < 1, K out of range),
+ * SV_ERR_OVERFLOW (V or R above INT_MAX), SV_ERR_ALIGN, SV_ERR_HIP.
+ */
+int sv_topk_logprobs(const float *logits, int64_t R, int64_t V, int32_t K, int32_t *top_tokens,
+                     double *top_logp, hipStream_t stream);
+
+/* Bytes of workspace sv_draft_tree needs (0 when the shape is invalid). */
+size_t sv_draft_tree_workspace_size(int32_t B, int32_t T, int32_t K);
+
+/*
+ * Draft tree by EAGLE-2 global best-first expansion, from the drafter's logits.
+ * Defined by: ADR-037 Phase status row E4a (one queue of pending candidates keyed
+ * by the fp64 cumulative log-probability, admitted one node at a time, so that a
+ * grandchild of A can come before a sibling of A), row E4b.10a (the top-K of each
+ * drafter row), section 4 Phase E4 (expand by cumulative log-probability until the
+ * node budget is reached); "Speculative-decoding heads: Medusa + EAGLE-2",
+ * "Mechanism comparison" (EAGLE-2's dynamic candidate tree).
+ *
+ *   drafter_logits float32 [B][T][V]: row i of sequence b is the drafter's output
+ *              for the node admitted i-th (row T-1 is never read)
+ *   root_token int32 [B]: token of node 0 (the last committed token)
+ *   K          candidates offered per expanded node, 1 <= K <= min(V, 64)
+ *   max_levels levels of the tree, the root being level 1 (>= 1)
+ *   parents    int32 [B][T]: parent of each node (node 0: -1; parent[i] < i)
+ *   tokens     int32 [B][T]: draft token of each node (node 0: root_token)
+ *   cum_logp   float64 [B][T]: cumulative log-probability of each node (root 0)
+ * Node 0 is the root.  Admitting node i offers the K tokens of sv_topk_logprobs on
+ * row i as candidate children with key cum_logp[i] + logp, best first, unless node
+ * i is on level max_levels or is node T-1.  The pending candidate with the largest
+ * key is admitted next, ties to the one offered first (earlier parent, then better
+ * rank).  The output feeds sv_build_tree_mask (parents) and the acceptance calls
+ * (tokens as draft).  Keys are compared in fp64; two keys within ~1e-15 relative of
+ * each other may be ordered differently from an exact evaluation.
+ * T must not exceed the nodes of a full K-ary tree of max_levels levels.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, V < 1, K or max_levels out of range, T
+ * above that capacity), SV_ERR_TREE_SIZE (T outside [1, 64]), SV_ERR_OVERFLOW,
+ * SV_ERR_WORKSPACE (when T > 1), SV_ERR_ALIGN, SV_ERR_HIP.
+ */
+int sv_draft_tree(const float *drafter_logits, const int32_t *root_token, int32_t B, int32_t T,
+                  int64_t V, int32_t K, int32_t max_levels, int32_t *parents, int32_t *tokens,
+                  double *cum_logp, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
 
 /*
  * Delayed KV write-through: commit only the accepted rows.

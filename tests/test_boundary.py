@@ -173,3 +173,35 @@ def test_commit_validation(lib):
     assert call(kt=FAKE + 2) == -11
     assert call(kt=None) == -1
     assert call(B=0) == 0
+
+
+def test_topk_validation(lib):
+    f = lib.sv_topk_logprobs
+    args = lambda R=4, V=1000, K=8, lg=FAKE, tk=FAKE, lp=FAKE: (lg, R, V, K, tk, lp, None)
+    assert f(*args(K=0)) == -2 and f(*args(K=65)) == -2 and f(*args(V=5, K=6)) == -2
+    assert f(*args(R=-1)) == -2 and f(*args(V=0)) == -2
+    assert f(*args(V=1 << 31)) == -8 and f(*args(R=1 << 31)) == -8
+    assert f(*args(R=0, lg=None, tk=None, lp=None)) == 0          # nothing to do
+    assert f(*args(lg=None)) == -1 and f(*args(lp=None)) == -1
+    assert f(*args(lg=FAKE + 2)) == -11 and f(*args(lp=FAKE + 4)) == -11
+    assert f(*args(tk=FAKE + 2)) == -11
+
+
+def test_draft_tree_validation(lib):
+    f = lib.sv_draft_tree
+    args = lambda B=2, T=8, V=1000, K=4, lv=4, dl=FAKE, cum=FAKE, ws=FAKE, wsb=1 << 20: (
+        dl, FAKE, B, T, V, K, lv, FAKE, FAKE, cum, ws, wsb, None)
+    assert f(*args(T=0)) == -6 and f(*args(T=65)) == -6
+    assert f(*args(K=0)) == -2 and f(*args(K=65)) == -2 and f(*args(V=3)) == -2
+    assert f(*args(lv=0)) == -2 and f(*args(B=-1)) == -2
+    # a full binary tree of 3 levels has 7 nodes; a chain of K = 1 has max_levels nodes
+    assert f(*args(K=2, lv=3)) == -2 and f(*args(K=1, lv=7)) == -2
+    assert f(*args(V=1 << 31)) == -8
+    assert f(*args(B=0)) == 0
+    assert f(*args(dl=None)) == -1
+    assert f(*args(cum=FAKE + 4)) == -11 and f(*args(dl=FAKE + 2)) == -11
+    assert f(*args(wsb=16)) == -9 and f(*args(ws=None)) == -9
+    assert f(*args(ws=FAKE + 8)) == -11
+    ws = sv.sv_draft_tree_workspace_size
+    assert ws(2, 8, 4) == 512 + 256     # [2][7][4] fp64 log-probs, then int32 tokens
+    assert ws(2, 1, 4) == 0 and ws(-1, 8, 4) == 0 and ws(2, 65, 4) == 0 and ws(2, 8, 65) == 0

@@ -24,7 +24,9 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
 ENTRY_POINTS = ("sv_build_tree_mask", "sv_tree_verify_attention_workspace_size",
                 "sv_tree_verify_attention", "sv_accept_longest_path_workspace_size",
                 "sv_accept_longest_path", "sv_accept_sampled_workspace_size",
-                "sv_accept_sampled", "sv_rope_tree", "sv_kv_commit", "sv_status_string")
+                "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs",
+                "sv_draft_tree_workspace_size", "sv_draft_tree", "sv_kv_commit",
+                "sv_status_string")
 
 
 class SvError(RuntimeError):
@@ -70,12 +72,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, sz, vp]
     lib.sv_rope_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_double,
                                  vp]
+    lib.sv_topk_logprobs.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.sv_draft_tree_workspace_size.argtypes = [i32, i32, i32]
+    lib.sv_draft_tree_workspace_size.restype = sz
+    lib.sv_draft_tree.argtypes = [vp, vp, i32, i32, i64, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.sv_kv_commit.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp,
                                  i32, i32, i32, i32, vp]
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
     for f in ("sv_build_tree_mask", "sv_tree_verify_attention", "sv_accept_longest_path",
-              "sv_accept_sampled", "sv_rope_tree", "sv_kv_commit"):
+              "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs", "sv_draft_tree",
+              "sv_kv_commit"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -183,6 +190,30 @@ def sv_rope_tree(q, k_tree, prefix_len, depth, theta, stream=None) -> None:
     rc = load_library().sv_rope_tree(_ptr(q), _ptr(k_tree), _ptr(prefix_len), _ptr(depth), B, Hq,
                                      Hkv, T, D, dtype_code(q), float(theta), _stream(stream))
     _check("sv_rope_tree", rc)
+
+
+def sv_topk_logprobs(logits, K, top_tokens, top_logp, stream=None) -> None:
+    """logits float32 [..., V] -> top_tokens int32 / top_logp float64 [..., K]."""
+    V = logits.shape[-1]
+    R = logits.numel() // V if V else 0
+    rc = load_library().sv_topk_logprobs(_ptr(logits), R, V, int(K), _ptr(top_tokens),
+                                         _ptr(top_logp), _stream(stream))
+    _check("sv_topk_logprobs", rc)
+
+
+def sv_draft_tree_workspace_size(B, T, K) -> int:
+    return int(load_library().sv_draft_tree_workspace_size(B, T, K))
+
+
+def sv_draft_tree(drafter_logits, root_token, K, max_levels, parents, tokens, cum_logp,
+                  workspace, stream=None) -> None:
+    B, T, V = drafter_logits.shape
+    rc = load_library().sv_draft_tree(
+        _ptr(drafter_logits), _ptr(root_token), B, T, V, int(K), int(max_levels), _ptr(parents),
+        _ptr(tokens), _ptr(cum_logp), _ptr(workspace),
+        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check("sv_draft_tree", rc)
 
 
 def sv_kv_commit(k_tree, v_tree, accepted_len, accepted_nodes, tree_err, cache: sv_kv_cache,

@@ -287,6 +287,71 @@ int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t
                                        theta, stream));
 }
 
+int sv_topk_logprobs(const float *logits, int64_t R, int64_t V, int32_t K, int32_t *top_tokens,
+                     double *top_logp, hipStream_t stream) {
+    if (R < 0 || V < 1 || K < 1 || K > 64 || (int64_t)K > V) return SV_ERR_SHAPE;
+    int64_t tmp;
+    if (V > INT_MAX || R > INT_MAX || !prod_ok({R, V, 4}, &tmp) || !prod_ok({R, K, 8}, &tmp))
+        return SV_ERR_OVERFLOW;
+    if (R == 0) return SV_OK;
+    if (!logits || !top_tokens || !top_logp) return SV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(logits) & 3u) || (reinterpret_cast<uintptr_t>(top_tokens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(top_logp) & 7u))
+        return SV_ERR_ALIGN;
+    return hip_status(launch_topk_rows(logits, R, V, K, 1, 1, top_tokens, top_logp, stream));
+}
+
+// Nodes of a full K-ary tree with `levels` levels, capped at 65.
+static int64_t tree_capacity(int32_t K, int32_t levels) {
+    int64_t cap = 0, width = 1;
+    for (int32_t lv = 0; lv < levels && cap <= 64; ++lv) {
+        cap += width;
+        width = width * K > 65 ? 65 : width * K;
+    }
+    return cap;
+}
+
+static bool draft_shape_ok(int32_t B, int32_t T, int64_t V, int32_t K, int32_t max_levels) {
+    return B >= 0 && V >= 1 && K >= 1 && K <= 64 && (int64_t)K <= V &&
+           max_levels >= 1 && T >= 1 && T <= 64 && tree_capacity(K, max_levels) >= T;
+}
+
+size_t sv_draft_tree_workspace_size(int32_t B, int32_t T, int32_t K) {
+    if (B < 0 || T < 1 || T > 64 || K < 1 || K > 64) return 0;
+    const size_t n = (size_t)B * (size_t)(T - 1) * (size_t)K;
+    return round256(n * sizeof(double)) + round256(n * sizeof(int32_t));
+}
+
+int sv_draft_tree(const float *drafter_logits, const int32_t *root_token, int32_t B, int32_t T,
+                  int64_t V, int32_t K, int32_t max_levels, int32_t *parents, int32_t *tokens,
+                  double *cum_logp, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (!draft_shape_ok(B, T, V, K, max_levels)) return SV_ERR_SHAPE;
+    int64_t tmp;
+    if (V > INT_MAX || !prod_ok({(int64_t)B, T, V, 4}, &tmp) || (int64_t)B * (T - 1) > INT_MAX)
+        return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!drafter_logits || !root_token || !parents || !tokens || !cum_logp) return SV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(drafter_logits) & 3u) ||
+        (reinterpret_cast<uintptr_t>(cum_logp) & 7u))
+        return SV_ERR_ALIGN;
+    const size_t need = sv_draft_tree_workspace_size(B, T, K);
+    if (T > 1 && (!workspace || workspace_bytes < need)) return SV_ERR_WORKSPACE;
+    if (T > 1 && !aligned16(workspace)) return SV_ERR_ALIGN;
+    const size_t n = (size_t)B * (size_t)(T - 1) * (size_t)K;
+    double *lp = static_cast<double *>(workspace);
+    int32_t *tk = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                              round256(n * sizeof(double)));
+    if (T > 1) {
+        const int rc = hip_status(launch_topk_rows(drafter_logits, (int64_t)B * (T - 1), V, K,
+                                                   T - 1, T, tk, lp, stream));
+        if (rc != SV_OK) return rc;
+    }
+    return hip_status(launch_best_first(tk, lp, root_token, B, T, K, max_levels, parents, tokens,
+                                        cum_logp, stream));
+}
+
 int sv_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                  const int32_t *accepted_nodes, const int32_t *tree_err,
                  const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,

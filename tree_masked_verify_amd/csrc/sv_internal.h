@@ -104,6 +104,16 @@ hipError_t launch_rope_tree(void *q, void *k_tree, const int32_t *prefix_len,
                             const int32_t *depth, int B, int Hq, int Hkv, int T, int D, int dtype,
                             double theta, hipStream_t stream);
 
+// Top-K of the log-softmax of rows: row r of the call reads logits row
+// (r / rows_per_group) * group_stride + r % rows_per_group and writes [r][K].
+hipError_t launch_topk_rows(const float *logits, int64_t rows, int64_t V, int K,
+                            int rows_per_group, int64_t group_stride, int32_t *top_tok,
+                            double *top_logp, hipStream_t stream);
+// Best-first expansion from the top-K lists [B][T - 1][K] of each sequence's rows.
+hipError_t launch_best_first(const int32_t *top_tok, const double *top_logp,
+                             const int32_t *root_token, int B, int T, int K, int max_levels,
+                             int32_t *parents, int32_t *tokens, double *cum, hipStream_t stream);
+
 hipError_t launch_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                             const int32_t *accepted_nodes, const int32_t *tree_err,
                             void *k_cache, void *v_cache, const CacheView &c,

@@ -1,0 +1,376 @@
+// topk.hip -- top-K of the log-softmax of logits rows, and the global best-first
+// expansion of a draft tree from the drafter's rows.
+//
+// Rules (ADR-037 Phase status rows E4b.10a and E4a; section 4 Phase E4):
+//   l(y) = the logit, with NaN and -inf read as -inf and +inf as the largest finite float;
+//   logp(y) = (l(y) - m) - log Z in fp64, m = max l, Z = sum over finite l of exp(l - m)
+//   (every logp is -inf when the row has no finite entry).  The K largest log-probabilities
+//   are chosen by comparing l itself (logp increases strictly with l, so no rounding can
+//   merge two distinct values), ties to the smaller token, best first.
+//   Best-first: node 0 is the root (cumulative log-prob 0, level 1).  The drafter's output
+//   for the node admitted i-th is row i; admitting node i offers its K best tokens as
+//   candidate children with key cum(i) + logp, unless node i is on the last allowed level
+//   or completes the tree.  The pending candidate with the largest key (fp64) is admitted
+//   next, ties to the one offered first; until T nodes.
+//
+// topk_rows_kernel: one workgroup of four wavefronts per row.  Every lane streams its
+// 16-byte pieces once and keeps an online max and an fp64 sum of exponentials
+// (exp_nonpos below).  Each wavefront keeps a candidate buffer in LDS: a piece's element
+// enters it when it beats the wavefront's K-th best so far (while fewer than K entries
+// exist, every element enters).  When the buffer could overflow, the wavefront keeps its K
+// best (K rounds of a 64-lane max over (value, -index) keys) and raises its threshold.
+// At the end the four wavefronts' lists are merged the same way.
+// best_first_kernel: one wavefront per sequence.  Lane j stands for admitted node j and
+// holds its best child not admitted yet: a node's children come best first, so no other
+// child of it can be next.  Each admission is a 64-lane max over those keys, ties to the
+// lower lane (the earlier parent); the winner moves on to its next child and the lane of
+// the new node starts on its own first child.
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kTkWaves = 4;                 // wavefronts per row
+constexpr int kTkThreads = 64 * kTkWaves;
+constexpr int kCap = 512;                   // candidate entries per wavefront
+constexpr int kPiece = 256;                 // the most one piece (one 16-byte load per lane) adds
+constexpr float kFltMax = 3.40282347e38f;
+
+// exp(d) for d <= 0 in fp64; d = -inf gives 0.  Table-driven method (P. T. P. Tang, "Table-
+// driven implementation of the exponential function in IEEE floating-point arithmetic", ACM
+// TOMS 15(2), 1989): d = (32 k + j) ln2/32 + r with |r| <= ln2/64, so
+// e^d = 2^k * 2^(j/32) * e^r; e^r - 1 is its Taylor polynomial of degree 6 (remainder below
+// 2^-57 relative) and 2^(j/32) comes from a 32-entry table.
+__device__ __forceinline__ double exp_nonpos(double d, const double *tab) {
+    if (!(d > -745.5)) return 0.0;                    // below the smallest subnormal, or -inf
+    constexpr double kInvL = 0x1.71547652b82fep+5;    // 32 / ln 2
+    constexpr double kL1 = 0x1.62e42fefa39efp-6;      // ln 2 / 32, leading part
+    constexpr double kL2 = 0x1.abc9e3b39803fp-61;     // ln 2 / 32 - kL1
+    const double n = rint(d * kInvL);
+    double r = fma(-n, kL1, d);
+    r = fma(-n, kL2, r);
+    const int ni = (int)n;
+    double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+    q = fma(q, r, 1.0 / 24.0);
+    q = fma(q, r, 1.0 / 6.0);
+    q = fma(q, r, 0.5);
+    const double p = fma(r * r, q, r);                // e^r - 1
+    const double t = tab[ni & 31];
+    return ldexp(fma(t, p, t), ni >> 5);               // ni >> 5 = floor(ni / 32)
+}
+
+// A logit as the rule reads it: NaN and -inf give -inf, +inf the largest finite float, and
+// -0 becomes +0 so that the two zeros compare equal as keys.
+__device__ __forceinline__ float clean(float x) {
+    if (!(x > -__builtin_huge_valf())) return -__builtin_huge_valf();
+    x = x < kFltMax ? x : kFltMax;
+    return x + 0.0f;
+}
+
+// Order-preserving 64-bit key of (value, index): larger value first, then smaller index.
+// 0 marks an empty slot (every real key is larger: ord(-inf) = 0x007fffff).
+__device__ __forceinline__ uint64_t cand_key(float v, int32_t idx) {
+    if (idx < 0) return 0;
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t k) {
+    return (int32_t)(0xffffffffu - (uint32_t)k);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(x, off, 64);
+        x = o > x ? o : x;
+    }
+    return x;
+}
+
+// Keeps the best min(n, K) of entries [0, n) (n <= kCap) of a wavefront's (value, index)
+// arrays in slots [0, min(n, K)), best first, and returns that count.  Entries with index -1
+// are empty.  Every lane reads its entries before any slot is written.
+__device__ int keep_best(float *cv, int32_t *ci, int n, int K, int lane) {
+    constexpr int kPer = kCap / 64;
+    uint64_t key[kPer];
+#pragma unroll
+    for (int s = 0; s < kPer; ++s) {
+        const int q = s * 64 + lane;
+        key[s] = q < n ? cand_key(cv[q], ci[q]) : 0;
+    }
+    const int m = n < K ? n : K;
+    uint64_t mine = 0;
+    for (int r = 0; r < m; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int s = 1; s < kPer; ++s) best = key[s] > best ? key[s] : best;
+        const uint64_t w = wave_max_u64(best);
+#pragma unroll
+        for (int s = 0; s < kPer; ++s) key[s] = key[s] == w ? 0 : key[s];
+        mine = lane == r ? w : mine;
+    }
+    if (lane < m) {
+        cv[lane] = key_value(mine);
+        ci[lane] = mine ? key_index(mine) : -1;
+    }
+    return m;
+}
+
+struct WaveCands {
+    float *cv;
+    int32_t *ci;
+    int cnt;      // entries in the buffer (wavefront-uniform)
+    float tau;    // K-th best value once the buffer was cut to K, else -inf
+};
+
+// One piece: up to four consecutive elements per lane (ok[e] says which exist), all with
+// larger indices than every entry already in the buffer.  They are judged against the
+// buffer as it stood before the piece.
+__device__ __forceinline__ void offer_piece(WaveCands &wc, const float (&x)[4], const bool (&ok)[4],
+                                            int32_t idx0, int K, int lane) {
+    bool full = wc.cnt >= K;
+    float mx = -__builtin_huge_valf();
+    bool any_ok = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        mx = ok[e] ? fmaxf(mx, x[e]) : mx;
+        any_ok |= ok[e];
+    }
+    if (!__any(any_ok && (!full || mx > wc.tau))) return;
+    if (wc.cnt + kPiece > kCap) {
+        wc.cnt = keep_best(wc.cv, wc.ci, wc.cnt, K, lane);
+        full = wc.cnt >= K;
+        wc.tau = full ? wc.cv[K - 1] : -__builtin_huge_valf();
+    }
+    int cnt = wc.cnt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bool pass = ok[e] && (!full || x[e] > wc.tau);
+        const uint64_t bal = __ballot(pass);
+        if (bal) {
+            const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
+                                      (uint32_t)(bal >> 32),
+                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (pass) {
+                wc.cv[pos] = x[e];
+                wc.ci[pos] = idx0 + e;
+            }
+            cnt += __popcll(bal);
+        }
+    }
+    wc.cnt = cnt;
+}
+
+struct RowSum {
+    float m;     // running max of the lane's finite values (-FLT_MAX before the first)
+    double s;    // sum of exp(l - m) over them
+};
+
+__device__ __forceinline__ void sum_piece(RowSum &a, const float (&x)[4], const double *tab) {
+    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (mx > a.m) {
+        a.s *= exp_nonpos((double)a.m - (double)mx, tab);
+        a.m = mx;
+    }
+    const double md = (double)a.m;
+    double t = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t += exp_nonpos((double)x[e] - md, tab);
+    a.s += t;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
+    const float *__restrict__ logits, int64_t V, int K, int rows_per_group,
+    int64_t group_stride, int32_t *__restrict__ top_tok, double *__restrict__ top_logp) {
+    __shared__ float s_cv[kTkWaves][kCap];
+    __shared__ int32_t s_ci[kTkWaves][kCap];
+    __shared__ double s_tab[32];
+    __shared__ float s_m[kTkWaves];
+    __shared__ double s_s[kTkWaves];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int64_t r = blockIdx.x;
+    const int64_t src = (r / rows_per_group) * group_stride + r % rows_per_group;
+    const float *rp = logits + src * V;
+
+    if (tid < 32) s_tab[tid] = exp2((double)tid / 32.0);
+    __syncthreads();
+
+    WaveCands wc{s_cv[w], s_ci[w], 0, -__builtin_huge_valf()};
+    RowSum acc{-kFltMax, 0.0};
+
+    // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
+    const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);
+    int64_t a0 = (4 - mis) & 3;
+    if (a0 > V) a0 = V;
+    const int64_t nvec = (V - a0) >> 2;
+    const int64_t a1 = a0 + 4 * nvec;
+    if (w == 0) {
+        float x[4] = {-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
+                      -__builtin_huge_valf()};
+        bool ok[4] = {lane < a0, false, false, false};
+        if (ok[0]) x[0] = clean(rp[lane]);
+        sum_piece(acc, x, s_tab);
+        offer_piece(wc, x, ok, lane, K, lane);
+    }
+
+    // body: 16-byte pieces, piece p = base + u * 256 + tid holds elements a0 + 4p .. + 3
+    const f32x4 *vp = reinterpret_cast<const f32x4 *>(rp + a0);
+    for (int64_t base = 0; base < nvec; base += 4 * kTkThreads) {
+        f32x4 raw[4];
+        bool have[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t p = base + u * kTkThreads + tid;
+            have[u] = p < nvec;
+            raw[u] = have[u] ? vp[p] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t p = base + u * kTkThreads + tid;
+            float x[4];
+            bool ok[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ok[e] = have[u];
+                x[e] = have[u] ? clean(raw[u][e]) : -__builtin_huge_valf();
+            }
+            sum_piece(acc, x, s_tab);
+            offer_piece(wc, x, ok, (int32_t)(a0 + 4 * p), K, lane);
+        }
+    }
+
+    // tail: the last V - a1 (< 4) elements (wavefront 0), larger than every index above
+    if (w == 0) {
+        float x[4] = {-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
+                      -__builtin_huge_valf()};
+        bool ok[4] = {a1 + lane < V, false, false, false};
+        if (ok[0]) x[0] = clean(rp[a1 + lane]);
+        sum_piece(acc, x, s_tab);
+        offer_piece(wc, x, ok, (int32_t)(a1 + lane), K, lane);
+    }
+
+    // each wavefront's K best, then the max and sum of the wavefront
+    const int c = keep_best(wc.cv, wc.ci, wc.cnt, K, lane);
+    for (int k = c + lane; k < K; k += 64) wc.ci[k] = -1;
+    float M = acc.m;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    double S = acc.s * exp_nonpos((double)acc.m - (double)M, s_tab);
+    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+    if (lane == 0) {
+        s_m[w] = M;
+        s_s[w] = S;
+    }
+    __syncthreads();
+    // the other three lists move behind wavefront 0's, which then keeps the best K of 4K
+    for (int q = tid; q < (kTkWaves - 1) * K; q += kTkThreads) {
+        const int ww = 1 + q / K, k = q - (ww - 1) * K;
+        s_cv[0][K + q] = s_cv[ww][k];
+        s_ci[0][K + q] = s_ci[ww][k];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const int kept = keep_best(s_cv[0], s_ci[0], kTkWaves * K, K, lane);
+    (void)kept;  // = K: the row holds V >= K elements
+    M = s_m[0];
+    for (int j = 1; j < kTkWaves; ++j) M = fmaxf(M, s_m[j]);
+    S = 0.0;
+    for (int j = 0; j < kTkWaves; ++j) S += s_s[j] * exp_nonpos((double)s_m[j] - (double)M, s_tab);
+    const double logS = S > 0.0 ? log(S) : 0.0;
+    for (int k = lane; k < K; k += 64) {
+        const float v = s_cv[0][k];
+        top_tok[r * K + k] = s_ci[0][k];
+        top_logp[r * K + k] =
+            (S > 0.0 && v > -__builtin_huge_valf()) ? ((double)v - (double)M) - logS
+                                                     : -__builtin_huge_val();
+    }
+}
+
+__device__ __forceinline__ uint64_t ord_f64(double x) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// One wavefront per sequence (T <= 64: one lane per node).  Row i's lists sit at
+// [b][i][K] for i < T - 1.
+__global__ __launch_bounds__(64) void best_first_kernel(
+    const int32_t *__restrict__ top_tok, const double *__restrict__ top_logp,
+    const int32_t *__restrict__ root_token, int T, int K, int max_levels,
+    int32_t *__restrict__ parents, int32_t *__restrict__ tokens, double *__restrict__ cum) {
+    extern __shared__ double s_lp[];              // [(T - 1) * K] log-probs, then tokens
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int nr = T - 1;
+    int32_t *s_tk = reinterpret_cast<int32_t *>(s_lp + (size_t)nr * K);
+    const int64_t off = (int64_t)b * nr * K;
+    for (int q = lane; q < nr * K; q += 64) {
+        s_lp[q] = top_logp[off + q];
+        s_tk[q] = top_tok[off + q];
+    }
+    __syncthreads();
+
+    int32_t par = -1, tok = lane == 0 ? root_token[b] : -1;
+    double cj = 0.0;     // this node's cumulative log-prob
+    int level = 1, next = 0;
+    bool live = lane == 0 && nr > 0 && max_levels > 1;   // has a pending child
+    double key = live ? cj + s_lp[0] : 0.0;
+    for (int n = 1; n < T; ++n) {
+        const uint64_t kk = live ? ord_f64(key) : 0;
+        const uint64_t top = wave_max_u64(kk);
+        if (top == 0) break;   // nothing pending: excluded by the caller's shape check
+        const uint64_t bal = __ballot(kk == top);
+        const int win = (int)__builtin_ctzll(bal);
+        const int32_t ctok = live ? s_tk[lane * K + next] : -1;
+        const int32_t wtok = __shfl(ctok, win, 64);
+        const double wkey = __shfl(key, win, 64);
+        const int wlevel = __shfl(level, win, 64);
+        if (lane == win) {
+            ++next;
+            live = next < K;
+            if (live) key = cj + s_lp[lane * K + next];
+        }
+        if (lane == n) {
+            par = win;
+            tok = wtok;
+            cj = wkey;
+            level = wlevel + 1;
+            next = 0;
+            live = n < nr && level < max_levels;
+            if (live) key = cj + s_lp[n * K];
+        }
+    }
+    if (lane < T) {
+        parents[(int64_t)b * T + lane] = par;
+        tokens[(int64_t)b * T + lane] = tok;
+        cum[(int64_t)b * T + lane] = cj;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk_rows(const float *logits, int64_t rows, int64_t V, int K,
+                            int rows_per_group, int64_t group_stride, int32_t *top_tok,
+                            double *top_logp, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(kTkThreads), 0, stream,
+                       logits, V, K, rows_per_group, group_stride, top_tok, top_logp);
+    return hipGetLastError();
+}
+
+hipError_t launch_best_first(const int32_t *top_tok, const double *top_logp,
+                             const int32_t *root_token, int B, int T, int K, int max_levels,
+                             int32_t *parents, int32_t *tokens, double *cum, hipStream_t stream) {
+    if (B == 0) return hipSuccess;
+    const size_t smem = (size_t)(T - 1) * K * (sizeof(double) + sizeof(int32_t));
+    hipLaunchKernelGGL(best_first_kernel, dim3((unsigned)B), dim3(64), smem, stream, top_tok,
+                       top_logp, root_token, T, K, max_levels, parents, tokens, cum);
+    return hipGetLastError();
+}
+
+}  // namespace sv

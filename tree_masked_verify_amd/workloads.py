@@ -319,6 +319,20 @@ def make_uniforms(B: int, T: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
     return np.ascontiguousarray(u[0]), np.ascontiguousarray(u[1])
 
 
+def make_drafter_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu",
+                        T: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Synthetic drafter output for building a tree of T (default w.T) nodes: float32
+    logits [B, T, V] ~ N(0, logit_std^2), row i standing for the drafter's output at the
+    node admitted i-th, and the root tokens int32 [B] uniform over the vocabulary."""
+    device = torch.device(device)
+    T = w.T if T is None else T
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed * 7919 + 0xD2A)
+    logits = _randn((w.B, T, w.V), "f32", w.logit_std, gen, device)
+    roots = torch.randint(0, w.V, (w.B,), generator=gen, device=device, dtype=torch.int64)
+    return logits, roots.to(torch.int32)
+
+
 def scaled(w: Workload, **kw) -> Workload:
     """A copy of a workload with some fields replaced (smaller parity variants)."""
     d = {f: getattr(w, f) for f in w.__dataclass_fields__}
