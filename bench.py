@@ -269,10 +269,22 @@ def main():
     # and the tree-position rotary embedding (in place on Q and the tree keys; last, so
     # that the other stages are timed on the unrotated inputs)
     from tree_masked_verify_amd import sv_rope_tree
+    # and the builder of the next draft tree (top-K of each drafter row, best-first
+    # expansion) on synthetic drafter logits of this batch and tree size
+    from tree_masked_verify_amd import (sv_draft_tree, sv_draft_tree_workspace_size,
+                                        workspace)
+    d_k, d_levels = (w.topk or 8), (w.max_levels or w.T)
+    d_logits, d_roots = wl.make_drafter_inputs(w, seed=args.seed, device=dev)
+    d_par = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+    d_tok = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+    d_cum = torch.empty((w.B, w.T), dtype=torch.float64, device=dev)
+    d_ws = workspace(sv_draft_tree_workspace_size(w.B, w.T, d_k), dev)
     stages = {}
     for name, fn in (("mask", st.build_mask), ("attention", st.attention),
                      ("accept", st.accept), ("commit", st.commit),
                      ("accept_sampled", lambda: st.accept_sampled(ua, us, w.temperature)),
+                     ("draft_tree", lambda: sv_draft_tree(d_logits, d_roots, d_k, d_levels,
+                                                          d_par, d_tok, d_cum, d_ws)),
                      ("rope", lambda: sv_rope_tree(st.q, st.k_tree, st.prefix_len, st.depth,
                                                    1e4))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -300,7 +312,8 @@ def main():
                    "head_dim": w.D, "prefix": list(w.prefix), "tree_nodes": w.T,
                    "tree": w.tree, "vocab": w.V, "paged_block": w.block_size,
                    "num_splits": args.splits, "seed": args.seed,
-                   "sampled_temperature": w.temperature},
+                   "sampled_temperature": w.temperature, "draft_topk": d_k,
+                   "draft_levels": d_levels},
         "roofline": {"bound": "hbm", "kernel": "tree-verify attention (split + merge kernels)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name),
@@ -313,6 +326,9 @@ def main():
         # sampled acceptance: one read of every logit row (the walk and the draw touch a
         # few more bytes per sequence, not counted)
         "accept_sampled_gbs": round(bytes_argmax / (stages["accept_sampled"] * 1e-6) / 1e9, 1),
+        # draft tree: one read of the drafter rows that can be expanded (all but the last)
+        "draft_tree_gbs": round(w.B * (w.T - 1) * w.V * 4 / (stages["draft_tree"] * 1e-6) / 1e9,
+                                1),
         # rotary embedding: Q and tree keys read and written once
         "rope_gbs": round(2 * w.B * (w.Hq + w.Hkv) * w.T * w.D * (2 if w.dtype == "bf16" else 4)
                           / (stages["rope"] * 1e-6) / 1e9, 1),

@@ -15,7 +15,7 @@
 //
 // topk_rows_kernel: one workgroup of four wavefronts per row.  Every lane streams its
 // 16-byte pieces once and keeps an online max and an fp64 sum of exponentials
-// (exp_nonpos below).  Each wavefront keeps a candidate buffer in LDS: a piece's element
+// (exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's element
 // enters it when it beats the wavefront's K-th best so far (while fewer than K entries
 // exist, every element enters).  When the buffer could overflow, the wavefront keeps its K
 // best (K rounds of a 64-lane max over (value, -index) keys) and raises its threshold.
@@ -36,35 +36,50 @@ constexpr int kCap = 512;                   // candidate entries per wavefront
 constexpr int kPiece = 256;                 // the most one piece (one 16-byte load per lane) adds
 constexpr float kFltMax = 3.40282347e38f;
 
-// exp(d) for d <= 0 in fp64; d = -inf gives 0.  Table-driven method (P. T. P. Tang, "Table-
-// driven implementation of the exponential function in IEEE floating-point arithmetic", ACM
-// TOMS 15(2), 1989): d = (32 k + j) ln2/32 + r with |r| <= ln2/64, so
-// e^d = 2^k * 2^(j/32) * e^r; e^r - 1 is its Taylor polynomial of degree 6 (remainder below
-// 2^-57 relative) and 2^(j/32) comes from a 32-entry table.
-__device__ __forceinline__ double exp_nonpos(double d, const double *tab) {
-    if (!(d > -745.5)) return 0.0;                    // below the smallest subnormal, or -inf
-    constexpr double kInvL = 0x1.71547652b82fep+5;    // 32 / ln 2
-    constexpr double kL1 = 0x1.62e42fefa39efp-6;      // ln 2 / 32, leading part
-    constexpr double kL2 = 0x1.abc9e3b39803fp-61;     // ln 2 / 32 - kL1
-    const double n = rint(d * kInvL);
+// exp(d) for d in [-700, 0] in fp64, callers clamp d into that range first.  Table-driven
+// method (P. T. P. Tang, "Table-driven implementation of the exponential function in IEEE
+// floating-point arithmetic", ACM TOMS 15(2), 1989): d = (256 k + j) ln2/256 + r with
+// |r| <= ln2/512, so e^d = 2^k * 2^(j/256) * e^r; e^r - 1 is its Taylor polynomial of
+// degree 4 (remainder below 2^-54 relative) and 2^(j/256) comes from a 256-entry table.
+// n = 256 k + j is rounded by adding 1.5 * 2^52 (its low word then holds n).
+__device__ __forceinline__ double exp_core(double d, const double *tab) {
+    constexpr double kInvL = 0x1.71547652b82fep+8;    // 256 / ln 2
+    constexpr double kL1 = 0x1.62e42fefa39efp-9;      // ln 2 / 256, leading part
+    constexpr double kL2 = 0x1.abc9e3b39803fp-64;     // ln 2 / 256 - kL1
+    constexpr double kRound = 0x1.8p52;
+    const double nb = fma(d, kInvL, kRound);
+    const double n = nb - kRound;
+    const int ni = __double2loint(nb);
     double r = fma(-n, kL1, d);
     r = fma(-n, kL2, r);
-    const int ni = (int)n;
-    double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-    q = fma(q, r, 1.0 / 24.0);
-    q = fma(q, r, 1.0 / 6.0);
+    double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
     q = fma(q, r, 0.5);
     const double p = fma(r * r, q, r);                // e^r - 1
-    const double t = tab[ni & 31];
-    return ldexp(fma(t, p, t), ni >> 5);               // ni >> 5 = floor(ni / 32)
+    const double t = tab[ni & 255];
+    return ldexp(fma(t, p, t), ni >> 8);               // ni >> 8 = floor(n / 256)
+}
+
+// exp(x - m) for a raw logit x and a lane max m >= every finite x seen: NaN and -inf give
+// ~1e-304 (d clamped at -700), +inf gives 1 (it counts as the largest finite float, which
+// then is m).  Those tiny terms are below the last bit of any sum that holds a finite entry
+// (such a sum is >= 1).
+__device__ __forceinline__ double exp_term(float x, double md, const double *tab) {
+    double d = (double)x - md;
+    d = fmin(fmax(d, -700.0), 0.0);                    // fmax(NaN, -700) = -700
+    return exp_core(d, tab);
 }
 
 // A logit as the rule reads it: NaN and -inf give -inf, +inf the largest finite float, and
 // -0 becomes +0 so that the two zeros compare equal as keys.
 __device__ __forceinline__ float clean(float x) {
-    if (!(x > -__builtin_huge_valf())) return -__builtin_huge_valf();
-    x = x < kFltMax ? x : kFltMax;
+    x = fminf(fmaxf(x, -__builtin_huge_valf()), kFltMax);   // fmaxf(NaN, -inf) = -inf
     return x + 0.0f;
+}
+
+// The largest of four raw logits as the rule reads them (-inf when none is finite).
+__device__ __forceinline__ float max4(const f32x4 &x) {
+    const float a = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));   // a NaN operand is ignored
+    return fminf(fmaxf(a, -__builtin_huge_valf()), kFltMax);
 }
 
 // Order-preserving 64-bit key of (value, index): larger value first, then smaller index.
@@ -127,20 +142,13 @@ struct WaveCands {
     float tau;    // K-th best value once the buffer was cut to K, else -inf
 };
 
-// One piece: up to four consecutive elements per lane (ok[e] says which exist), all with
-// larger indices than every entry already in the buffer.  They are judged against the
-// buffer as it stood before the piece.
-__device__ __forceinline__ void offer_piece(WaveCands &wc, const float (&x)[4], const bool (&ok)[4],
+// One piece: up to four consecutive raw logits per lane (the first `nok` exist), all with
+// larger indices than every entry already in the buffer, mx = max4 of them.  They are
+// judged against the buffer as it stood before the piece.
+__device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float mx, int nok,
                                             int32_t idx0, int K, int lane) {
     bool full = wc.cnt >= K;
-    float mx = -__builtin_huge_valf();
-    bool any_ok = false;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        mx = ok[e] ? fmaxf(mx, x[e]) : mx;
-        any_ok |= ok[e];
-    }
-    if (!__any(any_ok && (!full || mx > wc.tau))) return;
+    if (!__any(nok > 0 && (!full || mx > wc.tau))) return;
     if (wc.cnt + kPiece > kCap) {
         wc.cnt = keep_best(wc.cv, wc.ci, wc.cnt, K, lane);
         full = wc.cnt >= K;
@@ -149,14 +157,15 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const float (&x)[4], 
     int cnt = wc.cnt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const bool pass = ok[e] && (!full || x[e] > wc.tau);
+        const float v = clean(x[e]);
+        const bool pass = e < nok && (!full || v > wc.tau);
         const uint64_t bal = __ballot(pass);
         if (bal) {
             const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
                                       (uint32_t)(bal >> 32),
                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
             if (pass) {
-                wc.cv[pos] = x[e];
+                wc.cv[pos] = v;
                 wc.ci[pos] = idx0 + e;
             }
             cnt += __popcll(bal);
@@ -166,21 +175,22 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const float (&x)[4], 
 }
 
 struct RowSum {
-    float m;     // running max of the lane's finite values (-FLT_MAX before the first)
-    double s;    // sum of exp(l - m) over them
+    float m;     // running max of the lane's logits as read (-FLT_MAX before the first)
+    double md;   // m as a double
+    double s;    // sum of exp(l - m) over them (plus ~1e-304 per NaN / -inf entry)
 };
 
-__device__ __forceinline__ void sum_piece(RowSum &a, const float (&x)[4], const double *tab) {
-    const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+// Adds a piece to the lane's online max and sum (entries beyond those that exist are -inf).
+__device__ __forceinline__ void sum_piece(RowSum &a, const f32x4 &x, float mx, const double *tab) {
     if (mx > a.m) {
-        a.s *= exp_nonpos((double)a.m - (double)mx, tab);
+        const double mxd = (double)mx;
+        a.s *= exp_core(fmax(a.md - mxd, -700.0), tab);
         a.m = mx;
+        a.md = mxd;
     }
-    const double md = (double)a.m;
-    double t = 0.0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) t += exp_nonpos((double)x[e] - md, tab);
-    a.s += t;
+    const double e0 = exp_term(x[0], a.md, tab), e1 = exp_term(x[1], a.md, tab);
+    const double e2 = exp_term(x[2], a.md, tab), e3 = exp_term(x[3], a.md, tab);
+    a.s += (e0 + e1) + (e2 + e3);
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     int64_t group_stride, int32_t *__restrict__ top_tok, double *__restrict__ top_logp) {
     __shared__ float s_cv[kTkWaves][kCap];
     __shared__ int32_t s_ci[kTkWaves][kCap];
-    __shared__ double s_tab[32];
+    __shared__ double s_tab[256];
     __shared__ float s_m[kTkWaves];
     __shared__ double s_s[kTkWaves];
 
@@ -198,12 +208,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     const int64_t r = blockIdx.x;
     const int64_t src = (r / rows_per_group) * group_stride + r % rows_per_group;
     const float *rp = logits + src * V;
+    constexpr float kNInf = -__builtin_huge_valf();
 
-    if (tid < 32) s_tab[tid] = exp2((double)tid / 32.0);
+    s_tab[tid] = exp2((double)tid / 256.0);
     __syncthreads();
 
-    WaveCands wc{s_cv[w], s_ci[w], 0, -__builtin_huge_valf()};
-    RowSum acc{-kFltMax, 0.0};
+    WaveCands wc{s_cv[w], s_ci[w], 0, kNInf};
+    RowSum acc{-kFltMax, (double)-kFltMax, 0.0};
 
     // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
     const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);
@@ -212,48 +223,48 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     const int64_t nvec = (V - a0) >> 2;
     const int64_t a1 = a0 + 4 * nvec;
     if (w == 0) {
-        float x[4] = {-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
-                      -__builtin_huge_valf()};
-        bool ok[4] = {lane < a0, false, false, false};
-        if (ok[0]) x[0] = clean(rp[lane]);
-        sum_piece(acc, x, s_tab);
-        offer_piece(wc, x, ok, lane, K, lane);
+        const int nok = lane < a0 ? 1 : 0;
+        const f32x4 x{nok ? rp[lane] : kNInf, kNInf, kNInf, kNInf};
+        const float mx = max4(x);
+        sum_piece(acc, x, mx, s_tab);
+        offer_piece(wc, x, mx, nok, lane, K, lane);
     }
 
-    // body: 16-byte pieces, piece p = base + u * 256 + tid holds elements a0 + 4p .. + 3
+    // body: 16-byte pieces, piece p = base + u * 256 + tid holds elements a0 + 4p .. + 3;
+    // whole trips of four pieces per lane, then one trip with the pieces that are left
     const f32x4 *vp = reinterpret_cast<const f32x4 *>(rp + a0);
-    for (int64_t base = 0; base < nvec; base += 4 * kTkThreads) {
+    constexpr int64_t kTrip = 4 * kTkThreads;
+    const int64_t nfull = nvec / kTrip * kTrip;
+    for (int64_t base = 0; base < nfull; base += kTrip) {
         f32x4 raw[4];
-        bool have[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = vp[base + u * kTkThreads + tid];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t p = base + u * kTkThreads + tid;
-            have[u] = p < nvec;
-            raw[u] = have[u] ? vp[p] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float mx = max4(raw[u]);
+            sum_piece(acc, raw[u], mx, s_tab);
+            offer_piece(wc, raw[u], mx, 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)), K,
+                        lane);
         }
+    }
+    if (nfull < nvec) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t p = base + u * kTkThreads + tid;
-            float x[4];
-            bool ok[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ok[e] = have[u];
-                x[e] = have[u] ? clean(raw[u][e]) : -__builtin_huge_valf();
-            }
-            sum_piece(acc, x, s_tab);
-            offer_piece(wc, x, ok, (int32_t)(a0 + 4 * p), K, lane);
+            const int64_t p = nfull + u * kTkThreads + tid;
+            const f32x4 x = p < nvec ? vp[p] : f32x4{kNInf, kNInf, kNInf, kNInf};
+            const float mx = max4(x);
+            sum_piece(acc, x, mx, s_tab);
+            offer_piece(wc, x, mx, p < nvec ? 4 : 0, (int32_t)(a0 + 4 * p), K, lane);
         }
     }
 
     // tail: the last V - a1 (< 4) elements (wavefront 0), larger than every index above
     if (w == 0) {
-        float x[4] = {-__builtin_huge_valf(), -__builtin_huge_valf(), -__builtin_huge_valf(),
-                      -__builtin_huge_valf()};
-        bool ok[4] = {a1 + lane < V, false, false, false};
-        if (ok[0]) x[0] = clean(rp[a1 + lane]);
-        sum_piece(acc, x, s_tab);
-        offer_piece(wc, x, ok, (int32_t)(a1 + lane), K, lane);
+        const int nok = a1 + lane < V ? 1 : 0;
+        const f32x4 x{nok ? rp[a1 + lane] : kNInf, kNInf, kNInf, kNInf};
+        const float mx = max4(x);
+        sum_piece(acc, x, mx, s_tab);
+        offer_piece(wc, x, mx, nok, (int32_t)(a1 + lane), K, lane);
     }
 
     // each wavefront's K best, then the max and sum of the wavefront
@@ -261,7 +272,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     for (int k = c + lane; k < K; k += 64) wc.ci[k] = -1;
     float M = acc.m;
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    double S = acc.s * exp_nonpos((double)acc.m - (double)M, s_tab);
+    double S = acc.s * exp_core(fmax(acc.md - (double)M, -700.0), s_tab);
     for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
     if (lane == 0) {
         s_m[w] = M;
@@ -281,14 +292,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     M = s_m[0];
     for (int j = 1; j < kTkWaves; ++j) M = fmaxf(M, s_m[j]);
     S = 0.0;
-    for (int j = 0; j < kTkWaves; ++j) S += s_s[j] * exp_nonpos((double)s_m[j] - (double)M, s_tab);
-    const double logS = S > 0.0 ? log(S) : 0.0;
+    for (int j = 0; j < kTkWaves; ++j)
+        S += s_s[j] * exp_core(fmax((double)s_m[j] - (double)M, -700.0), s_tab);
+    const double logS = log(S);
     for (int k = lane; k < K; k += 64) {
         const float v = s_cv[0][k];
         top_tok[r * K + k] = s_ci[0][k];
-        top_logp[r * K + k] =
-            (S > 0.0 && v > -__builtin_huge_valf()) ? ((double)v - (double)M) - logS
-                                                     : -__builtin_huge_val();
+        top_logp[r * K + k] = v > kNInf ? ((double)v - (double)M) - logS : -__builtin_huge_val();
     }
 }
 
@@ -297,8 +307,41 @@ __device__ __forceinline__ uint64_t ord_f64(double x) {
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// A 64-bit value moved across lanes by one DPP control (both halves); lanes without a
+// source, or outside the rows of kRowMask, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, kRowMask, 0xf, true);
+    const int hi =
+        __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, kRowMask, 0xf, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wavefront of unsigned 64-bit values, in every lane: row_shr 1, 2, 4, 8
+// leave each row's maximum in its lane 15; row_bcast 15 and 31 carry it into lane 63.
+__device__ __forceinline__ uint64_t wave_max_dpp(uint64_t x) {
+    x = umax64(x, dpp_u64<0x111, 0xf>(x));
+    x = umax64(x, dpp_u64<0x112, 0xf>(x));
+    x = umax64(x, dpp_u64<0x114, 0xf>(x));
+    x = umax64(x, dpp_u64<0x118, 0xf>(x));
+    x = umax64(x, dpp_u64<0x142, 0xa>(x));
+    x = umax64(x, dpp_u64<0x143, 0xc>(x));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+    return __hiloint2double(hi, lo);
+}
+
 // One wavefront per sequence (T <= 64: one lane per node).  Row i's lists sit at
-// [b][i][K] for i < T - 1.
+// [b][i][K] for i < T - 1.  Each lane keeps its head child (the best one not admitted yet)
+// and the one after it in registers, so an admission reads no memory on its critical path.
 __global__ __launch_bounds__(64) void best_first_kernel(
     const int32_t *__restrict__ top_tok, const double *__restrict__ top_logp,
     const int32_t *__restrict__ root_token, int T, int K, int max_levels,
@@ -315,34 +358,46 @@ __global__ __launch_bounds__(64) void best_first_kernel(
     }
     __syncthreads();
 
+    int rank = 0;                                 // rank of the head child
+    double hlp = 0.0, nlp = 0.0;                  // log-probs of the head child and the next
+    int32_t htok = -1, ntok = -1;
+    if (lane < nr) {
+        hlp = s_lp[lane * K];
+        htok = s_tk[lane * K];
+        if (K > 1) {
+            nlp = s_lp[lane * K + 1];
+            ntok = s_tk[lane * K + 1];
+        }
+    }
     int32_t par = -1, tok = lane == 0 ? root_token[b] : -1;
-    double cj = 0.0;     // this node's cumulative log-prob
-    int level = 1, next = 0;
+    double cj = 0.0;                              // this node's cumulative log-prob
+    int level = 1;
     bool live = lane == 0 && nr > 0 && max_levels > 1;   // has a pending child
-    double key = live ? cj + s_lp[0] : 0.0;
     for (int n = 1; n < T; ++n) {
+        const double key = cj + hlp;
         const uint64_t kk = live ? ord_f64(key) : 0;
-        const uint64_t top = wave_max_u64(kk);
+        const uint64_t top = wave_max_dpp(kk);
         if (top == 0) break;   // nothing pending: excluded by the caller's shape check
-        const uint64_t bal = __ballot(kk == top);
-        const int win = (int)__builtin_ctzll(bal);
-        const int32_t ctok = live ? s_tk[lane * K + next] : -1;
-        const int32_t wtok = __shfl(ctok, win, 64);
-        const double wkey = __shfl(key, win, 64);
-        const int wlevel = __shfl(level, win, 64);
+        const int win = (int)__builtin_ctzll(__ballot(kk == top));
+        const double wkey = readlane_f64(key, win);
+        const int32_t wtok = __builtin_amdgcn_readlane(htok, win);
+        const int wlevel = __builtin_amdgcn_readlane(level, win);
         if (lane == win) {
-            ++next;
-            live = next < K;
-            if (live) key = cj + s_lp[lane * K + next];
+            ++rank;
+            live = rank < K;
+            hlp = nlp;
+            htok = ntok;
+            if (rank + 1 < K) {
+                nlp = s_lp[lane * K + rank + 1];
+                ntok = s_tk[lane * K + rank + 1];
+            }
         }
         if (lane == n) {
             par = win;
             tok = wtok;
             cj = wkey;
             level = wlevel + 1;
-            next = 0;
             live = n < nr && level < max_levels;
-            if (live) key = cj + s_lp[n * K];
         }
     }
     if (lane < T) {
