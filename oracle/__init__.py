@@ -58,13 +58,20 @@ def _declare(lib):
     lib.oracle_kv_commit.argtypes = [
         _vp, _vp, _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64,
         _int, _i32p, _int, _i32p, _int, _int, _int, _int]
+    lib.oracle_kv_append.argtypes = [
+        _vp, _vp, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64, _int, _i32p, _int,
+        _int, _int, _int, _int]
+    lib.oracle_kv_compact.argtypes = [
+        _i32p, _i32p, _i32p, _vp, _vp, _i32p, _int, _int, _i64, _i64, _i64, _i64, _int, _i32p,
+        _int, _i32p, _int, _int, _int, _int]
     _f64p = ctypes.POINTER(ctypes.c_double)
     lib.oracle_topk_logprobs.argtypes = [_f32p, _i64, _i64, _int, _i32p, _f64p, _int]
     lib.oracle_draft_tree.argtypes = [_f32p, _i32p, _int, _int, _i64, _int, _int, _i32p, _i32p,
                                       _f64p]
     for f in ("oracle_build_tree_mask", "oracle_tree_verify_attention", "oracle_argmax",
               "oracle_accept_longest_path", "oracle_accept_sampled", "oracle_rope_tree",
-              "oracle_kv_commit", "oracle_topk_logprobs", "oracle_draft_tree"):
+              "oracle_kv_commit", "oracle_topk_logprobs", "oracle_draft_tree",
+              "oracle_kv_append", "oracle_kv_compact"):
         getattr(lib, f).restype = _int
     return lib
 
@@ -126,13 +133,14 @@ class Oracle:
 
     def tree_verify_attention(self, q, k_tree, v_tree, cache: Cache, prefix_len, max_prefix_len,
                               mask, scale, rows=None, nthreads=0):
-        """q [B,Hq,T,D], k_tree/v_tree [B,Hkv,T,D] (float32, or uint16 bf16 bits).
+        """q [B,Hq,T,D], k_tree/v_tree [B,Hkv,T,D] (float32, or uint16 bf16 bits); with
+        k_tree and v_tree None the tree rows are read from the cache at positions P + j.
 
         Returns out float32 [B,T,Hq,D], or [len(rows), D] when rows (int32 [n,3] of
         (b, h, i)) is given.
         """
         B, Hq, T, D = q.shape
-        Hkv = k_tree.shape[1]
+        Hkv = k_tree.shape[1] if k_tree is not None else cache.block_stride // cache.head_stride
         prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
         mask = np.ascontiguousarray(mask, dtype=np.uint64)
         if rows is not None:
@@ -143,9 +151,11 @@ class Oracle:
             out = np.zeros((B, T, Hq, D), np.float32)
             nrows = 0
         for a in (q, k_tree, v_tree, cache.k, cache.v, cache.table):
-            assert a.flags["C_CONTIGUOUS"]
+            assert a is None or a.flags["C_CONTIGUOUS"]
+        assert (k_tree is None) == (v_tree is None)
         rc = self.lib.oracle_tree_verify_attention(
-            q.ctypes.data, k_tree.ctypes.data, v_tree.ctypes.data, cache.k.ctypes.data,
+            q.ctypes.data, None if k_tree is None else k_tree.ctypes.data,
+            None if v_tree is None else v_tree.ctypes.data, cache.k.ctypes.data,
             cache.v.ctypes.data, _p(cache.table, _i32p), cache.block_size, cache.max_blocks,
             cache.block_stride, cache.head_stride, cache.row_stride, cache.num_blocks,
             cache.dtype, _p(prefix_len, _i32p), int(max_prefix_len), _p(mask, _u64p), B, Hq,
@@ -202,6 +212,40 @@ class Oracle:
             _p(nodes, _i32p), _p(toks, _i32p))
         assert rc == 0
         return L, nodes, toks
+
+    def kv_append(self, k_tree, v_tree, tree_err, cache: Cache, prefix_len, max_prefix_len):
+        """Writes the tree rows into cache.k / cache.v at [P, P + T) in place; returns the
+        updated tree_err (3 where a sequence could not be written)."""
+        B, Hkv, T, D = k_tree.shape
+        err = np.zeros((B,), np.int32) if tree_err is None else \
+            np.array(tree_err, dtype=np.int32, copy=True)
+        prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        rc = self.lib.oracle_kv_append(
+            k_tree.ctypes.data, v_tree.ctypes.data, _p(err, _i32p), cache.k.ctypes.data,
+            cache.v.ctypes.data, _p(cache.table, _i32p), cache.block_size, cache.max_blocks,
+            cache.block_stride, cache.head_stride, cache.row_stride, cache.num_blocks,
+            cache.dtype, _p(prefix_len, _i32p), int(max_prefix_len), B, Hkv, T, D)
+        assert rc == 0
+        return err
+
+    def kv_compact(self, accepted_len, accepted_nodes, tree_err, cache: Cache, prefix_len,
+                   max_prefix_len, Hkv, T, D):
+        """Moves the accepted rows to [P, P + L) in place; returns new_prefix_len."""
+        accepted_len = np.ascontiguousarray(accepted_len, dtype=np.int32)
+        accepted_nodes = np.ascontiguousarray(accepted_nodes, dtype=np.int32)
+        prefix_len = np.ascontiguousarray(prefix_len, dtype=np.int32)
+        B = accepted_len.shape[0]
+        if tree_err is not None:
+            tree_err = np.ascontiguousarray(tree_err, dtype=np.int32)
+        npl = np.zeros((B,), np.int32)
+        rc = self.lib.oracle_kv_compact(
+            _p(accepted_len, _i32p), _p(accepted_nodes, _i32p), _p(tree_err, _i32p),
+            cache.k.ctypes.data, cache.v.ctypes.data, _p(cache.table, _i32p), cache.block_size,
+            cache.max_blocks, cache.block_stride, cache.head_stride, cache.row_stride,
+            cache.num_blocks, cache.dtype, _p(prefix_len, _i32p), int(max_prefix_len),
+            _p(npl, _i32p), B, Hkv, T, D)
+        assert rc == 0
+        return npl
 
     def topk_logprobs(self, logits, K, nthreads: int = 0):
         """Top-K of each row's log-softmax: (tokens int32 [..., K], logp float64 [..., K]),

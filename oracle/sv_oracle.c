@@ -127,6 +127,11 @@ static int64_t cache_row(const int32_t *table, int bs, int max_blocks, int64_t b
 /* as fp32 at out[b][i][h][:] (layout [q_seq_len, num_heads, head_dim]).      */
 /* P_b is clamped into [0, max_prefix_len]; prefix keys whose block-table     */
 /* entry is out of range are left out.                                        */
+/* With k_tree and v_tree NULL the tree rows live in the cache ([ADR] row E6  */
+/* per-layer tree-verify block: K/V appended at [prefix_len, prefix_len +     */
+/* tree_seq_len) before the attention reads them): tree row j is the cache    */
+/* row at position P_b + j (left out if its block-table entry is out of       */
+/* range).                                                                     */
 /* rows: optional list of (b, h, i) triples; then out is [nrows][D].          */
 static void attend_one(const void *q, const void *k_tree, const void *v_tree,
                        const void *k_cache, const void *v_cache, const int32_t *table, int bs,
@@ -158,11 +163,19 @@ static void attend_one(const void *q, const void *k_tree, const void *v_tree,
     const uint64_t *mrow = mask + ((int64_t)b * T + i) * W;
     for (int j = 0; j < T; ++j) {
         if (!((mrow[j / 64] >> (j % 64)) & 1)) continue;
-        const int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;
+        const void *ksrc = k_tree, *vsrc_j = v_tree;
+        int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;
+        if (!k_tree) { /* tree rows kept in the cache: node j at position P + j */
+            off = cache_row(table, bs, max_blocks, block_stride, head_stride, row_stride,
+                            num_blocks, b, kvh, P + j);
+            if (off < 0) continue;
+            ksrc = k_cache;
+            vsrc_j = v_cache;
+        }
         double dot = 0.0;
-        for (int d = 0; d < D; ++d) dot += elem(q, dtype, qoff + d) * elem(k_tree, dtype, off + d);
+        for (int d = 0; d < D; ++d) dot += elem(q, dtype, qoff + d) * elem(ksrc, dtype, off + d);
         s[n] = scale * dot;
-        vsrc[n] = v_tree;
+        vsrc[n] = vsrc_j;
         voff[n] = off;
         ++n;
     }
@@ -530,6 +543,107 @@ int oracle_kv_commit(const void *k_tree, const void *v_tree, const int32_t *acce
         }
         if (new_prefix_len) new_prefix_len[b] = ok ? P + L : P;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Write-before-accept variant ([ADR] row E6 per-layer tree-verify block: the */
+/* tree's K/V rows are appended to the cache at [prefix_len, prefix_len + T)  */
+/* before the attention; [ADR] section 4 Phase E5 and row E5b: after the      */
+/* acceptance, the cache is rolled back to the accepted path; [ANE] Facts on   */
+/* KV write-before-accept, the trade-off delayed write-through avoids).        */
+/* Append: for every sequence b with tree_err[b] == 0, if prefix_len[b] lies  */
+/* in [0, max_prefix_len] and every position of [P, P + T) has a block-table  */
+/* entry in range, tree row i of every kv head is copied to position P + i;   */
+/* otherwise nothing is written and tree_err[b] becomes 3.                    */
+int oracle_kv_append(const void *k_tree, const void *v_tree, int32_t *tree_err, void *k_cache,
+                     void *v_cache, const int32_t *table, int bs, int max_blocks,
+                     int64_t block_stride, int64_t head_stride, int64_t row_stride,
+                     int64_t num_blocks, int dtype, const int32_t *prefix_len, int max_prefix_len,
+                     int B, int Hkv, int T, int D) {
+    if (B < 0 || Hkv < 1 || T < 1 || D < 1 || bs < 1 || max_blocks < 1 || !tree_err) return -1;
+    const size_t esz = dtype == OR_F32 ? 4 : 2;
+    const int64_t cap = (int64_t)max_blocks * bs;
+    for (int b = 0; b < B; ++b) {
+        if (tree_err[b] != 0) continue;
+        const int32_t P = prefix_len[b];
+        int ok = P >= 0 && P <= max_prefix_len && (int64_t)P + T <= cap;
+        for (int i = 0; ok && i < T; ++i)
+            if (cache_row(table, bs, max_blocks, block_stride, head_stride, row_stride, num_blocks,
+                          b, 0, (int64_t)P + i) < 0)
+                ok = 0;
+        if (!ok) {
+            tree_err[b] = 3;
+            continue;
+        }
+        for (int h = 0; h < Hkv; ++h)
+            for (int i = 0; i < T; ++i) {
+                const int64_t dst = cache_row(table, bs, max_blocks, block_stride, head_stride,
+                                              row_stride, num_blocks, b, h, (int64_t)P + i);
+                const int64_t src = (((int64_t)b * Hkv + h) * T + i) * D;
+                memcpy((char *)k_cache + dst * esz, (const char *)k_tree + src * esz, esz * D);
+                memcpy((char *)v_cache + dst * esz, (const char *)v_tree + src * esz, esz * D);
+            }
+    }
+    return 0;
+}
+
+/* Compaction: for every sequence b with tree_err[b] == 0 (or tree_err NULL),  */
+/* L = accepted_len[b] in [0, T], path nodes in [0, T), P in                   */
+/* [0, max_prefix_len] and every position of [P, P + T) with a block-table    */
+/* entry in range: the cache row at P + j becomes the row that was at         */
+/* P + accepted_nodes[b][j], for j < L (all rows are read before any is       */
+/* written), and new_prefix_len[b] = P + L.  Otherwise nothing moves and      */
+/* new_prefix_len[b] = P.  Rows from P + L on are left as they are.           */
+int oracle_kv_compact(const int32_t *accepted_len, const int32_t *accepted_nodes,
+                      const int32_t *tree_err, void *k_cache, void *v_cache, const int32_t *table,
+                      int bs, int max_blocks, int64_t block_stride, int64_t head_stride,
+                      int64_t row_stride, int64_t num_blocks, int dtype,
+                      const int32_t *prefix_len, int max_prefix_len, int32_t *new_prefix_len,
+                      int B, int Hkv, int T, int D) {
+    if (B < 0 || Hkv < 1 || T < 1 || D < 1 || bs < 1 || max_blocks < 1) return -1;
+    const size_t esz = dtype == OR_F32 ? 4 : 2;
+    const int64_t cap = (int64_t)max_blocks * bs;
+    char *tk = (char *)malloc(esz * (size_t)D * (size_t)T);
+    char *tv = (char *)malloc(esz * (size_t)D * (size_t)T);
+    if (!tk || !tv) {
+        free(tk);
+        free(tv);
+        return -2;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int32_t P = prefix_len[b];
+        const int32_t L = accepted_len[b];
+        const int32_t *nodes = accepted_nodes + (int64_t)b * T;
+        int ok = !(tree_err && tree_err[b] != 0);
+        ok = ok && L >= 0 && L <= T && P >= 0 && P <= max_prefix_len && (int64_t)P + T <= cap;
+        for (int j = 0; ok && j < L; ++j)
+            if (nodes[j] < 0 || nodes[j] >= T) ok = 0;
+        for (int i = 0; ok && i < T; ++i)
+            if (cache_row(table, bs, max_blocks, block_stride, head_stride, row_stride, num_blocks,
+                          b, 0, (int64_t)P + i) < 0)
+                ok = 0;
+        if (ok) {
+            for (int h = 0; h < Hkv; ++h) {
+                for (int j = 0; j < L; ++j) { /* read every source row first */
+                    const int64_t src = cache_row(table, bs, max_blocks, block_stride, head_stride,
+                                                  row_stride, num_blocks, b, h,
+                                                  (int64_t)P + nodes[j]);
+                    memcpy(tk + (size_t)j * D * esz, (const char *)k_cache + src * esz, esz * D);
+                    memcpy(tv + (size_t)j * D * esz, (const char *)v_cache + src * esz, esz * D);
+                }
+                for (int j = 0; j < L; ++j) {
+                    const int64_t dst = cache_row(table, bs, max_blocks, block_stride, head_stride,
+                                                  row_stride, num_blocks, b, h, (int64_t)P + j);
+                    memcpy((char *)k_cache + dst * esz, tk + (size_t)j * D * esz, esz * D);
+                    memcpy((char *)v_cache + dst * esz, tv + (size_t)j * D * esz, esz * D);
+                }
+            }
+        }
+        if (new_prefix_len) new_prefix_len[b] = ok ? P + L : P;
+    }
+    free(tk);
+    free(tv);
     return 0;
 }
 

@@ -988,6 +988,120 @@ def pin_draft_tree_structure(orc):
         pairs = [(int(par[b, c]), int(tok[b, c])) for c in range(1, 12)]
         assert len(set(pairs)) == len(pairs)
 
+
+# ============================================= write-before-accept (in-cache) variant
+def gather_at(cache: O.Cache, b: int, h: int, pos, which: str = "k") -> np.ndarray:
+    """Rows at the given positions of sequence b, kv head h, float64 [n, D] (numpy
+    indexing over the block table, independent of the oracle's addressing)."""
+    pool = cache.k if which == "k" else cache.v
+    D = cache.row_stride
+    pool4 = pool.reshape(pool.shape[0], -1, cache.block_size, D)
+    pos = np.asarray(pos)
+    rows = pool4[cache.table[b, pos // cache.block_size], h, pos % cache.block_size, :]
+    return as_f64(rows, cache.dtype)
+
+
+def pin_incache_append_and_attention(orc):
+    """Append puts tree row i at position P + i and touches nothing else; attention over
+    the cache-resident tree equals attention over the tree buffers (bit for bit) and the
+    fp64 SDPA reference; sequences that cannot be appended are refused whole."""
+    inp = small_inputs("batched8k", 51, B=3, prefix=(10, 77), T=12, Hq=4, Hkv=2, D=64)
+    w = inp.w
+    cache = _cache(inp)
+    k0, v0 = cache.k.copy(), cache.v.copy()
+    P = to_np(inp.prefix_len)
+    kt, vt, q = to_np(inp.k_tree), to_np(inp.v_tree), to_np(inp.q)
+    err = orc.kv_append(kt, vt, None, cache, P, inp.max_prefix_len)
+    assert np.all(err == 0)
+    changed = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            pos = int(P[b]) + np.arange(w.T)
+            assert np.array_equal(gather_at(cache, b, h, pos, "k"), as_f64(kt[b, h], cache.dtype))
+            assert np.array_equal(gather_at(cache, b, h, pos, "v"), as_f64(vt[b, h], cache.dtype))
+            changed += w.T
+    D = w.D
+    diff_rows = np.any(cache.k.reshape(-1, D) != k0.reshape(-1, D), axis=1).sum()
+    assert diff_rows <= changed and np.array_equal(
+        cache.k.reshape(-1, D)[np.all(cache.k.reshape(-1, D) == k0.reshape(-1, D), axis=1)],
+        k0.reshape(-1, D)[np.all(cache.k.reshape(-1, D) == k0.reshape(-1, D), axis=1)])
+    mask, _, _ = orc.build_tree_mask(to_np(inp.parents))
+    a = orc.tree_verify_attention(q, None, None, cache, P, inp.max_prefix_len, mask, inp.scale)
+    c = run_attention(orc, inp)
+    assert np.array_equal(a, c)
+    for b in range(w.B):
+        kp = np.stack([gather_prefix(cache, b, h, int(P[b]), "k") for h in range(w.Hkv)])
+        vp = np.stack([gather_prefix(cache, b, h, int(P[b]), "v") for h in range(w.Hkv)])
+        pos = int(P[b]) + np.arange(w.T)
+        kk = np.stack([gather_at(cache, b, h, pos, "k") for h in range(w.Hkv)])
+        vv = np.stack([gather_at(cache, b, h, pos, "v") for h in range(w.Hkv)])
+        ref = sdpa_reference(as_f64(q[b], cache.dtype), kp, vp, kk, vv,
+                             closure_mask(to_np(inp.parents)[b]), inp.scale)
+        np.testing.assert_allclose(a[b].astype(np.float64), ref, rtol=2e-6, atol=2e-6)
+    # refusals: a sequence already invalid, a prefix past max_prefix_len, a block entry
+    # out of range inside [P, P + T); each leaves its sequence untouched
+    cache = _cache(inp)
+    table = cache.table.copy()
+    blk = (int(P[2]) + 3) // cache.block_size
+    table[2, blk] = -1
+    cache = O.Cache(**{**cache.__dict__, "table": table})
+    Pbad = P.copy()
+    Pbad[1] = inp.max_prefix_len + 1
+    k0 = cache.k.copy()
+    err = orc.kv_append(kt, vt, np.array([5, 0, 0], np.int32), cache, Pbad, inp.max_prefix_len)
+    assert err.tolist() == [5, 3, 3] and np.array_equal(cache.k, k0)
+
+
+def pin_incache_compaction(orc):
+    """Append then compaction leaves the cache rows [0, P + L) and the new prefix lengths
+    of delayed write-through, each row P + j holding tree row nodes[j] (numpy); a path
+    whose rows overlap their destinations, L = 0 and invalid requests behave as stated."""
+    inp = small_inputs("batched8k", 52, B=4, prefix=(20, 90), T=16, Hq=4, Hkv=2, D=32,
+                       draft_p=0.9)
+    w = inp.w
+    P = to_np(inp.prefix_len)
+    kt, vt = to_np(inp.k_tree), to_np(inp.v_tree)
+    parents = to_np(inp.parents)
+    _, _, err = orc.build_tree_mask(parents)
+    _, L, nodes, _ = orc.accept_longest_path(to_np(inp.logits), to_np(inp.draft), parents, err)
+    assert L.max() > 2
+    ca = _cache(inp)
+    orc.kv_append(kt, vt, err, ca, P, inp.max_prefix_len)
+    npl_a = orc.kv_compact(L, nodes, err, ca, P, inp.max_prefix_len, w.Hkv, w.T, w.D)
+    cb = _cache(inp)
+    npl_b = orc.kv_commit(kt, vt, L, nodes, err, cb, P, inp.max_prefix_len)
+    assert np.array_equal(npl_a, npl_b) and np.array_equal(npl_a, P + L)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            pos = np.arange(int(P[b] + L[b]))
+            for which, src in (("k", kt), ("v", vt)):
+                ra, rb = gather_at(ca, b, h, pos, which), gather_at(cb, b, h, pos, which)
+                assert np.array_equal(ra, rb)
+                for j in range(int(L[b])):
+                    assert np.array_equal(ra[P[b] + j], as_f64(src[b, h, nodes[b, j]], ca.dtype))
+    # a path whose sources are later destinations: nodes [0, 2, 3]
+    cc = _cache(inp)
+    orc.kv_append(kt, vt, None, cc, P, inp.max_prefix_len)
+    before = [gather_at(cc, 0, h, int(P[0]) + np.arange(w.T), "k") for h in range(w.Hkv)]
+    Lx = np.array([3, 0, 2, 2], np.int32)
+    nx = np.zeros((w.B, w.T), np.int32)
+    nx[0, :3] = [0, 2, 3]
+    nx[2, :2] = [0, w.T]            # a node index out of range: refused
+    nx[3, :2] = [0, 1]
+    ex = np.array([0, 0, 0, 4], np.int32)       # sequence 3 invalid
+    snap = [cc.k.copy(), cc.v.copy()]
+    npl = orc.kv_compact(Lx, nx, ex, cc, P, inp.max_prefix_len, w.Hkv, w.T, w.D)
+    assert npl.tolist() == [P[0] + 3, P[1], P[2], P[3]]
+    for h in range(w.Hkv):
+        after = gather_at(cc, 0, h, int(P[0]) + np.arange(w.T), "k")
+        assert np.array_equal(after[:3], before[h][[0, 2, 3]])
+        assert np.array_equal(after[3:], before[h][3:])
+    for b in (1, 2, 3):
+        for h in range(w.Hkv):
+            pos = np.arange(int(P[b]) + w.T)
+            cc_only = O.Cache(**{**cc.__dict__, "k": snap[0], "v": snap[1]})
+            assert np.array_equal(gather_at(cc, b, h, pos, "k"), gather_at(cc_only, b, h, pos, "k"))
+
 ALL_PINS = [
     pin_mask_worked_example, pin_mask_closed_forms, pin_mask_bruteforce, pin_mask_invalid,
     pin_attn_decode_T1, pin_attn_chain_causal, pin_attn_tree_vs_sdpa, pin_attn_prefix_zero,
@@ -1002,6 +1116,7 @@ ALL_PINS = [
     pin_rope_bf16_rounding,
     pin_topk_worked_examples, pin_topk_vs_library, pin_draft_tree_worked_example,
     pin_draft_tree_bruteforce, pin_draft_tree_structure,
+    pin_incache_append_and_attention, pin_incache_compaction,
     pin_commit_invariants, pin_commit_single_root, pin_commit_refusals,
     pin_commit_chain_equals_serial,
 ]

@@ -30,8 +30,8 @@ MUTANTS = [
     ("softmax_weight_dropped", "num[d] += w * elem(vsrc[k], dtype, voff[k] + d);",
      "num[d] += elem(vsrc[k], dtype, voff[k] + d);", 0),
     ("values_read_from_keys", "vsrc[n] = v_cache;", "vsrc[n] = k_cache;", 0),
-    ("tree_rows_from_head0", "const int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;",
-     "const int64_t off = (((int64_t)b * Hkv) * T + j) * D;", 0),
+    ("tree_rows_from_head0", "int64_t off = (((int64_t)b * Hkv + kvh) * T + j) * D;",
+     "int64_t off = (((int64_t)b * Hkv) * T + j) * D;", 0),
     ("argmax_ties_to_last", "best < 0 || x[v] > bv", "best < 0 || x[v] >= bv", 0),
     ("argmax_nan_not_skipped", "if (isnan(x[v])) continue;", "", 0),
     ("argmax_all_nan_minus_one", "return best < 0 ? 0 : (int32_t)best;",
@@ -89,6 +89,13 @@ MUTANTS = [
      "for (int r = 0; r < 1; ++r) {\n                    ckey", 0),
     ("draft_token_of_parent", "tk[n] = ctok[best];", "tk[n] = tk[cpar[best]];", 0),
     ("draft_cum_in_f32", "cm[n] = ckey[best];", "cm[n] = (float)ckey[best];", 0),
+    ("append_without_prefix_offset", "b, h, (int64_t)P + i);", "b, h, (int64_t)i);", 0),
+    ("append_hides_refusal", "tree_err[b] = 3;", "tree_err[b] = 0;", 0),
+    ("incache_tree_at_index", "num_blocks, b, kvh, P + j);", "num_blocks, b, kvh, j);", 0),
+    ("compact_reads_destination", "(int64_t)P + nodes[j]);", "(int64_t)P + j);", 0),
+    ("compact_length_short", "new_prefix_len[b] = ok ? P + L : P;",
+     "new_prefix_len[b] = ok ? P + L - 1 : P;", 1),
+    ("compact_ignores_tree_err", "int ok = !(tree_err && tree_err[b] != 0);", "int ok = 1;", 1),
     ("draft_prefers_last_parent", "if (!used[q] && (best < 0 || ckey[q] > ckey[best])) best = q;",
      "if (!used[q] && (best < 0 || ckey[q] > ckey[best] || (cpar[q] == last && cpar[best] != last))) best = q;", 0),
 ]
