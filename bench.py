@@ -262,6 +262,20 @@ def main():
     ms_step = ev[0].elapsed_time(ev[1]) / args.steps
     ms_attn = sum(a.elapsed_time(b) for a, b in ea) / args.steps
 
+    # the write-before-accept variant of the same step, timed the same way: the tree rows
+    # go into the cache first, the attention reads them there, the accepted path is
+    # compacted instead of committed
+    log(f"[bench] timing {args.steps} write-before-accept steps")
+    for _ in range(2):
+        st.run_in_cache()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        st.run_in_cache()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_step_in_cache = ev[0].elapsed_time(ev[1]) / args.steps
+
     # per-stage split (separate pass, one call type at a time); the sampled acceptance
     # (the alternative to the greedy accept stage) is timed here as well
     ua, us = wl.make_uniforms(w.B, w.T, args.seed)
@@ -285,6 +299,10 @@ def main():
                      ("accept_sampled", lambda: st.accept_sampled(ua, us, w.temperature)),
                      ("draft_tree", lambda: sv_draft_tree(d_logits, d_roots, d_k, d_levels,
                                                           d_par, d_tok, d_cum, d_ws)),
+                     # the write-before-accept variant (tree rows into the cache first,
+                     # attention reading them there, compaction instead of the commit)
+                     ("append", st.append), ("attention_in_cache", st.attention_in_cache),
+                     ("compact", st.compact),
                      ("rope", lambda: sv_rope_tree(st.q, st.k_tree, st.prefix_len, st.depth,
                                                    1e4))):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -326,6 +344,9 @@ def main():
         # sampled acceptance: one read of every logit row (the walk and the draw touch a
         # few more bytes per sequence, not counted)
         "accept_sampled_gbs": round(bytes_argmax / (stages["accept_sampled"] * 1e-6) / 1e9, 1),
+        # the whole step with the write-before-accept cache update (append, attention over
+        # the cache-resident tree, compaction) instead of delayed write-through
+        "ms_per_step_write_before_accept": round(ms_step_in_cache, 4),
         # draft tree: one read of the drafter rows that can be expanded (all but the last)
         "draft_tree_gbs": round(w.B * (w.T - 1) * w.V * 4 / (stages["draft_tree"] * 1e-6) / 1e9,
                                 1),

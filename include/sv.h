@@ -15,6 +15,10 @@
  *                                rotary embedding at base position + tree depth
  *   4. sv_kv_commit              copy only the accepted rows' K/V into the cache
  *
+ * Write-before-accept variant: sv_kv_append puts the tree's K/V rows into the cache
+ * before step 2, sv_tree_verify_attention then reads them there (NULL tree buffers),
+ * and sv_kv_compact replaces step 4.
+ *
  * Before the step, sv_draft_tree builds the draft tree itself from the drafter's
  * logits (top-K of each row's log-softmax, then EAGLE-2 global best-first
  * expansion); sv_topk_logprobs is its top-K on its own.
@@ -26,8 +30,10 @@
  *     E1 review gate (dtype and byte-length validation), E4a
  *     (build_tree_mask from the parent array, checked overflow; best-first tree
  *     expansion), E4b.5b (tree-position RoPE), E4b.10a (top-K extraction), E5a
- *     (tree-walk accept), E6 (zero-head guard before the GQA modulo), E6 v2
- *     (ancestors + self); section 4, Phases E1, E4 and E5.
+ *     (tree-walk accept), E5b (rollback to the accepted path), E6 (zero-head guard
+ *     before the GQA modulo; the per-layer block that appends the tree's K/V to the
+ *     cache before the attention), E6 v2 (ancestors + self); section 4, Phases E1,
+ *     E4 and E5.
  *   "Speculative-decoding heads: Medusa + EAGLE-2" (posttrainllm docs): "Why
  *     bother" (greedy longest-matching-prefix verification), "Mechanism
  *     comparison" (EAGLE-2's dynamic tree) and "What's not implemented" item 1
@@ -79,7 +85,12 @@ typedef enum sv_status {
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 /* Per-sequence tree status written by sv_build_tree_mask into tree_err[b]. */
-enum { SV_TREE_OK = 0, SV_TREE_BAD_ROOT = 1, SV_TREE_BAD_PARENT = 2 };
+enum {
+    SV_TREE_OK = 0,
+    SV_TREE_BAD_ROOT = 1,
+    SV_TREE_BAD_PARENT = 2,
+    SV_TREE_NOT_APPENDED = 3  /* sv_kv_append could not place the tree rows in the cache */
+};
 
 /*
  * KV cache descriptor: one layout for contiguous and paged caches.
@@ -148,7 +159,11 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  *           mask[b][i] set;  P_b = prefix_len[b] clamped into [0, max_prefix_len]
  *   out[b][i][h][:] = softmax(scale * q . k) weighted sum of the matching values
  *   q       [B][Hq][T][D]   dtype (SV_BF16, or SV_F32)
- *   k_tree, v_tree [B][Hkv][T][D]  the tree nodes' own K/V (not yet in the cache)
+ *   k_tree, v_tree [B][Hkv][T][D]  the tree nodes' own K/V (not yet in the cache),
+ *           or both NULL when the tree rows are already in the cache (sv_kv_append):
+ *           tree row j is then the cache row at position P_b + j (a row whose
+ *           block-table entry is out of range is read from block 0 instead: its
+ *           sequence was refused by sv_kv_append and marked in tree_err)
  *   cache   prefix K/V; cache->dtype must equal the Q/K/V dtype
  *   prefix_len int32 [B] device; max_prefix_len host upper bound of prefix_len
  *   mask    from sv_build_tree_mask
@@ -277,6 +292,52 @@ int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t
                  double theta, hipStream_t stream);
 
 /*
+ * Write-before-accept variant, step 1: the tree's K/V rows into the cache.
+ * Defined by: ADR-037 Phase status row E6, per-layer tree-verify block (K/V
+ * appended at [prefix_len, prefix_len + tree_seq_len) before the tree attention,
+ * which then reads them from the cache); llms-explorer page Facts on KV
+ * write-before-accept (the trade-off against delayed write-through).
+ *
+ * For every sequence b with tree_err[b] == 0: if prefix_len[b] lies in
+ * [0, max_prefix_len] and every position of [P, P + T) has a block-table entry in
+ * [0, num_blocks), tree row i of every kv head is copied to position P + i (byte
+ * copy); otherwise nothing is written and tree_err[b] becomes
+ * SV_TREE_NOT_APPENDED.  Sequences with tree_err[b] != 0 on entry are skipped.
+ *   k_tree, v_tree [B][Hkv][T][D] (16-byte aligned), cache dtype
+ *   tree_err int32 [B], read and updated (e.g. sv_build_tree_mask's output)
+ * Then call sv_tree_verify_attention with k_tree = v_tree = NULL, accept as usual,
+ * and sv_kv_compact instead of sv_kv_commit.
+ * Errors: as sv_kv_commit (tree_err is required here).
+ */
+int sv_kv_append(const void *k_tree, const void *v_tree, int32_t *tree_err,
+                 const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                 int32_t B, int32_t Hkv, int32_t T, int32_t D, hipStream_t stream);
+
+/*
+ * Write-before-accept variant, last step: compact the accepted path over the
+ * appended rows.
+ * Defined by: ADR-037 section 4 Phase E5 and Phase status row E5b (after the
+ * acceptance the cache is rolled back to the accepted path).
+ *
+ * For every sequence b with tree_err[b] == 0 (or tree_err NULL), L =
+ * accepted_len[b] in [0, T], accepted_nodes[b][j] in [0, T) for j < L, prefix_len[b]
+ * in [0, max_prefix_len] and every position of [P, P + T) with a block-table entry
+ * in range: the cache row at P + j becomes the row that was at
+ * P + accepted_nodes[b][j], for j < L and every kv head (all moving rows are read
+ * before any is written), and new_prefix_len[b] = P + L.  Otherwise nothing moves
+ * and new_prefix_len[b] = P.  Rows from P + L on keep what they held.  With the
+ * rows appended by sv_kv_append this leaves the same cache rows [0, P + L) and
+ * prefix lengths as sv_kv_commit.  new_prefix_len may be NULL, or may alias
+ * prefix_len.
+ * Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_GQA, SV_ERR_TREE_SIZE, SV_ERR_HEAD_DIM,
+ * SV_ERR_DTYPE, SV_ERR_CAPACITY, SV_ERR_ALIGN, SV_ERR_OVERFLOW, SV_ERR_HIP.
+ */
+int sv_kv_compact(const int32_t *accepted_len, const int32_t *accepted_nodes,
+                  const int32_t *tree_err, const sv_kv_cache *cache, const int32_t *prefix_len,
+                  int32_t max_prefix_len, int32_t *new_prefix_len, int32_t B, int32_t Hkv,
+                  int32_t T, int32_t D, hipStream_t stream);
+
+/*
  * Top-K of the log-softmax of each row.
  * Defined by: ADR-037 Phase status row E4b.10a (log_softmax of the row, the K
  * largest log-probabilities, the smaller token winning ties, the choice made on
@@ -294,6 +355,7 @@ int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t
  * Errors: SV_ERR_NULL, SV_ERR_SHAPE (R < 0, V < 1, K out of range),
  * SV_ERR_OVERFLOW (V or R above INT_MAX), SV_ERR_ALIGN, SV_ERR_HIP.
  */
+
 int sv_topk_logprobs(const float *logits, int64_t R, int64_t V, int32_t K, int32_t *top_tokens,
                      double *top_logp, hipStream_t stream);
 

@@ -59,9 +59,9 @@ def cache(**kw):
 
 
 def attn(lib, c=None, q=FAKE, B=2, Hq=8, Hkv=2, T=8, D=256, maxp=100, ws=FAKE, wsb=1 << 30,
-         splits=0, out=FAKE, null_cache=False, scale=0.0625):
+         splits=0, out=FAKE, null_cache=False, scale=0.0625, kt=FAKE, vt=FAKE):
     c = c or cache()
-    return lib.sv_tree_verify_attention(q, FAKE, FAKE, None if null_cache else ctypes.byref(c),
+    return lib.sv_tree_verify_attention(q, kt, vt, None if null_cache else ctypes.byref(c),
                                         FAKE, maxp, FAKE, B, Hq, Hkv, T, D, scale, out, ws, wsb,
                                         splits, None)
 
@@ -90,6 +90,10 @@ def test_attention_validation(lib):
     assert attn(lib, c=cache(num_blocks=1 << 62, block_stride=1 << 20)) == -8
     assert attn(lib, scale=0.0) == -2 and attn(lib, scale=-1.0) == -2
     assert attn(lib, scale=float("inf")) == -2 and attn(lib, scale=float("nan")) == -2
+    # tree rows in the cache: both tree buffers NULL, never just one
+    assert attn(lib, kt=None) == -1 and attn(lib, vt=None) == -1
+    assert attn(lib, kt=None, vt=None, ws=None) == -9      # both NULL passes the NULL check
+    assert attn(lib, kt=FAKE + 8) == -11
 
 
 def test_attention_workspace_size(lib):
@@ -205,3 +209,22 @@ def test_draft_tree_validation(lib):
     ws = sv.sv_draft_tree_workspace_size
     assert ws(2, 8, 4) == 512 + 256     # [2][7][4] fp64 log-probs, then int32 tokens
     assert ws(2, 1, 4) == 0 and ws(-1, 8, 4) == 0 and ws(2, 65, 4) == 0 and ws(2, 8, 65) == 0
+
+
+def test_append_compact_validation(lib):
+    fa, fc = lib.sv_kv_append, lib.sv_kv_compact
+    def app(c=None, Hkv=2, T=8, D=256, maxp=100, kt=FAKE, err=FAKE, B=2):
+        c = c or cache()
+        return fa(kt, FAKE, err, ctypes.byref(c), FAKE, maxp, B, Hkv, T, D, None)
+    def cmp(c=None, Hkv=2, T=8, D=256, maxp=100, L=FAKE, B=2):
+        c = c or cache()
+        return fc(L, FAKE, None, ctypes.byref(c), FAKE, maxp, None, B, Hkv, T, D, None)
+    assert fa(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 2, 8, 256, None) == -1
+    assert fc(FAKE, FAKE, None, None, FAKE, 1, None, 2, 2, 8, 256, None) == -1
+    for f in (app, cmp):
+        assert f(Hkv=0) == -4 and f(T=0) == -6 and f(T=65) == -6 and f(D=100) == -5
+        assert f(c=cache(dtype=3)) == -3 and f(maxp=153) == -7 and f(maxp=-1) == -2
+        assert f(B=-1) == -2 and f(B=0) == 0
+        assert f(c=cache(k=FAKE + 8)) == -11
+    assert app(kt=FAKE + 2) == -11 and app(kt=None) == -1 and app(err=None) == -1
+    assert cmp(L=None) == -1

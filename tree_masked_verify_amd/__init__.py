@@ -25,7 +25,8 @@ ENTRY_POINTS = ("sv_build_tree_mask", "sv_tree_verify_attention_workspace_size",
                 "sv_tree_verify_attention", "sv_accept_longest_path_workspace_size",
                 "sv_accept_longest_path", "sv_accept_sampled_workspace_size",
                 "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs",
-                "sv_draft_tree_workspace_size", "sv_draft_tree", "sv_kv_commit",
+                "sv_draft_tree_workspace_size", "sv_draft_tree", "sv_kv_append",
+                "sv_kv_compact", "sv_kv_commit",
                 "sv_status_string")
 
 
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, sz, vp]
     lib.sv_rope_tree.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_double,
                                  vp]
+    lib.sv_kv_append.argtypes = [vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, i32, i32, i32,
+                                 i32, vp]
+    lib.sv_kv_compact.argtypes = [vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp, i32, i32,
+                                  i32, i32, vp]
     lib.sv_topk_logprobs.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.sv_draft_tree_workspace_size.argtypes = [i32, i32, i32]
     lib.sv_draft_tree_workspace_size.restype = sz
@@ -82,7 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sv_status_string.restype = ctypes.c_char_p
     for f in ("sv_build_tree_mask", "sv_tree_verify_attention", "sv_accept_longest_path",
               "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs", "sv_draft_tree",
-              "sv_kv_commit"):
+              "sv_kv_append", "sv_kv_compact", "sv_kv_commit"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -141,9 +146,12 @@ def sv_tree_verify_attention_workspace_size(B, Hq, Hkv, T, D, max_prefix_len, dt
 
 
 def sv_tree_verify_attention(q, k_tree, v_tree, cache: sv_kv_cache, prefix_len, max_prefix_len,
-                             mask, scale, out, workspace, num_splits=0, stream=None) -> None:
+                             mask, scale, out, workspace, num_splits=0, stream=None,
+                             Hkv=None) -> None:
+    """k_tree = v_tree = None: the tree rows are read from the cache at P + j (then Hkv
+    must be given)."""
     B, Hq, T, D = q.shape
-    Hkv = k_tree.shape[1]
+    Hkv = k_tree.shape[1] if k_tree is not None else int(Hkv)
     rc = load_library().sv_tree_verify_attention(
         _ptr(q), _ptr(k_tree), _ptr(v_tree), ctypes.byref(cache), _ptr(prefix_len),
         int(max_prefix_len), _ptr(mask), B, Hq, Hkv, T, D, float(scale), _ptr(out),
@@ -190,6 +198,25 @@ def sv_rope_tree(q, k_tree, prefix_len, depth, theta, stream=None) -> None:
     rc = load_library().sv_rope_tree(_ptr(q), _ptr(k_tree), _ptr(prefix_len), _ptr(depth), B, Hq,
                                      Hkv, T, D, dtype_code(q), float(theta), _stream(stream))
     _check("sv_rope_tree", rc)
+
+
+def sv_kv_append(k_tree, v_tree, tree_err, cache: sv_kv_cache, prefix_len, max_prefix_len,
+                 stream=None) -> None:
+    B, Hkv, T, D = k_tree.shape
+    rc = load_library().sv_kv_append(_ptr(k_tree), _ptr(v_tree), _ptr(tree_err),
+                                     ctypes.byref(cache), _ptr(prefix_len), int(max_prefix_len),
+                                     B, Hkv, T, D, _stream(stream))
+    _check("sv_kv_append", rc)
+
+
+def sv_kv_compact(accepted_len, accepted_nodes, tree_err, cache: sv_kv_cache, prefix_len,
+                  max_prefix_len, new_prefix_len, Hkv, D, stream=None) -> None:
+    B, T = accepted_nodes.shape
+    rc = load_library().sv_kv_compact(_ptr(accepted_len), _ptr(accepted_nodes), _ptr(tree_err),
+                                      ctypes.byref(cache), _ptr(prefix_len), int(max_prefix_len),
+                                      _ptr(new_prefix_len), B, int(Hkv), T, int(D),
+                                      _stream(stream))
+    _check("sv_kv_compact", rc)
 
 
 def sv_topk_logprobs(logits, K, top_tokens, top_logp, stream=None) -> None:

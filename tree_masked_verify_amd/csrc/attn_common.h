@@ -31,6 +31,20 @@ struct MfmaParams {
     float *ws_ml;
 };
 
+// Tree rows kept in the cache (no tree buffers given): byte address of tree row r of
+// sequence b, kv head kvh, at cache position P + r of a bf16 pool (plus the lane's byte
+// offset already added to `pool`).  An out-of-range block-table entry reads block 0
+// instead: the rows were then never appended, and the sequence is marked invalid.
+__device__ __forceinline__ const unsigned char *tree_row_in_cache(const unsigned char *pool,
+                                                                  const MfmaParams &p, int b,
+                                                                  int kvh, int P, int r) {
+    const int pos = P + r;
+    int32_t blk = p.table[(int64_t)b * p.max_blocks + pos / p.bs];
+    blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
+    return pool + ((int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
+                   (int64_t)(pos % p.bs) * p.rstride) * 2;
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 

@@ -112,24 +112,36 @@ __device__ __forceinline__ TileLoad prepare_prefix(const MfmaParams &p, int kvh,
 }
 
 // Issues the whole tile; the returned descriptor re-reads the last node (for repeat
-// slots).
-template <int D>
-__device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int k0,
-                                               uint32_t stage) {
+// slots).  kInCache: the tree rows sit in the cache at positions P + r instead of in the
+// tree buffers.
+template <int D, bool kInCache>
+__device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int P,
+                                               int k0, uint32_t stage) {
     using Cf = MCfg<D>;
     const int w = uni(threadIdx.x >> 6);
     const int tensor = w >> 2;
     const int q = w & 3;
-    const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
-                                ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + load_lane_piece<D>() * 16;
     const int row = k0 + (D == 256 ? 4 * q + 16 * load_lane_half<D>(q) : 8 * q);
     TileLoad t;
     t.ustride = tensor ? Cf::VU : Cf::KU;
     t.lds = stage + (tensor ? Cf::KTILE : 0) + q * Cf::NI * t.ustride;
+    if constexpr (kInCache) {
+        const unsigned char *pool = reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
+                                    load_lane_piece<D>() * 16;
 #pragma unroll
-    for (int j = 0; j < Cf::NI; ++j)
-        dma16(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
-    t.src = base + (int64_t)(p.T - 1) * (D * 2);
+        for (int j = 0; j < Cf::NI; ++j)
+            dma16(tree_row_in_cache(pool, p, b, kvh, P, min(row + j, p.T - 1)),
+                  t.lds + j * t.ustride);
+        t.src = tree_row_in_cache(pool, p, b, kvh, P, p.T - 1);
+    } else {
+        const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
+                                    ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) +
+                                    load_lane_piece<D>() * 16;
+#pragma unroll
+        for (int j = 0; j < Cf::NI; ++j)
+            dma16(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
+        t.src = base + (int64_t)(p.T - 1) * (D * 2);
+    }
     t.step = 0;
     t.spread = false;
     return t;
@@ -295,7 +307,7 @@ __device__ __forceinline__ void tile_pv(const unsigned char *vs, int dpart,
     }
 }
 
-template <int D>
+template <int D, bool kInCache>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
     using Cf = MCfg<D>;
     static_assert(Cf::NST == 2 || Cf::NST == 4, "ring depth");
@@ -402,7 +414,7 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
             cissue = cursor_add(cissue, kKeyTile, p.bs);
             if (k + 1 < ntp) tbn = lookup_blocks(p, b, bl, cissue, start + (k + 1) * kKeyTile, end);
         } else if (k < nt) {
-            tl = issue_tree<D>(p, b, kvh, (k - ntp) * kKeyTile, stage);
+            tl = issue_tree<D, kInCache>(p, b, kvh, P, (k - ntp) * kKeyTile, stage);
         } else {
             tl.lds = stage + (tl.lds - smem0) % Cf::STAGE_BYTES;
             tl.spread = true;
@@ -511,7 +523,8 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
 template <int D>
 hipError_t launch_d(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     using Cf = MCfg<D>;
-    hipError_t e = hipFuncSetAttribute((const void *)attn_mfma_kernel<D>,
+    const auto kernel = a.k_tree ? attn_mfma_kernel<D, false> : attn_mfma_kernel<D, true>;
+    hipError_t e = hipFuncSetAttribute((const void *)kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cf::SMEM);
     if (e != hipSuccess) return e;
     MfmaParams p;
@@ -544,7 +557,7 @@ hipError_t launch_d(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
     const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
-    hipLaunchKernelGGL(attn_mfma_kernel<D>, dim3(grid), dim3(64 * kWaves), Cf::SMEM, stream, p);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kWaves), Cf::SMEM, stream, p);
     return hipGetLastError();
 }
 

@@ -95,26 +95,38 @@ __device__ __forceinline__ void load_unit_d(const TileLoad &t, int j) {
 }
 
 // Issues the whole tree tile (rows past the last node read the last node, masked); the
-// returned descriptor re-reads the last node (for repeat slots).
-template <int D>
-__device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int k0,
-                                               uint32_t stage) {
+// returned descriptor re-reads the last node (for repeat slots).  kInCache: the tree rows
+// sit in the cache at positions P + r instead of in the tree buffers.
+template <int D, bool kInCache>
+__device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int kvh, int P,
+                                               int k0, uint32_t stage) {
     using G = Geo<D>;
     const int w = uni(threadIdx.x >> 6);
     const int tensor = w >> 1;
     const int q = w & 1;
     const int lane = threadIdx.x & 63;
     const int half = (lane / G::LPK) & 1;
-    const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
-                                ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + (lane % G::LPK) * 16;
     const int row = k0 + 8 * q + 16 * half;
     TileLoad t;
     t.ustride = tensor ? G::VU : G::KU;
     t.lds = stage + (tensor ? G::KTILE : 0) + q * NI * t.ustride;
+    if constexpr (kInCache) {
+        const unsigned char *pool =
+            reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) + (lane % G::LPK) * 16;
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
-        unit_load<D>(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
-    t.src = base + (int64_t)(p.T - 1) * (D * 2);
+        for (int j = 0; j < NI; ++j)
+            unit_load<D>(tree_row_in_cache(pool, p, b, kvh, P, min(row + j, p.T - 1)),
+                         t.lds + j * t.ustride);
+        t.src = tree_row_in_cache(pool, p, b, kvh, P, p.T - 1);
+    } else {
+        const unsigned char *base =
+            reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
+            ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + (lane % G::LPK) * 16;
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            unit_load<D>(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
+        t.src = base + (int64_t)(p.T - 1) * (D * 2);
+    }
     t.step = 0;
     t.spread = false;
     return t;
@@ -362,7 +374,7 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[2][Geo<D>::DB], const RowSta
     }
 }
 
-template <int D>
+template <int D, bool kInCache>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_w4_kernel(MfmaParams p) {
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -531,7 +543,7 @@ void attn_w4_kernel(MfmaParams p) {
             tl.lds = stage + lds_w;
             tl.spread = true;
         } else if (k < nt) {
-            tl = issue_tree<D>(p, b, kvh, (k - ntp) * kKeyTile, stage);
+            tl = issue_tree<D, kInCache>(p, b, kvh, P, (k - ntp) * kKeyTile, stage);
         } else {
             tl.lds = stage + lds_w;
             tl.spread = true;
@@ -674,7 +686,8 @@ template <int D>
 hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     using namespace w4;
     constexpr int SMEM = Geo<D>::SMEM;
-    hipError_t e = hipFuncSetAttribute((const void *)attn_w4_kernel<D>,
+    const auto kernel = a.k_tree ? attn_w4_kernel<D, false> : attn_w4_kernel<D, true>;
+    hipError_t e = hipFuncSetAttribute((const void *)kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;
     MfmaParams p;
@@ -707,7 +720,7 @@ hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) 
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
     const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
-    hipLaunchKernelGGL(attn_w4_kernel<D>, dim3(grid), dim3(64 * kW), SMEM, stream, p);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kW), SMEM, stream, p);
     return hipGetLastError();
 }
 }  // namespace

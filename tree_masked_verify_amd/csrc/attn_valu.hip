@@ -108,8 +108,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
                 float kv = 0.0f, vv = 0.0f;
                 if (pos < hi) {
                     int64_t off = -1;
-                    if (tree) {
+                    if (tree && p.kt) {
                         off = (((int64_t)b * p.Hkv + kvh) * p.T + pos) * D;
+                    } else if (tree) {
+                        // tree rows kept in the cache at P + pos (an out-of-range block
+                        // entry reads block 0: such rows were never appended)
+                        const int cpos = P + pos;
+                        int32_t blk = p.table[(int64_t)b * p.max_blocks + cpos / p.bs];
+                        blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
+                        off = (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
+                              (int64_t)(cpos % p.bs) * p.rstride;
                     } else {
                         const int32_t blk = p.table[(int64_t)b * p.max_blocks + pos / p.bs];
                         if (blk >= 0 && blk < p.num_blocks)
@@ -117,8 +125,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
                                   (int64_t)(pos % p.bs) * p.rstride;
                     }
                     if (off >= 0) {
-                        kv = ld<kBF16>(tree ? p.kt : p.kc, off + d);
-                        vv = ld<kBF16>(tree ? p.vt : p.vc, off + d);
+                        kv = ld<kBF16>(tree && p.kt ? p.kt : p.kc, off + d);
+                        vv = ld<kBF16>(tree && p.kt ? p.vt : p.vc, off + d);
                     }
                 }
                 ks[kk * (D + 1) + d] = kv;

@@ -175,7 +175,8 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
     int rc = make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, &plan);
     if (rc != SV_OK) return rc;
     if (B == 0) return SV_OK;
-    if (!q || !k_tree || !v_tree || !prefix_len || !mask || !out || !cache->k || !cache->v ||
+    // k_tree and v_tree both NULL: the tree rows are read from the cache at P + i
+    if (!q || (!k_tree != !v_tree) || !prefix_len || !mask || !out || !cache->k || !cache->v ||
         !cache->block_table)
         return SV_ERR_NULL;
     rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
@@ -285,6 +286,58 @@ int sv_rope_tree(void *q, void *k_tree, const int32_t *prefix_len, const int32_t
         return SV_ERR_ALIGN;
     return hip_status(launch_rope_tree(q, k_tree, prefix_len, depth, B, Hq, Hkv, T, D, dtype,
                                        theta, stream));
+}
+
+int sv_kv_append(const void *k_tree, const void *v_tree, int32_t *tree_err,
+                 const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                 int32_t B, int32_t Hkv, int32_t T, int32_t D, hipStream_t stream) {
+    if (!cache) return SV_ERR_NULL;
+    if (B < 0 || max_prefix_len < 0) return SV_ERR_SHAPE;
+    if (Hkv <= 0) return SV_ERR_GQA;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (D != 128 && D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    const int dtype = cache->dtype;
+    const int es = esize_of(dtype);
+    if (es == 0) return SV_ERR_DTYPE;
+    int64_t tmp;
+    if (!prod_ok({(int64_t)B, Hkv, T, D, es}, &tmp)) return SV_ERR_OVERFLOW;
+    if ((int64_t)max_prefix_len + T > INT_MAX) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!k_tree || !v_tree || !tree_err || !prefix_len || !cache->k || !cache->v ||
+        !cache->block_table)
+        return SV_ERR_NULL;
+    int rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
+    if (rc != SV_OK) return rc;
+    if (!aligned16(k_tree) || !aligned16(v_tree)) return SV_ERR_ALIGN;
+    return hip_status(launch_kv_append(k_tree, v_tree, tree_err, cache->k, cache->v,
+                                       view_of(cache), prefix_len, max_prefix_len, B, Hkv, T, D,
+                                       es, stream));
+}
+
+int sv_kv_compact(const int32_t *accepted_len, const int32_t *accepted_nodes,
+                  const int32_t *tree_err, const sv_kv_cache *cache, const int32_t *prefix_len,
+                  int32_t max_prefix_len, int32_t *new_prefix_len, int32_t B, int32_t Hkv,
+                  int32_t T, int32_t D, hipStream_t stream) {
+    if (!cache) return SV_ERR_NULL;
+    if (B < 0 || max_prefix_len < 0) return SV_ERR_SHAPE;
+    if (Hkv <= 0) return SV_ERR_GQA;
+    if (T < 1 || T > 64) return SV_ERR_TREE_SIZE;
+    if (D != 128 && D != 256 && D != 512) return SV_ERR_HEAD_DIM;
+    const int dtype = cache->dtype;
+    const int es = esize_of(dtype);
+    if (es == 0) return SV_ERR_DTYPE;
+    int64_t tmp;
+    if (!prod_ok({(int64_t)B, Hkv, T, D, es}, &tmp)) return SV_ERR_OVERFLOW;
+    if ((int64_t)max_prefix_len + T > INT_MAX) return SV_ERR_OVERFLOW;
+    if (B == 0) return SV_OK;
+    if (!accepted_len || !accepted_nodes || !prefix_len || !cache->k || !cache->v ||
+        !cache->block_table)
+        return SV_ERR_NULL;
+    int rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
+    if (rc != SV_OK) return rc;
+    return hip_status(launch_kv_compact(accepted_len, accepted_nodes, tree_err, cache->k, cache->v,
+                                        view_of(cache), prefix_len, max_prefix_len,
+                                        new_prefix_len, B, Hkv, T, D, es, stream));
 }
 
 int sv_topk_logprobs(const float *logits, int64_t R, int64_t V, int32_t K, int32_t *top_tokens,

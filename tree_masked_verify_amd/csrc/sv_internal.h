@@ -114,6 +114,18 @@ hipError_t launch_best_first(const int32_t *top_tok, const double *top_logp,
                              const int32_t *root_token, int B, int T, int K, int max_levels,
                              int32_t *parents, int32_t *tokens, double *cum, hipStream_t stream);
 
+// The write-before-accept variant: tree rows into the cache at [P, P + T), then the
+// accepted path compacted to [P, P + L).
+hipError_t launch_kv_append(const void *k_tree, const void *v_tree, int32_t *tree_err,
+                            void *k_cache, void *v_cache, const CacheView &c,
+                            const int32_t *prefix_len, int32_t max_prefix_len, int B, int Hkv,
+                            int T, int D, int esize, hipStream_t stream);
+hipError_t launch_kv_compact(const int32_t *accepted_len, const int32_t *accepted_nodes,
+                             const int32_t *tree_err, void *k_cache, void *v_cache,
+                             const CacheView &c, const int32_t *prefix_len,
+                             int32_t max_prefix_len, int32_t *new_prefix_len, int B, int Hkv,
+                             int T, int D, int esize, hipStream_t stream);
+
 hipError_t launch_kv_commit(const void *k_tree, const void *v_tree, const int32_t *accepted_len,
                             const int32_t *accepted_nodes, const int32_t *tree_err,
                             void *k_cache, void *v_cache, const CacheView &c,

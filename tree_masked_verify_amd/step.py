@@ -4,6 +4,8 @@ Allocation (outputs, workspaces) happens once in the constructor through torch; 
 only enqueues sv_build_tree_mask -> sv_tree_verify_attention ->
 sv_accept_longest_path -> sv_kv_commit on one stream.  accept_sampled() enqueues the
 sampled acceptance instead of the greedy one (same outputs, which commit() reads).
+run_in_cache() is the write-before-accept variant: sv_kv_append puts the tree rows into the
+cache first, the attention reads them there, and sv_kv_compact replaces the commit.
 """
 from __future__ import annotations
 
@@ -11,8 +13,9 @@ import torch
 
 from . import (dtype_code, make_cache, sv_accept_longest_path,
                sv_accept_longest_path_workspace_size, sv_accept_sampled,
-               sv_accept_sampled_workspace_size, sv_build_tree_mask, sv_kv_commit,
-               sv_tree_verify_attention, sv_tree_verify_attention_workspace_size, workspace)
+               sv_accept_sampled_workspace_size, sv_build_tree_mask, sv_kv_append,
+               sv_kv_commit, sv_kv_compact, sv_tree_verify_attention,
+               sv_tree_verify_attention_workspace_size, workspace)
 
 
 class VerifyStep:
@@ -78,3 +81,26 @@ class VerifyStep:
         self.attention(stream)
         self.accept(stream)
         self.commit(stream)
+
+    # ---- write-before-accept variant
+    def append(self, stream=None):
+        sv_kv_append(self.k_tree, self.v_tree, self.tree_err, self.cache, self.prefix_len,
+                     self.max_prefix_len, stream)
+
+    def attention_in_cache(self, stream=None):
+        sv_tree_verify_attention(self.q, None, None, self.cache, self.prefix_len,
+                                 self.max_prefix_len, self.mask, self.scale, self.out,
+                                 self.attn_ws, self.num_splits, stream,
+                                 Hkv=self.k_tree.shape[1])
+
+    def compact(self, stream=None):
+        sv_kv_compact(self.accepted_len, self.accepted_nodes, self.tree_err, self.cache,
+                      self.prefix_len, self.max_prefix_len, self.new_prefix_len,
+                      self.k_tree.shape[1], self.k_tree.shape[3], stream)
+
+    def run_in_cache(self, stream=None):
+        self.build_mask(stream)
+        self.append(stream)
+        self.attention_in_cache(stream)
+        self.accept(stream)
+        self.compact(stream)
