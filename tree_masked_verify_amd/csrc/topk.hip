@@ -60,13 +60,36 @@ __device__ __forceinline__ double exp_core(double d, const double *tab) {
 }
 
 // exp(x - m) for a raw logit x and a lane max m >= every finite x seen: NaN and -inf give
-// ~1e-304 (d clamped at -700), +inf gives 1 (it counts as the largest finite float, which
-// then is m).  Those tiny terms are below the last bit of any sum that holds a finite entry
-// (such a sum is >= 1).
+// 0, +inf gives 1 (it counts as the largest finite float, which then is m).
 __device__ __forceinline__ double exp_term(float x, double md, const double *tab) {
     double d = (double)x - md;
     d = fmin(fmax(d, -700.0), 0.0);                    // fmax(NaN, -700) = -700
-    return exp_core(d, tab);
+    return x > -__builtin_huge_valf() ? exp_core(d, tab) : 0.0;
+}
+
+// e^x in fp64 for a logit with |x| < 64, from its fp32 value: n = round(512 x) by the
+// 1.5 * 2^23 rounding trick in fp32, after which r = x - n/512 is exact in fp32 with
+// |r| <= 2^-10; with n = 128 k + j, e^x = e^(k/4) * e^(j/512) * e^r, the first two factors
+// from tables (t1[k + 256], k in [-256, 256]; t2[j], j < 128) and e^r - 1 its Taylor
+// polynomial of degree 4 (remainder below 2^-56 relative).  Same table-driven method as
+// exp_core, with no reduction step and no reference maximum.
+__device__ __forceinline__ double exp_small(float x, const double *t1, const double *t2) {
+    constexpr float kMagic = 12582912.0f;              // 1.5 * 2^23
+    const float t = fmaf(x, 512.0f, kMagic);
+    const float rf = fmaf(t - kMagic, -1.0f / 512.0f, x);
+    const int n = __float_as_int(t) - 0x4B400000;
+    const double T = t1[(n >> 7) + 256] * t2[n & 127];
+    const double r = (double)rf;
+    double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+    q = fma(q, r, 0.5);
+    return fma(T, fma(r * r, q, r), T);
+}
+
+// Whether all four logits are finite with |x| < 64 (the range of exp_small).
+__device__ __forceinline__ bool small_piece(const f32x4 &x) {
+    const uint32_t a = max(max(__float_as_uint(x[0]) & 0x7fffffffu, __float_as_uint(x[1]) & 0x7fffffffu),
+                           max(__float_as_uint(x[2]) & 0x7fffffffu, __float_as_uint(x[3]) & 0x7fffffffu));
+    return a < 0x42800000u;                            // 64.0f; NaN and inf are above
 }
 
 // A logit as the rule reads it: NaN and -inf give -inf, +inf the largest finite float, and
@@ -106,14 +129,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     return x;
 }
 
-// Keeps the best min(n, K) of entries [0, n) (n <= kCap) of a wavefront's (value, index)
-// arrays in slots [0, min(n, K)), best first, and returns that count.  Entries with index -1
-// are empty.  Every lane reads its entries before any slot is written.
-__device__ int keep_best(float *cv, int32_t *ci, int n, int K, int lane) {
-    constexpr int kPer = kCap / 64;
-    uint64_t key[kPer];
+// Keeps the best min(n, K) of entries [0, n) (n <= 64 * kSlots) of a wavefront's (value,
+// index) arrays in slots [0, min(n, K)), best first, and returns that count.  Entries with
+// index -1 are empty.  Every lane reads its entries before any slot is written.
+template <int kSlots>
+__device__ int keep_best_n(float *cv, int32_t *ci, int n, int K, int lane) {
+    uint64_t key[kSlots];
 #pragma unroll
-    for (int s = 0; s < kPer; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
         const int q = s * 64 + lane;
         key[s] = q < n ? cand_key(cv[q], ci[q]) : 0;
     }
@@ -122,10 +145,10 @@ __device__ int keep_best(float *cv, int32_t *ci, int n, int K, int lane) {
     for (int r = 0; r < m; ++r) {
         uint64_t best = key[0];
 #pragma unroll
-        for (int s = 1; s < kPer; ++s) best = key[s] > best ? key[s] : best;
+        for (int s = 1; s < kSlots; ++s) best = key[s] > best ? key[s] : best;
         const uint64_t w = wave_max_u64(best);
 #pragma unroll
-        for (int s = 0; s < kPer; ++s) key[s] = key[s] == w ? 0 : key[s];
+        for (int s = 0; s < kSlots; ++s) key[s] = key[s] == w ? 0 : key[s];
         mine = lane == r ? w : mine;
     }
     if (lane < m) {
@@ -133,6 +156,13 @@ __device__ int keep_best(float *cv, int32_t *ci, int n, int K, int lane) {
         ci[lane] = mine ? key_index(mine) : -1;
     }
     return m;
+}
+
+// keep_best_n with as few slots per lane as n needs (n <= kCap).
+__device__ int keep_best(float *cv, int32_t *ci, int n, int K, int lane) {
+    if (n <= 64) return keep_best_n<1>(cv, ci, n, K, lane);
+    if (n <= 256) return keep_best_n<4>(cv, ci, n, K, lane);
+    return keep_best_n<kCap / 64>(cv, ci, n, K, lane);
 }
 
 struct WaveCands {
@@ -144,7 +174,9 @@ struct WaveCands {
 
 // One piece: up to four consecutive raw logits per lane (the first `nok` exist), all with
 // larger indices than every entry already in the buffer, mx = max4 of them.  They are
-// judged against the buffer as it stood before the piece.
+// judged against the buffer as it stood before the piece.  Once the buffer holds K + 24
+// entries it is cut back to K, so the threshold follows the running K-th best closely
+// (each cut is K rounds of a 64-lane max over one slot per lane).
 __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float mx, int nok,
                                             int32_t idx0, int K, int lane) {
     bool full = wc.cnt >= K;
@@ -172,16 +204,32 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float
         }
     }
     wc.cnt = cnt;
+    if (cnt >= K + 24) {
+        wc.cnt = keep_best(wc.cv, wc.ci, cnt, K, lane);
+        wc.tau = wc.cv[K - 1];
+    }
 }
 
+// The lane's share of sum_y exp(l(y)) in two parts: pieces whose logits all have |x| < 64
+// add exp(x) directly (sf); any other piece goes, whole, to an online max m and a sum s of
+// exp(x - m) (NaN and -inf add 0, +inf counts as the largest finite float).
 struct RowSum {
-    float m;     // running max of the lane's logits as read (-FLT_MAX before the first)
+    double sf;   // sum of exp(x) over the small pieces
+    float m;     // running max over the other pieces (-FLT_MAX before the first)
     double md;   // m as a double
-    double s;    // sum of exp(l - m) over them (plus ~1e-304 per NaN / -inf entry)
+    double s;    // sum of exp(x - m) over the other pieces
 };
 
-// Adds a piece to the lane's online max and sum (entries beyond those that exist are -inf).
-__device__ __forceinline__ void sum_piece(RowSum &a, const f32x4 &x, float mx, const double *tab) {
+// Adds a piece to the lane's sums (entries beyond those that exist are -inf).  Whether it
+// takes the small-piece path is decided for the whole wavefront.
+__device__ __forceinline__ void sum_piece(RowSum &a, const f32x4 &x, float mx, const double *tab,
+                                          const double *t1, const double *t2) {
+    if (__all(small_piece(x))) {
+        const double e0 = exp_small(x[0], t1, t2), e1 = exp_small(x[1], t1, t2);
+        const double e2 = exp_small(x[2], t1, t2), e3 = exp_small(x[3], t1, t2);
+        a.sf += (e0 + e1) + (e2 + e3);
+        return;
+    }
     if (mx > a.m) {
         const double mxd = (double)mx;
         a.s *= exp_core(fmax(a.md - mxd, -700.0), tab);
@@ -199,6 +247,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     __shared__ float s_cv[kTkWaves][kCap];
     __shared__ int32_t s_ci[kTkWaves][kCap];
     __shared__ double s_tab[256];
+    __shared__ double s_t1[513];
+    __shared__ double s_t2[128];
+    __shared__ double s_sf[kTkWaves];
     __shared__ float s_m[kTkWaves];
     __shared__ double s_s[kTkWaves];
 
@@ -211,10 +262,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     constexpr float kNInf = -__builtin_huge_valf();
 
     s_tab[tid] = exp2((double)tid / 256.0);
+    for (int k = tid; k < 513; k += kTkThreads) s_t1[k] = exp((double)(k - 256) * 0.25);
+    if (tid < 128) s_t2[tid] = exp((double)tid / 512.0);
     __syncthreads();
 
     WaveCands wc{s_cv[w], s_ci[w], 0, kNInf};
-    RowSum acc{-kFltMax, (double)-kFltMax, 0.0};
+    RowSum acc{0.0, -kFltMax, (double)-kFltMax, 0.0};
 
     // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
     const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);
@@ -226,7 +279,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
         const int nok = lane < a0 ? 1 : 0;
         const f32x4 x{nok ? rp[lane] : kNInf, kNInf, kNInf, kNInf};
         const float mx = max4(x);
-        sum_piece(acc, x, mx, s_tab);
+        sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
         offer_piece(wc, x, mx, nok, lane, K, lane);
     }
 
@@ -242,7 +295,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const float mx = max4(raw[u]);
-            sum_piece(acc, raw[u], mx, s_tab);
+            sum_piece(acc, raw[u], mx, s_tab, s_t1, s_t2);
             offer_piece(wc, raw[u], mx, 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)), K,
                         lane);
         }
@@ -253,7 +306,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
             const int64_t p = nfull + u * kTkThreads + tid;
             const f32x4 x = p < nvec ? vp[p] : f32x4{kNInf, kNInf, kNInf, kNInf};
             const float mx = max4(x);
-            sum_piece(acc, x, mx, s_tab);
+            sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
             offer_piece(wc, x, mx, p < nvec ? 4 : 0, (int32_t)(a0 + 4 * p), K, lane);
         }
     }
@@ -263,7 +316,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
         const int nok = a1 + lane < V ? 1 : 0;
         const f32x4 x{nok ? rp[a1 + lane] : kNInf, kNInf, kNInf, kNInf};
         const float mx = max4(x);
-        sum_piece(acc, x, mx, s_tab);
+        sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
         offer_piece(wc, x, mx, nok, (int32_t)(a1 + lane), K, lane);
     }
 
@@ -273,10 +326,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     float M = acc.m;
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     double S = acc.s * exp_core(fmax(acc.md - (double)M, -700.0), s_tab);
-    for (int off = 32; off > 0; off >>= 1) S += __shfl_xor(S, off, 64);
+    double SF = acc.sf;
+    for (int off = 32; off > 0; off >>= 1) {
+        S += __shfl_xor(S, off, 64);
+        SF += __shfl_xor(SF, off, 64);
+    }
     if (lane == 0) {
         s_m[w] = M;
         s_s[w] = S;
+        s_sf[w] = SF;
     }
     __syncthreads();
     // the other three lists move behind wavefront 0's, which then keeps the best K of 4K
@@ -289,16 +347,30 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     if (w != 0) return;
     const int kept = keep_best(s_cv[0], s_ci[0], kTkWaves * K, K, lane);
     (void)kept;  // = K: the row holds V >= K elements
+    // logp(y) = (l(y) - R) - log(SF e^-R + S e^(M-R)), the sum of exp(l - R) over the row,
+    // with R = 0 when only small pieces added anything, M when only the others did, else
+    // max(M, 0) (so both factors are <= 1 and l - R is exact)
     M = s_m[0];
     for (int j = 1; j < kTkWaves; ++j) M = fmaxf(M, s_m[j]);
     S = 0.0;
-    for (int j = 0; j < kTkWaves; ++j)
+    SF = 0.0;
+    for (int j = 0; j < kTkWaves; ++j) {
         S += s_s[j] * exp_core(fmax((double)s_m[j] - (double)M, -700.0), s_tab);
-    const double logS = log(S);
+        SF += s_sf[j];
+    }
+    double R = 0.0, logS = log(SF);
+    if (S > 0.0 && SF > 0.0) {
+        R = fmax((double)M, 0.0);
+        logS = log(SF * exp_core(fmax(-R, -700.0), s_tab) +
+                   S * exp_core(fmax((double)M - R, -700.0), s_tab));
+    } else if (S > 0.0) {
+        R = (double)M;
+        logS = log(S);
+    }
     for (int k = lane; k < K; k += 64) {
         const float v = s_cv[0][k];
         top_tok[r * K + k] = s_ci[0][k];
-        top_logp[r * K + k] = v > kNInf ? ((double)v - (double)M) - logS : -__builtin_huge_val();
+        top_logp[r * K + k] = v > kNInf ? ((double)v - R) - logS : -__builtin_huge_val();
     }
 }
 
