@@ -90,6 +90,18 @@ def test_topk_random(orc, R, V, K):
     check_topk(orc, x, K, label="random")
 
 
+@pytest.mark.parametrize("loc,std", [(0.0, 50.0), (1000.0, 3.0), (-500.0, 3.0), (60.0, 4.0),
+                                     (-62.0, 3.0), (0.0, 1e-3)])
+def test_topk_wide_range(orc, loc, std):
+    """Logits beyond the small-range path (|x| >= 64) alone and mixed with small ones:
+    far above and far below zero, straddling +-64, and tightly packed."""
+    rng = np.random.default_rng(int(abs(loc)) + 7)
+    x = (loc + std * rng.normal(size=(6, 20011))).astype(np.float32)
+    x[1, ::97] = np.float32(loc + 200.0)           # a few far larger entries
+    x[2, :] = np.where(rng.random(20011) < 0.5, x[2, :], np.float32(-70.0))
+    check_topk(orc, x, 16, label=f"loc {loc} std {std}")
+
+
 def test_topk_special_rows(orc):
     V = 3000
     rng = np.random.default_rng(5)
