@@ -84,7 +84,9 @@ typedef enum sv_status {
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
-/* Per-sequence tree status written by sv_build_tree_mask into tree_err[b]. */
+/* Per-sequence tree status in tree_err[b]: written by sv_build_tree_mask, and set to
+ * SV_TREE_NOT_APPENDED by sv_kv_append; every call that reads tree_err skips a sequence
+ * whose status is not SV_TREE_OK. */
 enum {
     SV_TREE_OK = 0,
     SV_TREE_BAD_ROOT = 1,
