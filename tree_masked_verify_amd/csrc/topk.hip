@@ -15,11 +15,12 @@
 //
 // topk_rows_kernel: one workgroup of four wavefronts per row.  Every lane streams its
 // 16-byte pieces once and keeps an online max and an fp64 sum of exponentials
-// (exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's element
-// enters it when it beats the wavefront's K-th best so far (while fewer than K entries
-// exist, every element enters).  When the buffer could overflow, the wavefront keeps its K
-// best (K rounds of a 64-lane max over (value, -index) keys) and raises its threshold.
-// At the end the four wavefronts' lists are merged the same way.
+// (exp_small / exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's
+// element enters it when it beats the wavefront's K-th best so far (while fewer than K
+// entries exist, every element enters) and is not below the K-th best another wavefront
+// has published.  When the buffer grows, the wavefront keeps its K best (K rounds of a
+// 64-lane DPP max over (value, -index) keys), raises its threshold and publishes it.  At
+// the end the four wavefronts' lists are merged the same way.
 // best_first_kernel: one wavefront per sequence.  Lane j stands for admitted node j and
 // holds its best child not admitted yet: a node's children come best first, so no other
 // child of it can be next.  Each admission is a 64-lane max over those keys, ties to the
@@ -68,28 +69,30 @@ __device__ __forceinline__ double exp_term(float x, double md, const double *tab
 }
 
 // e^x in fp64 for a logit with |x| < 64, from its fp32 value: n = round(512 x) by the
-// 1.5 * 2^23 rounding trick in fp32, after which r = x - n/512 is exact in fp32 with
-// |r| <= 2^-10; with n = 128 k + j, e^x = e^(k/4) * e^(j/512) * e^r, the first two factors
-// from tables (t1[k + 256], k in [-256, 256]; t2[j], j < 128) and e^r - 1 its Taylor
-// polynomial of degree 4 (remainder below 2^-56 relative).  Same table-driven method as
-// exp_core, with no reduction step and no reference maximum.
+// rounding trick in fp32 (adding 1.5 * 2^23 + 2^15 leaves 0x4B408000 + n in the bits), after
+// which r = x - n/512 is exact in fp32 with |r| <= 2^-10; with n = 128 k + j, e^x =
+// e^(k/4) * e^(j/512) * e^r, the first two factors from tables (t1[k + 256], k in
+// [-256, 256], which is bits 7..16 of t; t2[j], j < 128, its low 7 bits) and e^r - 1 its
+// Taylor polynomial of degree 4 (remainder below 2^-56 relative).  Same table-driven method
+// as exp_core, with no reduction step and no reference maximum.
 __device__ __forceinline__ double exp_small(float x, const double *t1, const double *t2) {
-    constexpr float kMagic = 12582912.0f;              // 1.5 * 2^23
+    constexpr float kMagic = 12615680.0f;              // 1.5 * 2^23 + 2^15
     const float t = fmaf(x, 512.0f, kMagic);
     const float rf = fmaf(t - kMagic, -1.0f / 512.0f, x);
-    const int n = __float_as_int(t) - 0x4B400000;
-    const double T = t1[(n >> 7) + 256] * t2[n & 127];
+    const uint32_t b = __float_as_uint(t);
+    const double T = t1[(b >> 7) & 1023u] * t2[b & 127u];
     const double r = (double)rf;
     double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
     q = fma(q, r, 0.5);
     return fma(T, fma(r * r, q, r), T);
 }
 
-// Whether all four logits are finite with |x| < 64 (the range of exp_small).
+// Whether all four logits are finite with |x| < 64 (the range of exp_small), tested as a
+// sum of squares below 64^2: rounding is monotone and every term is >= 0, so the rounded
+// sum reaches 4096 whenever one |x| does reach 64; inf gives inf and NaN fails the test.
 __device__ __forceinline__ bool small_piece(const f32x4 &x) {
-    const uint32_t a = max(max(__float_as_uint(x[0]) & 0x7fffffffu, __float_as_uint(x[1]) & 0x7fffffffu),
-                           max(__float_as_uint(x[2]) & 0x7fffffffu, __float_as_uint(x[3]) & 0x7fffffffu));
-    return a < 0x42800000u;                            // 64.0f; NaN and inf are above
+    const float q = fmaf(x[3], x[3], fmaf(x[2], x[2], fmaf(x[1], x[1], x[0] * x[0])));
+    return q < 4096.0f;
 }
 
 // A logit as the rule reads it: NaN and -inf give -inf, +inf the largest finite float, and
@@ -99,9 +102,19 @@ __device__ __forceinline__ float clean(float x) {
     return x + 0.0f;
 }
 
-// The largest of four raw logits as the rule reads them (-inf when none is finite).
+// The largest of four raw logits as the rule reads them (-inf when none is finite).  The
+// max instructions ignore a quiet NaN operand; v_max_f32 x, x first quiets a signalling
+// one.  (Inline assembly, so that these moves stay on the path that needs them.)
 __device__ __forceinline__ float max4(const f32x4 &x) {
-    const float a = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));   // a NaN operand is ignored
+    float a, b;
+    asm("v_max_f32 %0, %2, %2\n\t"
+        "v_max_f32 %1, %3, %3\n\t"
+        "v_max_f32 %0, %0, %1\n\t"
+        "v_max_f32 %1, %4, %4\n\t"
+        "v_max_f32 %0, %0, %1\n\t"
+        "v_max_f32 %1, %5, %5\n\t"
+        "v_max_f32 %0, %0, %1"
+        : "=&v"(a), "=&v"(b) : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
     return fminf(fmaxf(a, -__builtin_huge_valf()), kFltMax);
 }
 
@@ -121,12 +134,30 @@ __device__ __forceinline__ int32_t key_index(uint64_t k) {
     return (int32_t)(0xffffffffu - (uint32_t)k);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = __shfl_xor(x, off, 64);
-        x = o > x ? o : x;
-    }
-    return x;
+// A 64-bit value moved across lanes by one DPP control (both halves); lanes without a
+// source, or outside the rows of kRowMask, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, kRowMask, 0xf, true);
+    const int hi =
+        __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, kRowMask, 0xf, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wavefront of unsigned 64-bit values, in every lane: row_shr 1, 2, 4, 8
+// leave each row's maximum in its lane 15; row_bcast 15 and 31 carry it into lane 63.
+__device__ __forceinline__ uint64_t wave_max_dpp(uint64_t x) {
+    x = umax64(x, dpp_u64<0x111, 0xf>(x));
+    x = umax64(x, dpp_u64<0x112, 0xf>(x));
+    x = umax64(x, dpp_u64<0x114, 0xf>(x));
+    x = umax64(x, dpp_u64<0x118, 0xf>(x));
+    x = umax64(x, dpp_u64<0x142, 0xa>(x));
+    x = umax64(x, dpp_u64<0x143, 0xc>(x));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Keeps the best min(n, K) of entries [0, n) (n <= 64 * kSlots) of a wavefront's (value,
@@ -146,7 +177,7 @@ __device__ int keep_best_n(float *cv, int32_t *ci, int n, int K, int lane) {
         uint64_t best = key[0];
 #pragma unroll
         for (int s = 1; s < kSlots; ++s) best = key[s] > best ? key[s] : best;
-        const uint64_t w = wave_max_u64(best);
+        const uint64_t w = wave_max_dpp(best);
 #pragma unroll
         for (int s = 0; s < kSlots; ++s) key[s] = key[s] == w ? 0 : key[s];
         mine = lane == r ? w : mine;
@@ -170,27 +201,57 @@ struct WaveCands {
     int32_t *ci;
     int cnt;      // entries in the buffer (wavefront-uniform)
     float tau;    // K-th best value once the buffer was cut to K, else -inf
+    float *pub;   // every wavefront's last tau, in LDS (-inf before its first cut)
+    float tsh;    // the largest of them when last read
 };
+
+__device__ __forceinline__ float uniform_f(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Reads the wavefronts' published thresholds.  Another wavefront's K-th best u means K
+// logits >= u exist, so a logit below u cannot be among the row's K best; one equal to u
+// still can (ties go to the smaller token, and the wavefronts' tokens interleave), hence
+// the test v >= tsh next to v > tau.  A stale value is an older, lower one: still a bound.
+__device__ __forceinline__ void refresh_shared(WaveCands &wc) {
+    float t = __hip_atomic_load(wc.pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+    for (int j = 1; j < kTkWaves; ++j)
+        t = fmaxf(t, __hip_atomic_load(wc.pub + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    wc.tsh = uniform_f(t);
+}
+
+// After a cut back to K entries: the new threshold, published for the other wavefronts.
+__device__ __forceinline__ void set_tau(WaveCands &wc, int w, int lane) {
+    wc.tau = uniform_f(wc.cv[wc.cnt - 1]);
+    if (lane == 0)
+        __hip_atomic_store(wc.pub + w, wc.tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // One piece: up to four consecutive raw logits per lane (the first `nok` exist), all with
 // larger indices than every entry already in the buffer, mx = max4 of them.  They are
 // judged against the buffer as it stood before the piece.  Once the buffer holds K + 24
 // entries it is cut back to K, so the threshold follows the running K-th best closely
 // (each cut is K rounds of a 64-lane max over one slot per lane).
+// Whether a logit of value m could enter the buffer now (the test of offer_piece).
+__device__ __forceinline__ bool may_enter(const WaveCands &wc, float m, int K) {
+    return (wc.cnt < K || m > wc.tau) && m >= wc.tsh;
+}
+
 __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float mx, int nok,
-                                            int32_t idx0, int K, int lane) {
+                                            int32_t idx0, int K, int w, int lane) {
+    if (!__any(nok > 0 && may_enter(wc, mx, K))) return;
     bool full = wc.cnt >= K;
-    if (!__any(nok > 0 && (!full || mx > wc.tau))) return;
     if (wc.cnt + kPiece > kCap) {
-        wc.cnt = keep_best(wc.cv, wc.ci, wc.cnt, K, lane);
+        wc.cnt = __builtin_amdgcn_readfirstlane(keep_best(wc.cv, wc.ci, wc.cnt, K, lane));
         full = wc.cnt >= K;
-        wc.tau = full ? wc.cv[K - 1] : -__builtin_huge_valf();
+        if (full) set_tau(wc, w, lane);
     }
     int cnt = wc.cnt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float v = clean(x[e]);
-        const bool pass = e < nok && (!full || v > wc.tau);
+        const bool pass = e < nok && (!full || v > wc.tau) && v >= wc.tsh;
         const uint64_t bal = __ballot(pass);
         if (bal) {
             const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi(
@@ -205,8 +266,9 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float
     }
     wc.cnt = cnt;
     if (cnt >= K + 24) {
-        wc.cnt = keep_best(wc.cv, wc.ci, cnt, K, lane);
-        wc.tau = wc.cv[K - 1];
+        wc.cnt = K;
+        keep_best(wc.cv, wc.ci, cnt, K, lane);
+        set_tau(wc, w, lane);
     }
 }
 
@@ -220,16 +282,27 @@ struct RowSum {
     double s;    // sum of exp(x - m) over the other pieces
 };
 
-// Adds a piece to the lane's sums (entries beyond those that exist are -inf).  Whether it
-// takes the small-piece path is decided for the whole wavefront.
-__device__ __forceinline__ void sum_piece(RowSum &a, const f32x4 &x, float mx, const double *tab,
-                                          const double *t1, const double *t2) {
+// The largest of four values that are not NaN (so the max instructions need no quieting
+// moves before them).
+__device__ __forceinline__ float max4_ordered(const f32x4 &x) {
+    float m;
+    asm("v_max3_f32 %0, %1, %2, %3\n\tv_max_f32 %0, %0, %4"
+        : "=&v"(m) : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+    return m;
+}
+
+// Adds a piece to the lane's sums (entries beyond those that exist are -inf) and returns
+// the largest of its logits as the rule reads them (max4).  Whether it takes the
+// small-piece path is decided for the whole wavefront.
+__device__ __forceinline__ float sum_piece(RowSum &a, const f32x4 &x, const double *tab,
+                                           const double *t1, const double *t2) {
     if (__all(small_piece(x))) {
         const double e0 = exp_small(x[0], t1, t2), e1 = exp_small(x[1], t1, t2);
         const double e2 = exp_small(x[2], t1, t2), e3 = exp_small(x[3], t1, t2);
         a.sf += (e0 + e1) + (e2 + e3);
-        return;
+        return max4_ordered(x);
     }
+    const float mx = max4(x);
     if (mx > a.m) {
         const double mxd = (double)mx;
         a.s *= exp_core(fmax(a.md - mxd, -700.0), tab);
@@ -239,6 +312,7 @@ __device__ __forceinline__ void sum_piece(RowSum &a, const f32x4 &x, float mx, c
     const double e0 = exp_term(x[0], a.md, tab), e1 = exp_term(x[1], a.md, tab);
     const double e2 = exp_term(x[2], a.md, tab), e3 = exp_term(x[3], a.md, tab);
     a.s += (e0 + e1) + (e2 + e3);
+    return mx;
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
@@ -252,6 +326,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     __shared__ double s_sf[kTkWaves];
     __shared__ float s_m[kTkWaves];
     __shared__ double s_s[kTkWaves];
+    __shared__ float s_pub[kTkWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -264,9 +339,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     s_tab[tid] = exp2((double)tid / 256.0);
     for (int k = tid; k < 513; k += kTkThreads) s_t1[k] = exp((double)(k - 256) * 0.25);
     if (tid < 128) s_t2[tid] = exp((double)tid / 512.0);
+    if (tid < kTkWaves) s_pub[tid] = kNInf;
     __syncthreads();
 
-    WaveCands wc{s_cv[w], s_ci[w], 0, kNInf};
+    WaveCands wc{s_cv[w], s_ci[w], 0, kNInf, s_pub, kNInf};
     RowSum acc{0.0, -kFltMax, (double)-kFltMax, 0.0};
 
     // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
@@ -278,9 +354,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     if (w == 0) {
         const int nok = lane < a0 ? 1 : 0;
         const f32x4 x{nok ? rp[lane] : kNInf, kNInf, kNInf, kNInf};
-        const float mx = max4(x);
-        sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
-        offer_piece(wc, x, mx, nok, lane, K, lane);
+        const float mx = sum_piece(acc, x, s_tab, s_t1, s_t2);
+        offer_piece(wc, x, mx, nok, lane, K, w, lane);
     }
 
     // body: 16-byte pieces, piece p = base + u * 256 + tid holds elements a0 + 4p .. + 3;
@@ -292,22 +367,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
         f32x4 raw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) raw[u] = vp[base + u * kTkThreads + tid];
+        refresh_shared(wc);
+        float mx[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float mx = max4(raw[u]);
-            sum_piece(acc, raw[u], mx, s_tab, s_t1, s_t2);
-            offer_piece(wc, raw[u], mx, 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)), K,
-                        lane);
-        }
+        for (int u = 0; u < 4; ++u) mx[u] = sum_piece(acc, raw[u], s_tab, s_t1, s_t2);
+        // most trips hold no logit that could enter: one test for the four pieces
+        if (!__any(may_enter(wc, max4_ordered(f32x4{mx[0], mx[1], mx[2], mx[3]}), K))) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            offer_piece(wc, raw[u], mx[u], 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)),
+                        K, w, lane);
     }
     if (nfull < nvec) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t p = nfull + u * kTkThreads + tid;
             const f32x4 x = p < nvec ? vp[p] : f32x4{kNInf, kNInf, kNInf, kNInf};
-            const float mx = max4(x);
-            sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
-            offer_piece(wc, x, mx, p < nvec ? 4 : 0, (int32_t)(a0 + 4 * p), K, lane);
+            const float mx = sum_piece(acc, x, s_tab, s_t1, s_t2);
+            offer_piece(wc, x, mx, p < nvec ? 4 : 0, (int32_t)(a0 + 4 * p), K, w, lane);
         }
     }
 
@@ -315,9 +392,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     if (w == 0) {
         const int nok = a1 + lane < V ? 1 : 0;
         const f32x4 x{nok ? rp[a1 + lane] : kNInf, kNInf, kNInf, kNInf};
-        const float mx = max4(x);
-        sum_piece(acc, x, mx, s_tab, s_t1, s_t2);
-        offer_piece(wc, x, mx, nok, (int32_t)(a1 + lane), K, lane);
+        const float mx = sum_piece(acc, x, s_tab, s_t1, s_t2);
+        offer_piece(wc, x, mx, nok, (int32_t)(a1 + lane), K, w, lane);
     }
 
     // each wavefront's K best, then the max and sum of the wavefront
@@ -377,32 +453,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
 __device__ __forceinline__ uint64_t ord_f64(double x) {
     const uint64_t u = (uint64_t)__double_as_longlong(x);
     return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-// A 64-bit value moved across lanes by one DPP control (both halves); lanes without a
-// source, or outside the rows of kRowMask, read 0.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, kRowMask, 0xf, true);
-    const int hi =
-        __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, kRowMask, 0xf, true);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Maximum over the wavefront of unsigned 64-bit values, in every lane: row_shr 1, 2, 4, 8
-// leave each row's maximum in its lane 15; row_bcast 15 and 31 carry it into lane 63.
-__device__ __forceinline__ uint64_t wave_max_dpp(uint64_t x) {
-    x = umax64(x, dpp_u64<0x111, 0xf>(x));
-    x = umax64(x, dpp_u64<0x112, 0xf>(x));
-    x = umax64(x, dpp_u64<0x114, 0xf>(x));
-    x = umax64(x, dpp_u64<0x118, 0xf>(x));
-    x = umax64(x, dpp_u64<0x142, 0xa>(x));
-    x = umax64(x, dpp_u64<0x143, 0xc>(x));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ double readlane_f64(double x, int lane) {
