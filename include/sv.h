@@ -173,7 +173,11 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  *   scale   softmax scale, usually 1/sqrt(D); must be positive and finite
  *   workspace  device, >= sv_tree_verify_attention_workspace_size(...) bytes,
  *              256-byte aligned; scratch for per-split partial results
- *   num_splits 0 = automatic; otherwise the number of prefix chunks per sequence
+ *   num_splits 0 = automatic; otherwise the number of prefix chunks per sequence.
+ *              Automatic splitting at head_dim 128 / 256 with bf16 may size the chunks
+ *              from prefix_len on the device (so that sequences of different lengths
+ *              share the CUs evenly); the result then depends on every sequence's
+ *              length only through rounding of the chunked sums.
  * Arithmetic: bf16 (or fp32) operands, fp32 accumulation; the result matches
  * the exact softmax attention to within bf16 rounding of the probabilities.
  * Prefix rows whose block-table entry is outside [0, num_blocks) are left out.

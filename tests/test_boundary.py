@@ -106,6 +106,9 @@ def test_attention_workspace_size(lib):
     assert f(16, 32, 8, 60, 64, 32768, sv.SV_BF16) == 0
     assert f(16, 32, 8, 60, 128, 32768, sv.SV_BF16) > 0   # head_dim 128 is supported
     assert f(1, 1, 1, 1, 256, 0, sv.SV_F32) > 0
+    # a full grid of one chunk per sequence still reserves a second chunk, which the
+    # kernel uses when it re-cuts the chunks from the actual prefix lengths
+    assert f(32, 32, 4, 64, 256, 8192, sv.SV_BF16) >= 32 * 4 * 2 * 512 * 256 * 4
 
 
 def test_accept_validation(lib):

@@ -81,6 +81,26 @@ def test_long_reduced_splits(orc, splits):
     run_case(orc, w, 3, num_splits=splits)
 
 
+def _rows_every_sequence(w):
+    """Two (b, h, i) rows of every sequence."""
+    return np.array(sorted({(b, (7 * b) % w.Hq, (3 * b) % w.T) for b in range(w.B)} |
+                           {(b, (7 * b + 19) % w.Hq, (5 * b + 1) % w.T) for b in range(w.B)}),
+                    dtype=np.int32)
+
+
+@pytest.mark.parametrize("B,splits", [(32, 0), (32, 2), (70, 0)])
+def test_varied_prefix_chunking(orc, B, splits):
+    """The batched shape's heads with prefix lengths from 0 to 3000, some on either side of
+    the chunk boundary the kernel picks.  Automatic chunking at B = 32 (64 (sequence, chunk)
+    pairs) cuts the chunks from the actual lengths and starts the largest first; B = 70 and
+    an explicit split count keep the plan's uniform chunks.  Two rows of every sequence."""
+    rng = np.random.default_rng(B)
+    P = [3000, 0, 2999, 1, 2016, 2015, 2017, 32, 31, 33, 2000, 1500]  # chunk length 2016 at B = 32
+    P += [int(v) for v in rng.integers(1500, 3001, B - len(P))]
+    w = wl.scaled(wl.WORKLOADS["batched8k"], name=f"varied{B}", B=B, prefix=(0, 3000), V=1000)
+    run_case(orc, w, 5, num_splits=splits, rows=_rows_every_sequence(w), prefix_override=P)
+
+
 @pytest.mark.parametrize("bs", [32, 48, 64, 256])
 def test_block_sizes(orc, bs):
     # cache blocks larger than a 16-key group: both groups of a tile often share a block

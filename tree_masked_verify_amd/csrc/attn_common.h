@@ -27,8 +27,10 @@ struct MfmaParams {
     int B, Hq, Hkv, T, G, R;
     float scale_log2;
     int S, C, n_rg, total;
+    int balanced;          // chunks cut from the actual prefix lengths, largest first
     float *ws_o;
     float *ws_ml;
+    int32_t *ws_c;         // where a balanced call leaves its chunk length
 };
 
 // Tree rows kept in the cache (no tree buffers given): byte address of tree row r of
@@ -58,6 +60,90 @@ __device__ __forceinline__ int xcd_logical_id() {
 }
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int clamp_prefix(int P, int max_P) {
+    return P < 0 ? 0 : (P > max_P ? max_P : P);
+}
+
+// Keys of chunk s of a sequence with P prefix keys (chunks of C keys); the first chunk
+// also holds the T tree keys.
+__device__ __forceinline__ int chunk_keys(int P, int s, int C, int T) {
+    const int start = s * C;
+    const int n = start < P ? min(C, P - start) : 0;
+    return s == 0 ? n + T : n;
+}
+
+// Balanced chunk length: the whole call's prefix keys, times the workgroups that read
+// each of them (kv heads x row groups), over the compute units, so that about one
+// chunk per CU remains; at least ceil(max_P / S) so that S chunks cover any sequence
+// (the plan's own chunk length is at least that, so it fits an int), at most max_P;
+// whole key tiles.  Same value in every wavefront that calls it.
+__device__ __forceinline__ int balanced_chunk_len(const MfmaParams &p) {
+    const int lane = threadIdx.x & 63;
+    int64_t sum = 0;
+    for (int b = lane; b < p.B; b += 64) sum += clamp_prefix(p.prefix_len[b], p.max_P);
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const auto tiles = [](int64_t n) { return (n + kKeyTile - 1) / kKeyTile * kKeyTile; };
+    const int64_t lower = tiles(((int64_t)p.max_P + p.S - 1) / p.S);
+    int64_t upper = tiles(p.max_P);
+    if (upper > INT_MAX / kKeyTile * kKeyTile) upper = INT_MAX / kKeyTile * kKeyTile;
+    if (upper < lower) upper = lower;
+    int64_t C = tiles((sum * p.Hkv * p.n_rg + kNumCU - 1) / kNumCU);
+    C = C < lower ? lower : (C > upper ? upper : C);
+    return uni((int)(C < kKeyTile ? kKeyTile : C));
+}
+
+// The work item of this workgroup in a balanced call.  The B * S chunks (id c = b S + s)
+// are ranked by their keys, largest first (ties: smaller id); rank j has one block per kv
+// head, and a block is n_rg workgroups (its row groups) that read the same keys.  Blocks
+// are dealt to the XCDs in rank order, snaking (0..7, 7..0, ...), and each XCD starts its
+// blocks in that order as CUs come free, so the smallest chunks fill in after the
+// largest.  False when the workgroup has no item.
+__device__ __forceinline__ bool balanced_item(const MfmaParams &p, int C, int *b, int *kvh,
+                                              int *s, int *rg) {
+    const int x = blockIdx.x % kNumXCD;
+    const int pos = blockIdx.x / kNumXCD;
+    const int k = pos / p.n_rg;
+    *rg = pos - k * p.n_rg;
+    const int gq = k * kNumXCD + ((k & 1) ? kNumXCD - 1 - x : x);
+    const int N = p.B * p.S;  // <= kBalancedChunks
+    if (gq >= N * p.Hkv) return false;
+    const int j = gq / p.Hkv;
+    *kvh = gq - j * p.Hkv;
+    // lane l ranks chunks l and l + 64
+    const int lane = threadIdx.x & 63;
+    int sz[2], rk[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = lane + 64 * i;
+        sz[i] = c < N ? chunk_keys(clamp_prefix(p.prefix_len[c / p.S], p.max_P), c % p.S, C, p.T)
+                      : -1;
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+        const int n2 = min(64, N - 64 * i2);
+        for (int l2 = 0; l2 < n2; ++l2) {
+            const int z = __builtin_amdgcn_readlane(sz[i2], l2);
+            const int c2 = 64 * i2 + l2;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = lane + 64 * i;
+                rk[i] += (z > sz[i] || (z == sz[i] && c2 < c)) ? 1 : 0;
+            }
+        }
+    }
+    int c = -1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint64_t hit = __ballot(lane + 64 * i < N && rk[i] == j);
+        if (hit) c = 64 * i + (int)__builtin_ctzll(hit);
+    }
+    c = uni(c);
+    if (c < 0) return false;  // not reached: ranks 0 .. N-1 are all taken
+    *b = c / p.S;
+    *s = c - *b * p.S;
+    return true;
+}
 
 // Block-table entry number `idx` of sequence b, or -1 when it is out of range.  The
 // table is read through the constant address space: with a uniform index this is a

@@ -563,6 +563,13 @@ hipError_t launch_d(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
 
 }  // namespace
 
+bool attn_w4_handles(int D) {
+#ifndef SV_ATTN_LEGACY256
+    if (D == 256) return true;
+#endif
+    return D == 128;
+}
+
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (a.D == 128) return launch_attn_w4(a, pl, stream);

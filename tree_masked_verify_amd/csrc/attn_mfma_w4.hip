@@ -27,7 +27,10 @@
 //     matrix instructions of its first chunk's PV product;
 //   * the reference max only moves when a tile raises it by more than 2^8, so the
 //     accumulators are rarely rescaled (the merged result does not depend on the
-//     reference values used).
+//     reference values used);
+//   * with automatic splitting (balanced plan) the chunk length comes from the actual
+//     prefix lengths, about one chunk per CU in all, and the chunks start largest first
+//     (balanced_item), so sequences of different lengths finish together.
 #include "attn_common.h"
 
 namespace sv {
@@ -382,21 +385,28 @@ void attn_w4_kernel(MfmaParams p) {
     constexpr int KS = G::KS, DB = G::DB, KU = G::KU, VU = G::VU, KTILE = G::KTILE;
     constexpr int STAGE_BYTES = G::STAGE_BYTES, GTAB_OFF = G::GTAB_OFF, MASK_OFF = G::MASK_OFF;
 
-    const int logical = xcd_logical_id();
-    if (logical >= p.total) return;
-    int t = logical;
-    const int rg = t % p.n_rg;
-    t /= p.n_rg;
-    const int s = t % p.S;
-    t /= p.S;
-    const int kvh = t % p.Hkv;
-    const int b = t / p.Hkv;
+    int b, kvh, s, rg, C;
+    if (p.balanced) {
+        C = balanced_chunk_len(p);
+        if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws_c = C;  // for the merge
+        if (!balanced_item(p, C, &b, &kvh, &s, &rg)) return;
+    } else {
+        const int logical = xcd_logical_id();
+        if (logical >= p.total) return;
+        int t = logical;
+        rg = t % p.n_rg;
+        t /= p.n_rg;
+        s = t % p.S;
+        t /= p.S;
+        kvh = t % p.Hkv;
+        b = t / p.Hkv;
+        C = p.C;
+    }
 
-    int P = p.prefix_len[b];
-    P = P < 0 ? 0 : (P > p.max_P ? p.max_P : P);
-    const int start = s * p.C;
+    const int P = clamp_prefix(p.prefix_len[b], p.max_P);
+    const int start = s * C;
     if (s > 0 && start >= P) return;  // chunk past this sequence's prefix: nothing to merge
-    const int end = min(start + p.C, P);
+    const int end = min(start + C, P);
     const int ntp = end > start ? (end - start + kKeyTile - 1) / kKeyTile : 0;
     const int ntt = s == 0 ? (p.T + kKeyTile - 1) / kKeyTile : 0;
     const int nt = ntp + ntt;
@@ -717,9 +727,14 @@ hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) 
     p.C = pl.C;
     p.n_rg = pl.n_rg;
     p.total = a.B * a.Hkv * pl.S * pl.n_rg;
+    p.balanced = pl.balanced;
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
-    const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
+    p.ws_c = a.ws_c;
+    // balanced: whole blocks (n_rg workgroups) per XCD and round, see balanced_item
+    const int grid = pl.balanced
+                         ? (a.B * pl.S * a.Hkv + kNumXCD - 1) / kNumXCD * kNumXCD * pl.n_rg
+                         : (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kW), SMEM, stream, p);
     return hipGetLastError();
 }

@@ -1,7 +1,9 @@
 // attn_reduce.hip -- merge the per-chunk partial attention results of each query row.
 //
 // Chunk s of a row left an unnormalised output O_s, its reference max m_s (log2
-// units) and the sum l_s of its exp2(score - m_s) weights.  With M = max_s m_s:
+// units) and the sum l_s of its exp2(score - m_s) weights; the chunks of C keys that
+// exist for the row's prefix length took part (C from the plan, or from the workspace
+// header when the attention kernel chose it).  With M = max_s m_s:
 //   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,
 // the split-then-merge scheme the pages' flash_attn_vec_reduce plays (ADR-037
 // Phase status row E1.2 and the E6 full-layer rows).  One wavefront per output row
@@ -20,6 +22,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
                                                           const int32_t *__restrict__ prefix_len,
                                                           int max_P, int B, int Hq, int Hkv,
                                                           int T, int R, int S, int C,
+                                                          const int32_t *__restrict__ c_hdr,
                                                           float *__restrict__ out) {
     constexpr int NV4 = D / 4;                 // float4 vectors per row
     constexpr int VPL = (NV4 + 63) / 64;       // per lane (lanes past NV4 idle at D = 128)
@@ -36,6 +39,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
 
     int P = prefix_len[b];
     P = P < 0 ? 0 : (P > max_P ? max_P : P);
+    if (c_hdr) C = *c_hdr;  // the chunk length the attention kernel chose
     int nv = (P + C - 1) / C;
     nv = nv < 1 ? 1 : (nv > S ? S : nv);
 
@@ -68,19 +72,20 @@ hipError_t launch_attn_reduce(const AttnArgs &a, const AttnPlan &pl, hipStream_t
     const int64_t nrows = (int64_t)a.B * a.T * a.Hq;
     if (nrows == 0) return hipSuccess;
     const int per = 4;
+    const int32_t *c_hdr = pl.balanced ? a.ws_c : nullptr;
     dim3 grid((unsigned)((nrows + per - 1) / per));
     if (a.D == 128)
         hipLaunchKernelGGL(attn_reduce_kernel<128>, grid, dim3(64 * per), 0, stream, a.ws_o,
                            a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
-                           pl.R, pl.S, pl.C, a.out);
+                           pl.R, pl.S, pl.C, c_hdr, a.out);
     else if (a.D == 256)
         hipLaunchKernelGGL(attn_reduce_kernel<256>, grid, dim3(64 * per), 0, stream, a.ws_o,
                            a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
-                           pl.R, pl.S, pl.C, a.out);
+                           pl.R, pl.S, pl.C, c_hdr, a.out);
     else
         hipLaunchKernelGGL(attn_reduce_kernel<512>, grid, dim3(64 * per), 0, stream, a.ws_o,
                            a.ws_ml, a.prefix_len, a.max_prefix_len, a.B, a.Hq, a.Hkv, a.T,
-                           pl.R, pl.S, pl.C, a.out);
+                           pl.R, pl.S, pl.C, c_hdr, a.out);
     return hipGetLastError();
 }
 

@@ -108,6 +108,17 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     if (C < kKeyTile) C = kKeyTile;
     int64_t S = (max_prefix_len + C - 1) / C;
     if (S < 1) S = 1;
+    // Prefix lengths that differ leave one chunk per workgroup unbalanced: the w4 kernel
+    // then re-cuts the chunks from the actual lengths (one more chunk per sequence when
+    // the grid is already full) and starts the largest first.
+    p->balanced = 0;
+    if (p->mfma && attn_w4_handles(D) && num_splits == 0) {
+        const int64_t S2 = (S == 1 && B > 1) ? 2 : S;
+        if ((int64_t)B * S2 <= kBalancedChunks) {
+            p->balanced = 1;
+            S = S2;
+        }
+    }
     p->C = (int)C;
     p->S = (int)S;
     int64_t work, o_elems, ml_elems;
@@ -116,7 +127,8 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     if (!prod_ok({(int64_t)B, Hkv, S, R, 2}, &ml_elems)) return SV_ERR_OVERFLOW;
     p->ws_o = round256((size_t)o_elems * 4);
     p->ws_ml = round256((size_t)ml_elems * 4);
-    p->ws_total = p->ws_o + p->ws_ml;
+    p->ws_hdr = 256;
+    p->ws_total = p->ws_o + p->ws_ml + p->ws_hdr;
     return SV_OK;
 }
 
@@ -203,6 +215,7 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
     a.out = out;
     a.ws_o = static_cast<float *>(workspace);
     a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_o);
+    a.ws_c = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + plan.ws_o + plan.ws_ml);
     hipError_t e = plan.mfma ? launch_attn_mfma(a, plan, stream)
                              : launch_attn_valu(a, plan, dtype, stream);
     if (e != hipSuccess) return SV_ERR_HIP;

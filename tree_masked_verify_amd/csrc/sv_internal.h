@@ -42,12 +42,18 @@ struct AttnPlan {
     int rows_per_wg;   // rows one workgroup owns
     int n_rg;          // row groups per kv head
     int nthreads;      // threads per workgroup
-    int S;             // prefix chunks (splits) per sequence
-    int C;             // keys per chunk, multiple of kKeyTile
+    int S;             // prefix chunks (splits) per sequence, at most
+    int C;             // keys per chunk, multiple of kKeyTile (unless balanced)
+    int balanced;      // 1: the kernel sizes chunks from the actual prefix lengths and
+                       // starts the largest first (attn_w4 kernel, B * S <= kBalancedChunks)
     size_t ws_o;       // bytes of partial outputs  [B][Hkv][S][R][D] fp32
     size_t ws_ml;      // bytes of partial (m, l)   [B][Hkv][S][R][2] fp32
+    size_t ws_hdr;     // bytes of the header: the chunk length a balanced call chose
     size_t ws_total;
 };
+
+// The most (sequence, chunk) pairs that a balanced call ranks by size.
+constexpr int kBalancedChunks = 128;
 
 struct AttnArgs {
     const void *q;
@@ -62,6 +68,7 @@ struct AttnArgs {
     float *out;
     float *ws_o;
     float *ws_ml;
+    int32_t *ws_c;     // header: the chunk length of a balanced call
 };
 
 // Returns 0 and fills *p, or a negative sv_status for unsupported shapes.
@@ -70,6 +77,8 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
 
 hipError_t launch_tree_mask(const int32_t *parents, int B, int T, uint64_t *mask,
                             int32_t *depth, int32_t *tree_err, hipStream_t stream);
+// Whether launch_attn_mfma runs the four-wavefront kernel (attn_w4) at this head_dim.
+bool attn_w4_handles(int D);
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
 // head_dim 128 and 256, one wavefront per SIMD (called by launch_attn_mfma)
 hipError_t launch_attn_w4(const AttnArgs &a, const AttnPlan &p, hipStream_t stream);
