@@ -112,3 +112,19 @@ def test_large_positions_and_thetas(orc):
               large=True)
         inp = wl.make_inputs(w, seed=8, device=DEV, with_logits=False)
         check(orc, inp, 10.0, label=w.name + " theta 10")
+
+
+def test_unaligned_tensors(orc):
+    """Q and tree keys that start one element past a 16-byte boundary take the
+    element-wise form; the same data at aligned addresses the 16-byte one."""
+    for dtype in ("bf16", "f32"):
+        w = wl.scaled(wl.WORKLOADS["parity512"], B=2, dtype=dtype, name=f"unaligned-{dtype}")
+        inp = wl.make_inputs(w, seed=11, device=DEV, with_logits=False)
+        for name in ("q", "k_tree"):
+            t = getattr(inp, name)
+            buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+            view = buf[1:1 + t.numel()].view(t.shape)
+            view.copy_(t)
+            assert view.data_ptr() % 16 != 0
+            setattr(inp, name, view)
+        check(orc, inp, 1e4, label=w.name)
