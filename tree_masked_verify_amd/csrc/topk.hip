@@ -134,30 +134,40 @@ __device__ __forceinline__ int32_t key_index(uint64_t k) {
     return (int32_t)(0xffffffffu - (uint32_t)k);
 }
 
-// A 64-bit value moved across lanes by one DPP control (both halves); lanes without a
-// source, or outside the rows of kRowMask, read 0.
+// A 32-bit value moved across lanes by one DPP control; lanes without a source, or
+// outside the rows of kRowMask, read 0.
 template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, kRowMask, 0xf, true);
-    const int hi =
-        __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, kRowMask, 0xf, true);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xf, true);
 }
 
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// Maximum over the wavefront of unsigned 64-bit values, in every lane: row_shr 1, 2, 4, 8
+// Maximum over the wavefront of unsigned 32-bit values, in every lane: row_shr 1, 2, 4, 8
 // leave each row's maximum in its lane 15; row_bcast 15 and 31 carry it into lane 63.
-__device__ __forceinline__ uint64_t wave_max_dpp(uint64_t x) {
-    x = umax64(x, dpp_u64<0x111, 0xf>(x));
-    x = umax64(x, dpp_u64<0x112, 0xf>(x));
-    x = umax64(x, dpp_u64<0x114, 0xf>(x));
-    x = umax64(x, dpp_u64<0x118, 0xf>(x));
-    x = umax64(x, dpp_u64<0x142, 0xa>(x));
-    x = umax64(x, dpp_u64<0x143, 0xc>(x));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_dpp32(uint32_t x) {
+    x = max(x, dpp_u32<0x111, 0xf>(x));
+    x = max(x, dpp_u32<0x112, 0xf>(x));
+    x = max(x, dpp_u32<0x114, 0xf>(x));
+    x = max(x, dpp_u32<0x118, 0xf>(x));
+    x = max(x, dpp_u32<0x142, 0xa>(x));
+    x = max(x, dpp_u32<0x143, 0xc>(x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// The lowest lane holding the largest nonzero 64-bit key, or -1 when every key is 0: a
+// 32-bit maximum over the high words, then (only when several lanes share that word)
+// over the low words of those lanes.
+__device__ __forceinline__ int wave_argmax_key(uint64_t k) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    const uint32_t mhi = wave_max_dpp32(hi);
+    const bool cand = k != 0 && hi == mhi;
+    uint64_t bal = __ballot(cand);
+    if (bal == 0) return -1;
+    if (bal & (bal - 1)) {
+        const uint32_t lo = cand ? (uint32_t)k : 0u;
+        const uint32_t mlo = wave_max_dpp32(lo);
+        bal = __ballot(cand && lo == mlo);
+    }
+    return (int)__builtin_ctzll(bal);
 }
 
 // Keeps the best min(n, K) of entries [0, n) (n <= 64 * kSlots) of a wavefront's (value,
@@ -177,7 +187,12 @@ __device__ int keep_best_n(float *cv, int32_t *ci, int n, int K, int lane) {
         uint64_t best = key[0];
 #pragma unroll
         for (int s = 1; s < kSlots; ++s) best = key[s] > best ? key[s] : best;
-        const uint64_t w = wave_max_dpp(best);
+        const int wl = wave_argmax_key(best);
+        const uint64_t w =
+            wl < 0 ? 0
+                   : ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(best >> 32), wl)
+                      << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, wl);
 #pragma unroll
         for (int s = 0; s < kSlots; ++s) key[s] = key[s] == w ? 0 : key[s];
         mine = lane == r ? w : mine;
@@ -497,10 +512,8 @@ __global__ __launch_bounds__(64) void best_first_kernel(
     bool live = lane == 0 && nr > 0 && max_levels > 1;   // has a pending child
     for (int n = 1; n < T; ++n) {
         const double key = cj + hlp;
-        const uint64_t kk = live ? ord_f64(key) : 0;
-        const uint64_t top = wave_max_dpp(kk);
-        if (top == 0) break;   // nothing pending: excluded by the caller's shape check
-        const int win = (int)__builtin_ctzll(__ballot(kk == top));
+        const int win = wave_argmax_key(live ? ord_f64(key) : 0);
+        if (win < 0) break;    // nothing pending: excluded by the caller's shape check
         const double wkey = readlane_f64(key, win);
         const int32_t wtok = __builtin_amdgcn_readlane(htok, win);
         const int wlevel = __builtin_amdgcn_readlane(level, win);
