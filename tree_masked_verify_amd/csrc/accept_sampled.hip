@@ -104,10 +104,15 @@ __global__ __launch_bounds__(256) void softmax_partial_kernel(const float *__res
     }
 }
 
-// Weight of token y in a row whose max is m: exp2((l - m) * k), 0 for NaN / -inf.
-__device__ __forceinline__ float weight(const float *row, int64_t y, float m, float k) {
-    const float l = clean_logit(row[y]);
+// Weight of a raw logit in a row whose max is m: exp2((l - m) * k), 0 for NaN / -inf.
+__device__ __forceinline__ float weight_of(float raw, float m, float k) {
+    const float l = clean_logit(raw);
     return l == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f((l - m) * k);
+}
+
+// Weight of token y in a row whose max is m.
+__device__ __forceinline__ float weight(const float *row, int64_t y, float m, float k) {
+    return weight_of(row[y], m, k);
 }
 
 constexpr int kWalkWaves = 16;  // wavefronts of the walk kernel's workgroup
@@ -135,6 +140,13 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
     const int64_t row0 = (int64_t)b * T;
     if (w == 0) {
         const bool in = lane < T;
+        const int p = in ? parents[row0 + lane] : -1;
+        const int32_t x = in ? draft[row0 + lane] : -1;
+        const bool xin = x >= 0 && (int64_t)x < V;
+        // this node's token in its parent's row, fetched before the walk needs it (every
+        // node at once, instead of one dependent load per level)
+        const bool fetch = in && lane > 0 && p >= 0 && p < lane && xin;
+        const float lx = fetch ? logits[(row0 + p) * V + x] : 0.0f;
         // row statistics of node `lane`
         MS st{-__builtin_huge_valf(), 0.0f};
         if (in) {
@@ -148,7 +160,6 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 for (int j = 0; j < 8; ++j) st = ms_merge(st, q[j], k);
             }
         }
-        const int p = in ? parents[row0 + lane] : -1;
         const bool bad = (lane == 0 && p != -1) || (lane >= 1 && in && (p < 0 || p >= lane));
         const bool invalid = __ballot(bad) != 0ull || (tree_err && tree_err[b] != 0);
         if (invalid) {
@@ -161,8 +172,6 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 s_state[0] = 1;
             }
         } else {
-            const int32_t x = in ? draft[row0 + lane] : -1;
-            const bool xin = x >= 0 && (int64_t)x < V;
             const float ux = in ? u_accept[row0 + lane] : 1.0f;  // this node's draw as a proposal
             int v = 0, L = 1;
             uint64_t path = 1ull;
@@ -174,8 +183,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 const float mv = __shfl(st.m, v, 64);
                 const float zv = __shfl(st.s, v, 64);
                 const bool kid = in && p == v && lane > 0;
-                const float *rowv = logits + (row0 + v) * V;
-                wx = (kid && xin && zv > 0.0f) ? weight(rowv, x, mv, k) : 0.0f;
+                wx = (kid && xin && zv > 0.0f) ? weight_of(lx, mv, k) : 0.0f;  // kid: p < lane
                 const float px = zv > 0.0f ? wx / zv : 0.0f;
                 rej = false;
                 uint64_t kids = __ballot(kid);
