@@ -319,6 +319,21 @@ def main():
     bytes_attn, flops_attn = attention_traffic(inp, st.depth)
     gbs = bytes_attn / (ms_attn * 1e-3) / 1e9
     tflops = flops_attn / (ms_attn * 1e-3) / 1e12
+    # the bound is the side the call's arithmetic intensity puts it on: matrix cores when
+    # its flops per algorithmic byte exceed the ratio of the two peaks (2500e12 / 8000e9)
+    mfma_bound = flops_attn / bytes_attn > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    roofline = {"bound": "mfma" if mfma_bound else "hbm",
+                "kernel": "tree-verify attention (split + merge kernels)",
+                "achieved": round(tflops, 1) if mfma_bound else round(gbs, 1),
+                "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+                "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                "frac": round(tflops / BF16_PEAK_TFLOPS if mfma_bound else gbs / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(w.name),
+                "bytes_per_launch": bytes_attn, "flops_per_launch": flops_attn,
+                "us_per_launch": round(ms_attn * 1e3, 2),
+                "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "mfma_tflops": round(tflops, 1),
+                "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
     bytes_argmax = w.B * w.T * w.V * 4
     tokens = w.B * w.T
     result = {
@@ -335,12 +350,7 @@ def main():
                    "num_splits": args.splits, "seed": args.seed,
                    "sampled_temperature": w.temperature, "draft_topk": d_k,
                    "draft_levels": d_levels},
-        "roofline": {"bound": "hbm", "kernel": "tree-verify attention (split + merge kernels)",
-                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(w.name),
-                     "bytes_per_launch": bytes_attn, "us_per_launch": round(ms_attn * 1e3, 2),
-                     "mfma_tflops": round(tflops, 1),
-                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
         "stages_us": stages,
         "accepted_tokens_per_step": int(st.accepted_len.sum()),
         "argmax_gbs": round(bytes_argmax / (stages["accept"] * 1e-6) / 1e9, 1),
