@@ -193,7 +193,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the clock takes ~30 steps (~35 ms) to settle at the board's power limit; the first
+    # steps after idle run ~5% slower
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
