@@ -79,14 +79,18 @@ __global__ __launch_bounds__(256) void softmax_partial_kernel(const float *__res
     const int64_t nvec = (a1 - a0) >> 2;
     int64_t i = tid;
     for (; i + 3 * 256 < nvec; i += 4 * 256) {  // four 16-byte loads in flight per thread
-        const f32x4 x0 = vp[i], x1 = vp[i + 256], x2 = vp[i + 512], x3 = vp[i + 768];
+        // non-temporal: every logit is read once here (the draw re-reads one chunk)
+        const f32x4 x0 = __builtin_nontemporal_load(vp + i),
+                    x1 = __builtin_nontemporal_load(vp + i + 256),
+                    x2 = __builtin_nontemporal_load(vp + i + 512),
+                    x3 = __builtin_nontemporal_load(vp + i + 768);
         for (int j = 0; j < 4; ++j) ms_add(a, x0[j], k);
         for (int j = 0; j < 4; ++j) ms_add(a, x1[j], k);
         for (int j = 0; j < 4; ++j) ms_add(a, x2[j], k);
         for (int j = 0; j < 4; ++j) ms_add(a, x3[j], k);
     }
     for (; i < nvec; i += 256) {
-        const f32x4 x0 = vp[i];
+        const f32x4 x0 = __builtin_nontemporal_load(vp + i);
         for (int j = 0; j < 4; ++j) ms_add(a, x0[j], k);
     }
     if (a1 + tid < hi) ms_add(a, rp[a1 + tid], k);

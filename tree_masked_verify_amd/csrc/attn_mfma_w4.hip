@@ -87,14 +87,14 @@ __device__ __forceinline__ int key_offset(int r, int u) { return (r & 15) * u + 
 
 // A unit load: every lane of the wavefront with D = 256, lanes 0-31 with D = 128 (the
 // others would write past the unit).
-template <int D>
+template <int D, bool kNT = false>
 __device__ __forceinline__ void unit_load(const unsigned char *src, uint32_t lds) {
-    if (Geo<D>::LPK == 32 || (threadIdx.x & 63) < 2 * Geo<D>::LPK) dma16(src, lds);
+    if (Geo<D>::LPK == 32 || (threadIdx.x & 63) < 2 * Geo<D>::LPK) dma16<kNT>(src, lds);
 }
 
-template <int D>
+template <int D, bool kNT>
 __device__ __forceinline__ void load_unit_d(const TileLoad &t, int j) {
-    unit_load<D>(t.src + j * t.step, t.lds + j * t.ustride);
+    unit_load<D, kNT>(t.src + j * t.step, t.lds + j * t.ustride);
 }
 
 // Issues the whole tree tile (rows past the last node read the last node, masked); the
@@ -377,7 +377,7 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[2][Geo<D>::DB], const RowSta
     }
 }
 
-template <int D, bool kInCache>
+template <int D, bool kInCache, bool kNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_w4_kernel(MfmaParams p) {
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -562,7 +562,7 @@ void attn_w4_kernel(MfmaParams p) {
     // the NI loads of the prepared tile go between the k-steps of the score product
     auto load_in_scores = [&](int k) {
         constexpr int every = KS / NI;
-        if (k % every == 0 && tl.spread) load_unit_d<D>(tl, k / every);
+        if (k % every == 0 && tl.spread) load_unit_d<D, kNT>(tl, k / every);
     };
 
     // ---- iteration u: the score product of tile u (the hook issues loads between its
@@ -591,7 +591,7 @@ void attn_w4_kernel(MfmaParams p) {
         prepare(k + ahead);
         if (tl.spread)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) load_unit_d<D>(tl, j);
+            for (int j = 0; j < NI; ++j) load_unit_d<D, kNT>(tl, j);
     }
     int u = 0;
     if (staged && all_ok) {
@@ -615,7 +615,7 @@ void attn_w4_kernel(MfmaParams p) {
                 cur_c, uu,
                 [&](int k) {
                     constexpr int every = KS / NI;
-                    if (k % every == 0) load_unit_d<D>(f, k / every);
+                    if (k % every == 0) load_unit_d<D, kNT>(f, k / every);
                 },
                 false, 0u, false, 0);
         };
@@ -696,7 +696,10 @@ template <int D>
 hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     using namespace w4;
     constexpr int SMEM = Geo<D>::SMEM;
-    const auto kernel = a.k_tree ? attn_w4_kernel<D, false> : attn_w4_kernel<D, true>;
+    // one row group per kv head: each workgroup streams its keys alone (non-temporal loads)
+    const bool nt = pl.n_rg == 1;
+    const auto kernel = a.k_tree ? (nt ? attn_w4_kernel<D, false, true> : attn_w4_kernel<D, false, false>)
+                                 : (nt ? attn_w4_kernel<D, true, true> : attn_w4_kernel<D, true, false>);
     hipError_t e = hipFuncSetAttribute((const void *)kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     if (e != hipSuccess) return e;

@@ -381,7 +381,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     for (int64_t base = 0; base < nfull; base += kTrip) {
         f32x4 raw[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) raw[u] = vp[base + u * kTkThreads + tid];
+        for (int u = 0; u < 4; ++u)  // non-temporal: every logit is read once
+            raw[u] = __builtin_nontemporal_load(vp + base + u * kTkThreads + tid);
         refresh_shared(wc);
         float mx[4];
 #pragma unroll
