@@ -172,7 +172,12 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  *   out     float32 [B][T][Hq][D]   (layout [q_seq_len, num_heads, head_dim] per sequence)
  *   scale   softmax scale, usually 1/sqrt(D); must be positive and finite
  *   workspace  device, >= sv_tree_verify_attention_workspace_size(...) bytes,
- *              256-byte aligned; scratch for per-split partial results
+ *              256-byte aligned; scratch for per-split partial results.  Its first
+ *              256 KiB hold arrival counters of the chunk merge: they must be zero
+ *              before the first call on a workspace (allocate it zero-filled, or clear
+ *              it once), and every call leaves them zero again.  Do not write that
+ *              region between calls; calls that share a workspace must not overlap
+ *              in time (same stream, or ordered).
  *   num_splits 0 = automatic; otherwise the number of prefix chunks per sequence.
  *              Automatic splitting at head_dim 128 / 256 with bf16 may size the chunks
  *              from prefix_len on the device (so that sequences of different lengths
@@ -181,6 +186,14 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  * Arithmetic: bf16 (or fp32) operands, fp32 accumulation; the result matches
  * the exact softmax attention to within bf16 rounding of the probabilities.
  * Prefix rows whose block-table entry is outside [0, num_blocks) are left out.
+ * Non-finite values: q, k_tree, v_tree and the cache rows a row attends to must be
+ * finite (every tree row is attended to by its own node).  Anything else the cache
+ * holds -- rows at positions >= P_b, blocks the table does not reach, the block an
+ * out-of-range entry would have named -- may be anything, NaN included, without
+ * affecting any output.  A non-finite value in an attended row gives an
+ * unspecified (typically NaN) output for the rows that attend to it, and, on the
+ * matrix-core paths (bf16, >= 16 query rows per kv head), possibly for the other
+ * rows of the same sequence and kv head (0 * inf in the weighted sum).
  * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, max_prefix_len < 0, block_size not a
  * positive multiple of 16, num_splits < 0, strides not positive, scale not
  * positive and finite),

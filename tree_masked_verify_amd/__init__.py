@@ -258,5 +258,6 @@ def sv_status_string(code: int) -> str:
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A device byte buffer of at least nbytes (256-byte aligned by the allocator)."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A zero-filled device byte buffer of at least nbytes (256-byte aligned by the
+    allocator); the attention call needs the start of its workspace zero before first use."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)

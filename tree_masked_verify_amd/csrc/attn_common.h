@@ -30,7 +30,11 @@ struct MfmaParams {
     int balanced;          // chunks cut from the actual prefix lengths, largest first
     float *ws_o;
     float *ws_ml;
-    int32_t *ws_c;         // where a balanced call leaves its chunk length
+    int32_t *ws_c;         // where a balanced call leaves its chunk length (separate merge)
+    float *out;            // [B][T][Hq][D]
+    int D;
+    int32_t *counters;     // arrivals per (sequence, kv head, row group); NULL: the
+                           // separate merge kernel combines the chunks
 };
 
 // Tree rows kept in the cache (no tree buffers given): byte address of tree row r of
@@ -60,6 +64,14 @@ __device__ __forceinline__ int xcd_logical_id() {
 }
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// A pointer that is the same in every lane, made visibly uniform (kept in SGPRs).
+__device__ __forceinline__ const unsigned char *uni_ptr(const unsigned char *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const unsigned char *>(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ int clamp_prefix(int P, int max_P) {
     return P < 0 ? 0 : (P > max_P ? max_P : P);
@@ -243,6 +255,7 @@ __device__ __forceinline__ int lookup_entry(const MfmaParams &p, int b, BlockLoo
 struct TileBlocks {
     int blk[2];
     int slot[2];
+    bool ok[2];  // the group's block-table entry is in range
 };
 
 __device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, BlockLookup &bl,
@@ -251,8 +264,10 @@ __device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, 
     const int e0 = lookup_entry(p, b, bl, c.idx);
     tb.blk[0] = e0 < 0 ? 0 : e0;
     tb.slot[0] = c.slot;
+    tb.ok[0] = e0 >= 0;
     tb.blk[1] = tb.blk[0];
     tb.slot[1] = c.slot;
+    tb.ok[1] = tb.ok[0];
     if (k0 + 16 < kend) {
         // c.slot is a multiple of 16 below the block size (also a multiple of 16)
         if (c.slot + 16 < p.bs) {
@@ -261,6 +276,7 @@ __device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, 
             const int e1 = lookup_entry(p, b, bl, c.idx + 1);
             tb.blk[1] = e1 < 0 ? 0 : e1;
             tb.slot[1] = 0;
+            tb.ok[1] = e1 >= 0;
         }
     }
     return tb;
@@ -270,18 +286,29 @@ __device__ __forceinline__ TileBlocks lookup_blocks(const MfmaParams &p, int b, 
 // (first unit + j) of the wavefront's tensor from row j (counted from each lane's first
 // row) of the source.  Prefix tiles are issued one load at a time between matrix
 // products of the tile before; tree tiles (rows past the last node clamped to it) and
-// the trailing repeat slots are issued whole when prepared.  Wavefronts 0-3 load K,
-// 4-7 load V, a quarter of the units each.
+// the trailing repeat slots are issued whole when prepared.
+//
+// A row that holds no key of the sequence (past the chunk end, in a block whose table
+// entry is out of range, or a repeat slot) is read from `alt` instead: tree row 0 of
+// the same kv head, an input the caller guarantees finite.  Such keys get probability 0,
+// and a product 0 * v is 0 only for finite v, so reading whatever the cache holds there
+// (possibly NaN) could otherwise leak into the output.
 struct TileLoad {
     const unsigned char *src;   // per lane: its 16 bytes of the first row
     int64_t step;               // bytes between successive rows
     uint32_t lds;               // LDS address of the first unit
     int ustride;                // bytes between units
     bool spread;                // loads still to be issued one by one
+    int nvalid;                 // per lane: rows 0 .. nvalid-1 come from src, the rest from alt
+    const unsigned char *alt;   // per lane: its 16 bytes of a finite row
 };
 
+__device__ __forceinline__ const unsigned char *load_src(const TileLoad &t, int j) {
+    return j < t.nvalid ? t.src + j * t.step : t.alt;
+}
+
 __device__ __forceinline__ void load_unit(const TileLoad &t, int j) {
-    dma16(t.src + j * t.step, t.lds + j * t.ustride);
+    dma16(load_src(t, j), t.lds + j * t.ustride);
 }
 
 // Validity of the 32 keys of a prefix tile starting at cursor c (bit kk: key k0 + kk

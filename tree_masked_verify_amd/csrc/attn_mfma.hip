@@ -1,6 +1,6 @@
 // attn_mfma.hip -- tree-masked split-KV attention on the gfx950 matrix cores (bf16 in,
-// fp32 accumulate), for kv heads whose (GQA group x tree nodes) query rows fill at
-// least one 16-row tile.
+// fp32 accumulate) at head_dim 512, for kv heads whose (GQA group x tree nodes) query
+// rows fill at least one 16-row tile.  (head_dim 128 and 256: attn_mfma_w4.hip.)
 //
 // What is computed (ADR-037 Phase status rows E1.1-E1.5, section 4 Phase E1;
 // Medusa/EAGLE-2 page "What's not implemented" 1(c)): every query row (q head g of
@@ -10,8 +10,8 @@
 // output and its (reference max, sum) per row, merged afterwards by attn_reduce.
 //
 // Organisation (8 wavefronts per workgroup, two per SIMD, one workgroup per CU):
-//   * a wavefront owns 32 query rows as two 16-row blocks (with head_dim 512, two
-//     wavefronts share them, each with half of head_dim); their Q fragments stay in
+//   * a wavefront owns 32 query rows as two 16-row blocks, shared with a second
+//     wavefront that takes the other half of head_dim; their Q fragments stay in
 //     registers and the wavefront owns their output accumulators;
 //   * keys stream through an NST-deep ring of LDS stages, 32 keys of K and V per
 //     stage, filled by direct global->LDS loads (global_load_lds_dwordx4) issued
@@ -19,8 +19,8 @@
 //   * scores are formed transposed, S^T = K Q^T, as 2 x 2 blocks of
 //     v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows each): four independent
 //     accumulation chains.  A lane holds 8 of a row's 32 keys, so the row max takes
-//     two lane swaps; with head_dim 512 the two partial score tiles are summed
-//     through LDS first;
+//     two lane swaps; the two half-head_dim partial score tiles of a wavefront pair
+//     are summed through LDS first;
 //   * the output is accumulated transposed, O^T = V^T P^T, in 16 x 16 blocks, so a
 //     lane keeps the accumulators of the rows it computed probabilities for; the key
 //     order inside the 32-key step follows the score registers, so the P^T fragment is
@@ -30,8 +30,6 @@
 //     (ds_read_b128, 16 lanes per LDS cycle) and the V fragment reads (32 lanes per
 //     cycle) each touch 64 distinct banks, and every fragment address is one base
 //     register plus an immediate;
-//   * with head_dim 256 the wavefronts run in two groups half a tile apart
-//     (ping-pong), so one wavefront's softmax overlaps the other's matrix work;
 //   * the reference max only moves when a tile raises it by more than 2^8, so the
 //     accumulators are rarely rescaled (the merged result does not depend on the
 //     reference values used).
@@ -44,70 +42,75 @@ constexpr int kWaves = 8;
 
 template <int D>
 struct MCfg {
-    static constexpr int DSPLIT = D / 256;          // wavefronts sharing 32 rows
+    static_assert(D == 512, "head_dim 512 (128 and 256: attn_mfma_w4.hip)");
+    static constexpr int DSPLIT = 2;                // wavefronts sharing 32 rows
     static constexpr int DW = D / DSPLIT;           // head_dim share of one wavefront
     static constexpr int KS = DW / 32;              // 32-wide k-steps of S^T = K Q^T
     static constexpr int DB = DW / 16;              // 16-wide d blocks of O^T
     // An LDS tile is made of 1 KB units, each filled by one wavefront-wide direct load:
-    // with head_dim 256 unit p holds keys p and p + 16 of the tile side by side, with
-    // head_dim 512 unit p holds key p.  Units are padded (K by 16 bytes, V by 32) so
-    // that the fragment reads touch 64 distinct banks.
-    static constexpr int UNITS = kKeyTile * D * 2 / 1024;    // 16 or 32
+    // unit p holds key p.  Units are padded (K by 16 bytes, V by 32) so that the
+    // fragment reads touch 64 distinct banks.
+    static constexpr int UNITS = kKeyTile * D * 2 / 1024;    // 32
     static constexpr int KU = 1024 + 16;
     static constexpr int VU = 1024 + 32;
-    static constexpr int KHALF = D == 256 ? 512 : 16 * KU;   // key r + 16 relative to key r
-    static constexpr int VHALF = D == 256 ? 512 : 16 * VU;
+    static constexpr int KHALF = 16 * KU;                    // key r + 16 relative to key r
+    static constexpr int VHALF = 16 * VU;
     static constexpr int KTILE = UNITS * KU;
     static constexpr int STAGE_BYTES = UNITS * (KU + VU);    // K tile then V tile
-    static constexpr int NST = D == 256 ? 4 : 2;             // ring depth
-#ifndef SV_ATTN_PINGPONG
-#define SV_ATTN_PINGPONG 1
-#endif
-    // ping-pong scheduling needs no workgroup-wide barrier inside a tile, so not with
-    // the paired score exchange of DSPLIT = 2
-    static constexpr bool PINGPONG = SV_ATTN_PINGPONG && DSPLIT == 1;
-    static constexpr int LOOK = PINGPONG ? NST - 2 : NST - 1;   // tiles loaded ahead
-    static constexpr int NI = 2 * UNITS / kWaves;               // loads per wavefront per tile
-    static constexpr int VMWAIT = NI * (LOOK - 1);              // loads left in flight at a wait
+    static constexpr int NST = 2;                            // ring depth
+    static constexpr int LOOK = NST - 1;                     // tiles loaded ahead
+    static constexpr int NI = 2 * UNITS / kWaves;            // loads per wavefront per tile
+    static constexpr int VMWAIT = NI * (LOOK - 1);           // loads left in flight at a wait
     static constexpr int ROWS_PER_WG = kWaves / DSPLIT * 32;
-    static constexpr int XBYTES = DSPLIT > 1 ? kWaves / 2 * 64 * 16 * 4 : 0;  // score exchange
+    static constexpr int XBYTES = kWaves / 2 * 64 * 16 * 4;  // score exchange
     static constexpr int TBL_OFF = NST * STAGE_BYTES + XBYTES;  // staged block-table entries
     static constexpr int MASK_OFF = TBL_OFF + kTblMax * 4;      // ancestor-mask rows
     static constexpr int SMEM = MASK_OFF + ROWS_PER_WG * 8;
     static_assert(KS % NI == 0 || NI % KS == 0, "load spacing");
 };
 
-// Lane layout of a load: with head_dim 256 lanes 0-31 carry key p, 32-63 key p + 16
-// (16 bytes each); with head_dim 512 all 64 lanes carry key p.
-template <int D>
-__device__ __forceinline__ int load_lane_half(int q) {
-    return D == 256 ? (int)((threadIdx.x & 63) >> 5) : (q >> 1);
+// Lane layout of a load: all 64 lanes carry one key row (16 bytes each); wavefront q of
+// a tensor loads keys 8 q .. 8 q + 7 of the tile, i.e. group q / 2.
+__device__ __forceinline__ int load_lane_piece() { return (int)(threadIdx.x & 63); }
+
+// Per lane: its 16 bytes of tree row 0 of kv head kvh (finite by the caller's contract),
+// read in place of rows that hold no key.
+template <int D, bool kInCache>
+__device__ __forceinline__ const unsigned char *finite_row(const MfmaParams &p, int b, int kvh,
+                                                           int P, int tensor) {
+    if constexpr (kInCache)
+        return tree_row_in_cache(reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
+                                     load_lane_piece() * 16,
+                                 p, b, kvh, P, 0);
+    return reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
+           ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) + load_lane_piece() * 16;
 }
 
-template <int D>
-__device__ __forceinline__ int load_lane_piece() {
-    return D == 256 ? (int)(threadIdx.x & 31) : (int)(threadIdx.x & 63);
-}
-
+// This wavefront's loads of prefix tile k0 (chunk ending at `end`): rows past the end
+// or in a block whose table entry is out of range read `alt`.
 template <int D>
 __device__ __forceinline__ TileLoad prepare_prefix(const MfmaParams &p, int kvh, const TileBlocks &tb,
+                                                   int k0, int end, const unsigned char *alt,
                                                    uint32_t stage) {
     using Cf = MCfg<D>;
     const int w = uni(threadIdx.x >> 6);
     const int tensor = w >> 2;  // 0: K, 1: V
     const int q = w & 3;
-    const int half = load_lane_half<D>(q);
+    const int half = q >> 1;
     const int blk = half ? tb.blk[1] : tb.blk[0];
     // keys of one group stay inside its block: slot + 15 < block size
-    const int row = (half ? tb.slot[1] : tb.slot[0]) + (D == 256 ? 4 * q : 8 * (q & 1));
+    const int row = (half ? tb.slot[1] : tb.slot[0]) + 8 * (q & 1);
+    const int left = end - (k0 + 8 * q);
     TileLoad t;
     t.src = reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
             ((int64_t)blk * p.bstride + (int64_t)kvh * p.hstride + (int64_t)row * p.rstride) * 2 +
-            load_lane_piece<D>() * 16;
+            load_lane_piece() * 16;
     t.step = p.rstride * 2;
     t.ustride = tensor ? Cf::VU : Cf::KU;
     t.lds = stage + (tensor ? Cf::KTILE : 0) + q * Cf::NI * t.ustride;
     t.spread = true;
+    t.nvalid = (half ? tb.ok[1] : tb.ok[0]) ? (left < 0 ? 0 : (left > Cf::NI ? Cf::NI : left)) : 0;
+    t.alt = alt;
     return t;
 }
 
@@ -121,13 +124,13 @@ __device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int k
     const int w = uni(threadIdx.x >> 6);
     const int tensor = w >> 2;
     const int q = w & 3;
-    const int row = k0 + (D == 256 ? 4 * q + 16 * load_lane_half<D>(q) : 8 * q);
+    const int row = k0 + 8 * q;
     TileLoad t;
     t.ustride = tensor ? Cf::VU : Cf::KU;
     t.lds = stage + (tensor ? Cf::KTILE : 0) + q * Cf::NI * t.ustride;
     if constexpr (kInCache) {
         const unsigned char *pool = reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc) +
-                                    load_lane_piece<D>() * 16;
+                                    load_lane_piece() * 16;
 #pragma unroll
         for (int j = 0; j < Cf::NI; ++j)
             dma16(tree_row_in_cache(pool, p, b, kvh, P, min(row + j, p.T - 1)),
@@ -136,7 +139,7 @@ __device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int k
     } else {
         const unsigned char *base = reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
                                     ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2) +
-                                    load_lane_piece<D>() * 16;
+                                    load_lane_piece() * 16;
 #pragma unroll
         for (int j = 0; j < Cf::NI; ++j)
             dma16(base + (int64_t)min(row + j, p.T - 1) * (D * 2), t.lds + j * t.ustride);
@@ -144,6 +147,8 @@ __device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int k
     }
     t.step = 0;
     t.spread = false;
+    t.nvalid = Cf::NI;
+    t.alt = t.src;
     return t;
 }
 
@@ -156,13 +161,8 @@ struct RowState {
     float lsum[2];
 };
 
-#ifndef SV_ATTN_PERMLANE
-#define SV_ATTN_PERMLANE 1
-#endif
-
 // Max over the four 16-lane groups (lanes n, n + 16, n + 32, n + 48 end up equal).
 __device__ __forceinline__ float max_over_groups(float m) {
-#if SV_ATTN_PERMLANE
     // gfx950 row swaps: permlane16_swap exchanges rows 1 and 3 of its first operand
     // with rows 0 and 2 of its second, permlane32_swap the upper half of the first with
     // the lower half of the second; with both operands equal, the two results hold the
@@ -173,10 +173,6 @@ __device__ __forceinline__ float max_over_groups(float m) {
     const unsigned v = __float_as_uint(m);
     const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-#else
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    return fmaxf(m, __shfl_xor(m, 32, 64));
-#endif
 }
 
 // First half of a tile: scores, mask, online softmax (rescaling the accumulators when
@@ -213,7 +209,7 @@ __device__ __forceinline__ void tile_scores(const unsigned char *ks, float *xs, 
             sacc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[rb][kstep], sacc[rb][1], 0, 0, 0);
         }
     }
-    if (Cf::DSPLIT > 1) {
+    {
         // sum the two partial score tiles of a wavefront pair (same rows, halves of
         // head_dim): the second half hands its scores over, the first adds and hands
         // the sum back, so both hold bit-identical scores
@@ -310,7 +306,6 @@ __device__ __forceinline__ void tile_pv(const unsigned char *vs, int dpart,
 template <int D, bool kInCache>
 __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
     using Cf = MCfg<D>;
-    static_assert(Cf::NST == 2 || Cf::NST == 4, "ring depth");
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     float *xs = reinterpret_cast<float *>(smem + Cf::NST * Cf::STAGE_BYTES);
 
@@ -405,12 +400,14 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
     const uint32_t smem0 = lds_addr(smem);
     Cursor cissue = cstart;   // prefix tile whose block entries tbn holds
     Cursor ccomp = cstart;    // next prefix tile to compute
-    TileBlocks tbn = ntp > 0 ? lookup_blocks(p, b, bl, cissue, start, end) : TileBlocks{{0, 0}, {0, 0}};
+    TileBlocks tbn = ntp > 0 ? lookup_blocks(p, b, bl, cissue, start, end)
+                             : TileBlocks{{0, 0}, {0, 0}, {false, false}};
+    const unsigned char *alt = finite_row<D, kInCache>(p, b, kvh, P, uni(threadIdx.x >> 6) >> 2);
     TileLoad tl;
     auto prepare = [&](int k) {
         const uint32_t stage = smem0 + (k % Cf::NST) * Cf::STAGE_BYTES;
         if (k < ntp) {
-            tl = prepare_prefix<D>(p, kvh, tbn, stage);
+            tl = prepare_prefix<D>(p, kvh, tbn, start + k * kKeyTile, end, alt, stage);
             cissue = cursor_add(cissue, kKeyTile, p.bs);
             if (k + 1 < ntp) tbn = lookup_blocks(p, b, bl, cissue, start + (k + 1) * kKeyTile, end);
         } else if (k < nt) {
@@ -427,18 +424,13 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
             for (int j = 0; j < Cf::NI; ++j) load_unit(tl, j);
     };
     auto nohook = [](int) {};
-    // spread the NI loads of the prepared tile over the k-steps of a score product ...
+    // spread the NI loads of the prepared tile over the k-steps of a score product
     auto load_in_scores = [&](int kstep) {
         constexpr int every = Cf::KS >= Cf::NI ? Cf::KS / Cf::NI : 1;
         constexpr int per = Cf::NI > Cf::KS ? Cf::NI / Cf::KS : 1;
         if (kstep % every == 0 && tl.spread)
 #pragma unroll
             for (int j = 0; j < per; ++j) load_unit(tl, kstep / every * per + j);
-    };
-    // ... or over the d blocks of a PV product
-    auto load_in_pv = [&](int db) {
-        constexpr int every = Cf::DB / Cf::NI;
-        if (db % every == 0 && tl.spread) load_unit(tl, db / every);
     };
     auto scores = [&](int u, auto &&hook) {
         const unsigned char *stg = smem + (u % Cf::NST) * Cf::STAGE_BYTES;
@@ -460,43 +452,12 @@ __global__ __launch_bounds__(512) void attn_mfma_kernel(MfmaParams p) {
     };
 
     for (int k = 0; k < Cf::LOOK; ++k) issue(k);   // ring prologue
-    if (Cf::PINGPONG) {
-        // Wavefronts 4-7 run half a tile behind 0-3: barrier k sits at the start of
-        // tile k for the first group and between the softmax and the PV product of
-        // tile k-1 for the second, so on every SIMD one wavefront's vector work
-        // overlaps the other's matrix work.  After barrier k the stages of tiles k-1
-        // and k may still be read, so loads run two tiles ahead (stage of tile k-2),
-        // issued by the first group during its score product and by the second during
-        // its PV product.
-        if (w < 4) {
-            for (int u = 0; u < nt; ++u) {
-                wait_loads<Cf::VMWAIT>();
-                lds_barrier();
-                prepare(u + Cf::LOOK);
-                scores(u, load_in_scores);
-                pv(u, nohook);
-            }
-            lds_barrier();  // matches the second group's last barrier
-        } else {
-            wait_loads<Cf::VMWAIT>();
-            lds_barrier();
-            issue(Cf::LOOK);
-            for (int u = 0; u < nt; ++u) {
-                scores(u, nohook);
-                wait_loads<Cf::VMWAIT>();
-                lds_barrier();
-                prepare(u + 1 + Cf::LOOK);
-                pv(u, load_in_pv);
-            }
-        }
-    } else {
-        for (int u = 0; u < nt; ++u) {
-            wait_loads<Cf::VMWAIT>();
-            lds_barrier();  // tile u visible to all; stage of tile u-1 free for reuse
-            prepare(u + Cf::LOOK);
-            scores(u, load_in_scores);
-            pv(u, nohook);
-        }
+    for (int u = 0; u < nt; ++u) {
+        wait_loads<Cf::VMWAIT>();
+        lds_barrier();  // tile u visible to all; stage of tile u-1 free for reuse
+        prepare(u + Cf::LOOK);
+        scores(u, load_in_scores);
+        pv(u, nohook);
     }
     wait_loads<0>();  // the trailing repeat loads
 
@@ -563,20 +524,12 @@ hipError_t launch_d(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
 
 }  // namespace
 
-bool attn_w4_handles(int D) {
-#ifndef SV_ATTN_LEGACY256
-    if (D == 256) return true;
-#endif
-    return D == 128;
-}
+bool attn_w4_handles(int D) { return D == 128 || D == 256; }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
-    if (a.D == 128) return launch_attn_w4(a, pl, stream);
-#ifndef SV_ATTN_LEGACY256
-    if (a.D == 256) return launch_attn_w4(a, pl, stream);
-#endif
-    return a.D == 256 ? launch_d<256>(a, pl, stream) : launch_d<512>(a, pl, stream);
+    if (attn_w4_handles(a.D)) return launch_attn_w4(a, pl, stream);
+    return launch_d<512>(a, pl, stream);
 }
 
 }  // namespace sv

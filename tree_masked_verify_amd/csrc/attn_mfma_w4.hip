@@ -38,13 +38,8 @@ namespace {
 
 namespace w4 {
 
-#ifndef SV_W4_KD
-#define SV_W4_KD 5  // K fragments read ahead (k-steps)
-#endif
-#ifndef SV_W4_VD
-#define SV_W4_VD 4  // V fragments read ahead (d blocks)
-#endif
-
+constexpr int kKD = 5;                   // K fragments read ahead (k-steps)
+constexpr int kVD = 4;                   // V fragments read ahead (d blocks)
 constexpr int kW = 4;                    // wavefronts per workgroup
 constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerWG = kW * kRowsPerWave;
@@ -75,7 +70,8 @@ struct Geo {
     static constexpr int STAGE_BYTES = UNITS * (KU + VU);
     static constexpr int GTAB_OFF = NST * STAGE_BYTES;
     static constexpr int MASK_OFF = GTAB_OFF + kGrpMax * 4;
-    static constexpr int SMEM = MASK_OFF + kRowsPerWG * 8;
+    static constexpr int FLAG_OFF = MASK_OFF + kRowsPerWG * 8;  // the merge's arrival flag
+    static constexpr int SMEM = FLAG_OFF + 16;
     static_assert(D == 128 || D == 256, "head_dim 128 or 256");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     static_assert((KU % 256) == 16 && (VU % 256) == 64, "bank offsets");
@@ -94,7 +90,7 @@ __device__ __forceinline__ void unit_load(const unsigned char *src, uint32_t lds
 
 template <int D, bool kNT>
 __device__ __forceinline__ void load_unit_d(const TileLoad &t, int j) {
-    unit_load<D, kNT>(t.src + j * t.step, t.lds + j * t.ustride);
+    unit_load<D, kNT>(load_src(t, j), t.lds + j * t.ustride);
 }
 
 // Issues the whole tree tile (rows past the last node read the last node, masked); the
@@ -132,6 +128,8 @@ __device__ __forceinline__ TileLoad issue_tree(const MfmaParams &p, int b, int k
     }
     t.step = 0;
     t.spread = false;
+    t.nvalid = NI;
+    t.alt = t.src;
     return t;
 }
 
@@ -174,7 +172,7 @@ __device__ __forceinline__ void tile_scores(const unsigned char *ks, const bf16x
     const unsigned char *kb = ks + key_offset<D>(lane & 31, Geo<D>::KU) + (lane >> 5) * 16;
     // K fragments are read KD k-steps ahead of their products; the reads sit before the
     // tile loads the hook issues (which the compiler does not move reads across)
-    constexpr int KD = SV_W4_KD;
+    constexpr int KD = kKD;
     bf16x8 a[KD + 1];
 #pragma unroll
     for (int k = 0; k < KD; ++k) a[k] = *reinterpret_cast<const bf16x8 *>(kb + k * 32);
@@ -313,7 +311,7 @@ __device__ __forceinline__ void pv_tile(const unsigned char *vs, const bf16x8 (&
     const unsigned char *vb = vs + ((G >> 1) * 4 + r) * VU + (G & 1) * 32 + q * 8;
     // V^T fragments of the next VD (chunk, d block) steps are in flight while a step's
     // products run
-    constexpr int VD = SV_W4_VD;
+    constexpr int VD = kVD;
     constexpr int NSTEP = 2 * DB;
     bf16x8 v[VD + 1];
     auto read = [&](int i) {
@@ -377,6 +375,100 @@ __device__ __forceinline__ void rescale(f32x16 (&o)[2][Geo<D>::DB], const RowSta
     }
 }
 
+// Output row [b][i][h][:] of query row r (q head g = r / T of kv head kvh, node i).
+__device__ __forceinline__ float *out_row(const MfmaParams &p, int b, int kvh, int r) {
+    const int g = r / p.T;
+    const int i = r - g * p.T;
+    return p.out + (((int64_t)b * p.T + i) * p.Hq + (int64_t)kvh * p.G + g) * (int64_t)p.D;
+}
+
+// Device-coherent reads of what other workgroups (possibly on other XCDs) wrote: buffer
+// loads with the device-scope cache policy (sc1), through a resource covering `bytes`
+// from `base` (reads past it return 0).
+constexpr int kCoherent = 16;                       // sc1
+constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
+}
+
+// The merge of the nv chunks of one (sequence, kv head, row group), rows rbase and
+// rbase + 32 of this lane (its half h of each 8-wide d piece), from their partials:
+//   out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  M = max_c m_c,
+// over the chunks c in order, so the result does not depend on which chunk merges.
+// The loads go out in batches (four d blocks of two chunks at a time), so that the
+// merge waits for a few memory round trips, not one per piece.  The unit's partials
+// are nv * R rows from slot ubase (the launch keeps their bytes within 2^31).
+template <int D>
+__device__ __forceinline__ void merge_chunks(const MfmaParams &p, int b, int kvh, int64_t ubase,
+                                             int rbase, int nv) {
+    constexpr int DB = Geo<D>::DB;
+    constexpr int QB = DB < 4 ? DB : 4;  // d blocks per batch
+    const int h = (threadIdx.x & 63) >> 5;
+    const uint32_t rows = (uint32_t)nv * (uint32_t)p.R;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(p.ws_o + ubase * D, rows * D * 4);
+    const __amdgpu_buffer_rsrc_t rml = coherent_rsrc(p.ws_ml + ubase * 2, rows * 8);
+    const uint32_t cs = (uint32_t)p.R;  // slots between consecutive chunks
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = rbase + rb * 32;
+        if (row >= p.R) continue;
+        auto mref = [&](int c) { return coherent_load1(rml, ((uint32_t)c * cs + row) * 8); };
+        auto lsum = [&](int c) { return coherent_load1(rml, ((uint32_t)c * cs + row) * 8 + 4); };
+        float M = kNegInf;
+        for (int c = 0; c < nv; ++c) M = fmaxf(M, mref(c));
+        float L = 0.0f;
+        for (int c = 0; c < nv; ++c) {
+            const float m2 = mref(c);
+            const float wgt = m2 == kNegInf ? 0.0f : exp2f(m2 - M);
+            L += wgt * lsum(c);
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float *op = out_row(p, b, kvh, row) + 4 * h;
+#pragma unroll
+        for (int q = 0; q < DB / QB; ++q) {
+            f32x4 acc[QB][4];
+#pragma unroll
+            for (int d = 0; d < QB; ++d)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) acc[d][g4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < nv; c += 2) {
+                const bool two = c + 1 < nv;
+                const float m0 = mref(c);
+                const float m1 = two ? mref(c + 1) : kNegInf;
+                const float w0 = m0 == kNegInf ? 0.0f : exp2f(m0 - M);
+                const float w1 = m1 == kNegInf ? 0.0f : exp2f(m1 - M);
+                f32x4 v0[QB][4], v1[QB][4];
+#pragma unroll
+                for (int d = 0; d < QB; ++d)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const uint32_t e = (((uint32_t)c * cs + row) * D + (q * QB + d) * 32 + g4 * 8 + 4 * h) * 4;
+                        v0[d][g4] = coherent_load4(ro, e);
+                        v1[d][g4] = two ? coherent_load4(ro, e + cs * D * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+#pragma unroll
+                for (int d = 0; d < QB; ++d)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        acc[d][g4] += w0 * v0[d][g4];
+                        if (two) acc[d][g4] += w1 * v1[d][g4];
+                    }
+            }
+#pragma unroll
+            for (int d = 0; d < QB; ++d)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *reinterpret_cast<f32x4 *>(op + (q * QB + d) * 32 + g4 * 8) = acc[d][g4] * inv;
+        }
+    }
+}
+
 template <int D, bool kInCache, bool kNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_w4_kernel(MfmaParams p) {
@@ -388,7 +480,8 @@ void attn_w4_kernel(MfmaParams p) {
     int b, kvh, s, rg, C;
     if (p.balanced) {
         C = balanced_chunk_len(p);
-        if (blockIdx.x == 0 && threadIdx.x == 0) *p.ws_c = C;  // for the merge
+        // for the separate merge kernel (calls whose chunks are not merged in here)
+        if (!p.counters && blockIdx.x == 0 && threadIdx.x == 0) *p.ws_c = C;
         if (!balanced_item(p, C, &b, &kvh, &s, &rg)) return;
     } else {
         const int logical = xcd_logical_id();
@@ -534,6 +627,13 @@ void attn_w4_kernel(MfmaParams p) {
     const int64_t step = p.rstride * 2;
     // per lane: its 16 bytes of the wavefront's first row inside a group
     const int64_t lane_off = (int64_t)(8 * wq) * step + (lane % G::LPK) * 16;
+    // the first 16 bytes of tree row 0 of this kv head (finite by the caller's
+    // contract), read by every lane in place of rows that hold no key
+    const unsigned char *alt_w = uni_ptr(
+        kInCache ? tree_row_in_cache(reinterpret_cast<const unsigned char *>(tensor ? p.vc : p.kc),
+                                     p, b, kvh, P, 0)
+                 : reinterpret_cast<const unsigned char *>(tensor ? p.vt : p.kt) +
+                       ((int64_t)b * p.Hkv + kvh) * p.T * (D * 2));
     TileLoad tl;
     tl.ustride = ustride;
     auto prepare = [&](int k) {  // this wavefront's share of tile k (k >= -1)
@@ -542,19 +642,30 @@ void attn_w4_kernel(MfmaParams p) {
         if (k < ntp) {
             const int k0 = start + k * kKeyTile;
             int64_t off0, off1;
-            group_off(2 * k, off0);
+            const bool ok0 = group_off(2 * k, off0);
+            bool ok1 = false;
             if (k0 + 16 < end) {
-                group_off(2 * k + 1, off1);
+                ok1 = group_off(2 * k + 1, off1);
             } else {
-                off1 = off0;  // group past the chunk end: re-read group 0 (masked)
+                off1 = off0;  // group past the chunk end: no keys
             }
+            // rows of this lane's loads: keys first .. first + NI - 1 of the chunk
+            const int first = k0 + 16 * half + 8 * wq;
+            const int left = end - first;
+            tl.nvalid = (half ? ok1 : ok0) ? (left < 0 ? 0 : (left > NI ? NI : left)) : 0;
             tl.src = pool_w + (half ? off1 : off0) + lane_off;
+            tl.alt = alt_w;
             tl.step = step;
             tl.lds = stage + lds_w;
             tl.spread = true;
         } else if (k < nt) {
             tl = issue_tree<D, kInCache>(p, b, kvh, P, (k - ntp) * kKeyTile, stage);
         } else {
+            // repeat slot past the last tile (scores masked, probabilities 0)
+            tl.src = alt_w;
+            tl.alt = alt_w;
+            tl.nvalid = 0;
+            tl.step = 0;
             tl.lds = stage + lds_w;
             tl.spread = true;
         }
@@ -611,6 +722,8 @@ void attn_w4_kernel(MfmaParams p) {
             f.step = step;
             f.lds = smem0 + ((uu + ahead) & (NST - 1)) * STAGE_BYTES + lds_w;
             f.ustride = ustride;
+            f.nvalid = NI;  // full tiles in range: every row holds a key
+            f.alt = alt_w;
             iteration(
                 cur_c, uu,
                 [&](int k) {
@@ -623,7 +736,6 @@ void attn_w4_kernel(MfmaParams p) {
             fast(Set0{}, u);
             fast(Set1{}, u + 1);
         }
-        tl = TileLoad{pool_w + lane_off, step, 0u, ustride, true};  // repeat-slot source
     }
     auto generic = [&](auto cur_c, int uu) {
         wait_loads<VMWAIT>();
@@ -663,15 +775,31 @@ void attn_w4_kernel(MfmaParams p) {
     }
     wait_loads<0>();  // the trailing repeat loads
 
-    // ---- partial results: O (unnormalised), reference max (log2 units) and sum per row;
-    //      accumulator element r of block (rb, db) is d = 32 db + 8 (r / 4) + 4 h + r % 4
+    // ---- results.  Accumulator element r of block (rb, db) is d = 32 db + 8 (r / 4) + 4 h
+    //      + r % 4 of row row_base + 32 rb.  Each row has its reference max (log2 units;
+    //      -inf when it saw no key) and the sum of its weights.
+    float ltot[2], mfin[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float ltot = rs.lsum[rb] + __shfl_xor(rs.lsum[rb], 32, 64);
-        const int row = row_base + rb * 32;
+        ltot[rb] = rs.lsum[rb] + __shfl_xor(rs.lsum[rb], 32, 64);
+        mfin[rb] = rs.mref[rb] == kNoRef ? kNegInf : rs.mref[rb];
+    }
+    // recomputed here rather than kept live across the tile loop
+    int rbase = row_base;
+    asm volatile("" : "+v"(rbase));
+    // chunks of this sequence: chunk 0, and every later one that starts inside the prefix
+    const int64_t nv64 = P > 0 ? ((int64_t)P + C - 1) / C : 1;
+    const int nv = (int)(nv64 < 1 ? 1 : (nv64 > p.S ? p.S : nv64));
+    // the whole prefix in this chunk: the output goes straight to out (normalised
+    // below); otherwise the chunk's partial result (O unnormalised, reference max, sum)
+    const bool direct = p.counters && nv == 1;
+    const int64_t ubase = ((int64_t)b * p.Hkv + kvh) * p.S * (int64_t)p.R;  // slot (s, r): ubase + s R + r
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = rbase + rb * 32;
         if (row < p.R) {
-            const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
-            float *op = p.ws_o + base * D + 4 * h;
+            const int64_t base = ubase + (int64_t)s * p.R + row;
+            float *op = (direct ? out_row(p, b, kvh, row) : p.ws_o + base * D) + 4 * h;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -679,12 +807,59 @@ void attn_w4_kernel(MfmaParams p) {
                     *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8) =
                         f32x4{o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2],
                               o[rb][db][4 * g4 + 3]};
-            if (h == 0) {
-                p.ws_ml[base * 2 + 0] = rs.mref[rb] == kNoRef ? kNegInf : rs.mref[rb];
-                p.ws_ml[base * 2 + 1] = ltot;
+            if (!direct && h == 0) {
+                p.ws_ml[base * 2 + 0] = mfin[rb];
+                p.ws_ml[base * 2 + 1] = ltot[rb];
             }
         }
     }
+    if (direct) {
+        // O went out unnormalised (the accumulators are only ever read by stores, which
+        // keeps the allocator from moving them out of the accumulation registers); each
+        // lane now scales the lines it wrote, which are still in L2
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int row = rbase + rb * 32;
+            if (row < p.R) {
+                const float inv = ltot[rb] > 0.0f ? 1.0f / ltot[rb] : 0.0f;
+                float *op = out_row(p, b, kvh, row) + 4 * h;
+                f32x4 v[DB][4];  // all of the row's pieces in flight at once
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        v[db][g4] = *reinterpret_cast<const f32x4 *>(op + db * 32 + g4 * 8);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8) = v[db][g4] * inv;
+            }
+        }
+        return;
+    }
+    if (!p.counters) return;  // merged by the separate merge kernel
+
+    // The last of the nv chunks of this (sequence, kv head, row group) to finish merges
+    // them.  Each thread waits until its partial stores have reached L2; one thread then
+    // counts the arrival with a device-scope release (which writes this XCD's L2 back, so
+    // the partials are visible from every XCD).  The last arrival resets the counter for
+    // the next call and reads the partials with device-coherent loads, which need no L2
+    // invalidation (that would also evict the tiles other workgroups still share).
+    wait_loads<0>();
+    __syncthreads();
+    int *flag = reinterpret_cast<int *>(smem + G::FLAG_OFF);
+    if (threadIdx.x == 0) {
+        int32_t *cnt = p.counters + ((int64_t)b * p.Hkv + kvh) * p.n_rg + rg;
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == nv - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag) return;
+    merge_chunks<D>(p, b, kvh, ubase, rbase, nv);
 }
 
 }  // namespace w4
@@ -734,6 +909,9 @@ hipError_t launch_w4(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) 
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
     p.ws_c = a.ws_c;
+    p.out = a.out;
+    p.D = D;
+    p.counters = pl.fused ? a.ws_cnt : nullptr;
     // balanced: whole blocks (n_rg workgroups) per XCD and round, see balanced_item
     const int grid = pl.balanced
                          ? (a.B * pl.S * a.Hkv + kNumXCD - 1) / kNumXCD * kNumXCD * pl.n_rg

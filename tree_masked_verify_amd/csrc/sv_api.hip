@@ -108,27 +108,28 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     if (C < kKeyTile) C = kKeyTile;
     int64_t S = (max_prefix_len + C - 1) / C;
     if (S < 1) S = 1;
-    // Prefix lengths that differ leave one chunk per workgroup unbalanced: the w4 kernel
-    // then re-cuts the chunks from the actual lengths (one more chunk per sequence when
-    // the grid is already full) and starts the largest first.
+    // Prefix lengths that differ leave the chunks of a uniform cut unbalanced: when the
+    // prefixes are split at all, the w4 kernel re-cuts the chunks from the actual lengths
+    // and starts the largest first.  A grid that one chunk per sequence already fills is
+    // not split further: the calls run at the board's power limit, where evening out the
+    // finish times gains little and the partial results and their merge cost more.
     p->balanced = 0;
-    if (p->mfma && attn_w4_handles(D) && num_splits == 0) {
-        const int64_t S2 = (S == 1 && B > 1) ? 2 : S;
-        if ((int64_t)B * S2 <= kBalancedChunks) {
-            p->balanced = 1;
-            S = S2;
-        }
-    }
+    if (p->mfma && attn_w4_handles(D) && num_splits == 0 && S > 1 &&
+        (int64_t)B * S <= kBalancedChunks)
+        p->balanced = 1;
     p->C = (int)C;
     p->S = (int)S;
+    // in-kernel merge: the arrival counters must fit their region, and one unit's
+    // partials must stay within a 31-bit byte offset (the merge addresses them so)
+    p->fused = p->mfma && attn_w4_handles(D) && units <= kMaxMergeUnits &&
+               S * (int64_t)R * D * 4 < ((int64_t)1 << 31);
     int64_t work, o_elems, ml_elems;
     if (!prod_ok({units, S}, &work) || work > INT_MAX) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, D}, &o_elems)) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, 2}, &ml_elems)) return SV_ERR_OVERFLOW;
     p->ws_o = round256((size_t)o_elems * 4);
     p->ws_ml = round256((size_t)ml_elems * 4);
-    p->ws_hdr = 256;
-    p->ws_total = p->ws_o + p->ws_ml + p->ws_hdr;
+    p->ws_total = kCounterBytes + kHeaderBytes + p->ws_ml + p->ws_o;
     return SV_OK;
 }
 
@@ -213,12 +214,15 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
     a.D = D;
     a.scale = scale;
     a.out = out;
-    a.ws_o = static_cast<float *>(workspace);
-    a.ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.ws_o);
-    a.ws_c = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + plan.ws_o + plan.ws_ml);
+    char *ws = static_cast<char *>(workspace);
+    a.ws_cnt = reinterpret_cast<int32_t *>(ws);
+    a.ws_c = reinterpret_cast<int32_t *>(ws + kCounterBytes);
+    a.ws_ml = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes);
+    a.ws_o = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes + plan.ws_ml);
     hipError_t e = plan.mfma ? launch_attn_mfma(a, plan, stream)
                              : launch_attn_valu(a, plan, dtype, stream);
     if (e != hipSuccess) return SV_ERR_HIP;
+    if (plan.fused) return SV_OK;
     return hip_status(launch_attn_reduce(a, plan, stream));
 }
 

@@ -17,10 +17,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNumCU = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCD = 8;
 constexpr int kKeyTile = 32;    // keys per attention tile; split sizes are multiples of it
-#ifndef SV_ATTN_MAX_WAVES
-#define SV_ATTN_MAX_WAVES 8
-#endif
-constexpr int kAttnMaxWaves = SV_ATTN_MAX_WAVES;  // wavefronts per attention workgroup (<= 8)
+constexpr int kAttnMaxWaves = 8;  // wavefronts per attention workgroup
 
 // Paged cache as seen by a kernel (element strides).
 struct CacheView {
@@ -46,11 +43,22 @@ struct AttnPlan {
     int C;             // keys per chunk, multiple of kKeyTile (unless balanced)
     int balanced;      // 1: the kernel sizes chunks from the actual prefix lengths and
                        // starts the largest first (attn_w4 kernel, B * S <= kBalancedChunks)
-    size_t ws_o;       // bytes of partial outputs  [B][Hkv][S][R][D] fp32
+    int fused;         // 1: the attention kernel merges the chunks itself (attn_w4 kernel,
+                       // at most kMaxMergeUnits (sequence, kv head, row group) units);
+                       // 0: the separate merge kernel does
+    // Workspace layout: [arrival counters][header][partial (m, l)][partial O].  The
+    // counters sit at offset 0 in a region of fixed size, so that they stay where they
+    // were whatever the shapes of earlier calls on the same workspace.
     size_t ws_ml;      // bytes of partial (m, l)   [B][Hkv][S][R][2] fp32
-    size_t ws_hdr;     // bytes of the header: the chunk length a balanced call chose
+    size_t ws_o;       // bytes of partial outputs  [B][Hkv][S][R][D] fp32
     size_t ws_total;
 };
+
+// Arrival counters of the in-kernel merge: int32 per (sequence, kv head, row group), in
+// the first kCounterBytes of the workspace, zero before a call and zero after it.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr int64_t kMaxMergeUnits = kCounterBytes / 4;
+constexpr size_t kHeaderBytes = 256;  // the chunk length a balanced call chose
 
 // The most (sequence, chunk) pairs that a balanced call ranks by size.
 constexpr int kBalancedChunks = 128;
@@ -69,6 +77,7 @@ struct AttnArgs {
     float *ws_o;
     float *ws_ml;
     int32_t *ws_c;     // header: the chunk length of a balanced call
+    int32_t *ws_cnt;   // arrival counters of the in-kernel merge
 };
 
 // Returns 0 and fills *p, or a negative sv_status for unsupported shapes.
