@@ -60,6 +60,10 @@ def attention_error(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
     return float(err.max()), math.sqrt(float(np.mean(err * err))) / rms_ref
 
 
+def _bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
 def compare(g: dict, o: dict, rows=None, check_pools: bool = True) -> dict:
     assert np.array_equal(g["tree_err"], o["tree_err"]), (g["tree_err"], o["tree_err"])
     assert np.array_equal(g["mask"], o["mask"])
@@ -69,13 +73,13 @@ def compare(g: dict, o: dict, rows=None, check_pools: bool = True) -> dict:
     assert np.array_equal(g["nodes"], o["nodes"])
     assert np.array_equal(g["toks"], o["toks"])
     assert np.array_equal(g["npl"], o["npl"])
-    if check_pools:
-        assert np.array_equal(g["k_pool"], o["k_pool"]), "K pool differs after commit"
-        assert np.array_equal(g["v_pool"], o["v_pool"]), "V pool differs after commit"
+    if check_pools:  # byte for byte (NaN payloads included)
+        assert np.array_equal(_bits(g["k_pool"]), _bits(o["k_pool"])), "K pool differs after commit"
+        assert np.array_equal(_bits(g["v_pool"]), _bits(o["v_pool"])), "V pool differs after commit"
     got = g["out"]
+    assert np.all(np.isfinite(got)), "non-finite attention output"
     if rows is not None:
         got = np.stack([got[b, i, h] for b, h, i in rows])
-    assert np.all(np.isfinite(got))
     mx, rel = attention_error(got, o["out"])
     assert mx <= ATOL, f"attention max-abs error {mx}"
     assert rel <= REL_RMS, f"attention relative RMS error {rel}"

@@ -29,9 +29,11 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def run_case(orc, w, seed, num_splits=0, rows=None, **mk):
+def run_case(orc, w, seed, num_splits=0, rows=None, mutate=None, **mk):
     _say(f"[case] {w.name} seed={seed} splits={num_splits} B={w.B} T={w.T} D={w.D}")
     inp = wl.make_inputs(w, seed=seed, device=DEV, **mk)
+    if mutate is not None:
+        mutate(inp)
     h = host_copy(inp)
     g = gpu_step(inp, num_splits=num_splits)
     o = oracle_step(orc, inp, h, rows=rows)
@@ -58,13 +60,14 @@ def test_chain2k(orc, seed):
 
 
 def test_batched8k_full_size(orc):
-    w = wl.WORKLOADS["batched8k"]
-    run_case(orc, w, 0, rows=sample_rows(w, 48, 1))
+    """Every output row of the full batched workload (32 sequences, prefixes 4096-8192,
+    chunks cut from the actual lengths, merged inside the attention kernel)."""
+    run_case(orc, wl.WORKLOADS["batched8k"], 0)
 
 
 def test_long32k_full_size(orc):
-    w = wl.WORKLOADS["long32k"]
-    run_case(orc, w, 0, rows=sample_rows(w, 48, 2))
+    """Every output row of the full 32K workload (16 x 32 heads x 60 nodes)."""
+    run_case(orc, wl.WORKLOADS["long32k"], 0)
 
 
 # ----------------------------------------------------------------- reduced shapes, every row
@@ -88,14 +91,16 @@ def _rows_every_sequence(w):
                     dtype=np.int32)
 
 
-@pytest.mark.parametrize("B,splits", [(32, 0), (32, 2), (70, 0)])
+@pytest.mark.parametrize("B,splits", [(8, 0), (12, 0), (32, 0), (32, 2), (70, 0)])
 def test_varied_prefix_chunking(orc, B, splits):
     """The batched shape's heads with prefix lengths from 0 to 3000, some on either side of
-    the chunk boundary the kernel picks.  Automatic chunking at B = 32 (64 (sequence, chunk)
-    pairs) cuts the chunks from the actual lengths and starts the largest first; B = 70 and
-    an explicit split count keep the plan's uniform chunks.  Two rows of every sequence."""
+    a chunk boundary.  Automatic chunking at B = 8 and 12 (the grid needs several chunks per
+    sequence) cuts the chunks from the actual lengths, starts the largest first and merges
+    them inside the attention kernel; at B = 32 and 70 one chunk per sequence fills the
+    grid and each workgroup writes its rows' output directly; an explicit split count keeps
+    the plan's uniform chunks.  Two rows of every sequence."""
     rng = np.random.default_rng(B)
-    P = [3000, 0, 2999, 1, 2016, 2015, 2017, 32, 31, 33, 2000, 1500]  # chunk length 2016 at B = 32
+    P = [3000, 0, 2999, 1, 2016, 2015, 2017, 32, 31, 33, 2000, 1500][:B]
     P += [int(v) for v in rng.integers(1500, 3001, B - len(P))]
     w = wl.scaled(wl.WORKLOADS["batched8k"], name=f"varied{B}", B=B, prefix=(0, 3000), V=1000)
     run_case(orc, w, 5, num_splits=splits, rows=_rows_every_sequence(w), prefix_override=P)
@@ -163,6 +168,52 @@ def test_batched8k_head_dim_128(orc):
 
 
 def test_long32k_head_dim_128_full_size(orc):
-    """The 32K shape at head_dim 128, full size, sampled rows against the oracle."""
-    w = wl.WORKLOADS["long32k_d128"]
-    run_case(orc, w, 0, rows=sample_rows(w, 120, 9))
+    """The 32K shape at head_dim 128, full size, every row against the oracle."""
+    run_case(orc, wl.WORKLOADS["long32k_d128"], 0)
+
+
+# ----------------------------------------------------------------- head_dim 512, matrix cores
+def _d512(name, **kw):
+    base = dict(name=name, B=5, Hq=16, Hkv=2, T=8, tree="random", max_levels=4,
+                max_children=3, block_size=16, shuffled=True, prefix=(0, 2100), V=3000)
+    base.update(kw)
+    return wl.scaled(wl.WORKLOADS["chain2k"], **base)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_head_dim_512_paged_ragged(orc, splits):
+    """The head_dim-512 kernel on a paged cache: shuffled 16-row blocks, ragged prefixes
+    (0, 1, mid-tile ends), one out-of-range block-table entry, automatic and explicit
+    splits."""
+    P = [0, 1, 777, 2100, 1599]
+
+    def drop(inp):
+        inp.block_table[3, 5] = -1               # keys 80..95 of sequence 3 left out
+        inp.block_table[4, 50] = inp.num_blocks  # keys 800..815 of sequence 4 left out
+    run_case(orc, _d512("d512paged"), 31, num_splits=splits, mutate=drop, prefix_override=P)
+
+
+def test_head_dim_512_chunk_beyond_staged_table(orc):
+    """One chunk of 40000 keys in 16-row blocks (2500 table entries, more than the
+    kernel stages in LDS): its tiles read the block table directly."""
+    w = _d512("d512chunk40k", B=1, Hq=8, Hkv=1, prefix=(40000, 40000), tree="chain")
+    run_case(orc, w, 32, num_splits=1)
+
+
+# ----------------------------------------------------------------- vector-ALU instantiations
+def test_valu_bf16_head_dim_128_single_node(orc):
+    """bf16, head_dim 128, 8 query rows per kv head (< 16): the vector-ALU kernel."""
+    run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="t1-d128", D=128, T=1,
+                            tree="chain", prefix=(333, 333), capacity=352), 12)
+
+
+def test_valu_f32_head_dim_512(orc):
+    """fp32 at head_dim 512 (the tiny workload's tree): the vector-ALU kernel."""
+    run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], name="tiny-d512", D=512), 13)
+
+
+def test_valu_bf16_head_dim_512_paged(orc):
+    """bf16, head_dim 512, single-node trees on a paged cache with ragged prefixes: the
+    vector-ALU kernel, as the serial single-node verifies of the 2K chain run it."""
+    w = _d512("d512t1", T=1, tree="chain", Hq=8, Hkv=1, B=4)
+    run_case(orc, w, 14, prefix_override=[2040, 0, 1001, 17])
