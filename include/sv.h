@@ -79,7 +79,8 @@ typedef enum sv_status {
     SV_ERR_OVERFLOW = -8,   /* a byte size does not fit in 64 bits / an index in 32 bits */
     SV_ERR_WORKSPACE = -9,  /* workspace NULL or smaller than the *_workspace_size result */
     SV_ERR_HIP = -10,       /* the HIP runtime reported an error */
-    SV_ERR_ALIGN = -11      /* a pointer or stride is not 16-byte aligned */
+    SV_ERR_ALIGN = -11,     /* a pointer or stride is not 16-byte aligned */
+    SV_ERR_SCRATCH = -12    /* needs more scratch than the allocation-free entry point holds */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -207,6 +208,29 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
                              int32_t Hkv, int32_t T, int32_t D, float scale, float *out,
                              void *workspace, size_t workspace_bytes, int32_t num_splits,
                              hipStream_t stream);
+
+/*
+ * sv_tree_verify_attention without a workspace argument, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and errors as
+ * sv_tree_verify_attention; its scratch is a 64 MiB array in the library's code object,
+ * one per device, held until the process ends.  The call allocates nothing.
+ *   - A call whose workspace_size would exceed 64 MiB returns SV_ERR_SCRATCH before
+ *     anything is enqueued (the 32K-prefix batch of 16 x 8 kv heads needs ~61 MiB).
+ *   - The first call on a device looks the array up and enqueues a small fill kernel on
+ *     `stream` that clears its arrival counters (the only part that must start at zero;
+ *     every call leaves them zero again).
+ *   - All calls on one device share that device's array, which keeps the last call's
+ *     contents: calls that overlap in time on one device (different streams, or host
+ *     threads, without ordering) race and give unspecified results.
+ * Errors: those of sv_tree_verify_attention except SV_ERR_WORKSPACE; SV_ERR_SCRATCH;
+ * SV_ERR_HIP also when the array's device address cannot be obtained.
+ */
+int sv_tree_verify_attention_noalloc(const void *q, const void *k_tree, const void *v_tree,
+                                     const sv_kv_cache *cache, const int32_t *prefix_len,
+                                     int32_t max_prefix_len, const uint64_t *mask, int32_t B,
+                                     int32_t Hq, int32_t Hkv, int32_t T, int32_t D, float scale,
+                                     float *out, int32_t num_splits, hipStream_t stream);
 
 /* Bytes of workspace sv_accept_longest_path needs (0 when the shape is invalid). */
 size_t sv_accept_longest_path_workspace_size(int32_t B, int32_t T, int64_t V);

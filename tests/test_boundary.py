@@ -66,6 +66,26 @@ def attn(lib, c=None, q=FAKE, B=2, Hq=8, Hkv=2, T=8, D=256, maxp=100, ws=FAKE, w
                                         splits, None)
 
 
+def test_noalloc_attention_validation(lib):
+    """The allocation-free attention entry point shares the workspace entry point's host
+    checks, and refuses a call whose workspace would exceed its 64 MiB scratch, all before
+    touching the device."""
+    def call(c=None, B=2, Hq=8, Hkv=2, T=8, D=256, maxp=100, splits=0, scale=0.0625):
+        c = c or cache()
+        return lib.sv_tree_verify_attention_noalloc(FAKE, FAKE, FAKE, ctypes.byref(c), FAKE,
+                                                    maxp, FAKE, B, Hq, Hkv, T, D, scale, FAKE,
+                                                    splits, None)
+    assert lib.sv_tree_verify_attention_noalloc(FAKE, FAKE, FAKE, None, FAKE, 10, FAKE, 2, 8, 2,
+                                                8, 256, 0.0625, FAKE, 0, None) == -1
+    assert call(Hkv=0) == -4 and call(D=64) == -5 and call(T=65) == -6
+    assert call(maxp=153) == -7 and call(scale=0.0) == -2
+    assert call(B=0) == 0
+    big = cache(max_blocks_per_seq=2600, num_blocks=100000, block_stride=8 * 16 * 256)
+    assert sv.sv_tree_verify_attention_workspace_size(24, 32, 8, 60, 256, 40000, sv.SV_BF16) > (64 << 20)
+    assert call(c=big, B=24, Hq=32, Hkv=8, T=60, maxp=40000) == -12
+    assert "64 MiB" in sv.sv_status_string(-12)
+
+
 def test_attention_validation(lib):
     assert attn(lib, null_cache=True) == -1
     assert attn(lib, Hkv=0) == -4
@@ -106,9 +126,10 @@ def test_attention_workspace_size(lib):
     assert f(16, 32, 8, 60, 64, 32768, sv.SV_BF16) == 0
     assert f(16, 32, 8, 60, 128, 32768, sv.SV_BF16) > 0   # head_dim 128 is supported
     assert f(1, 1, 1, 1, 256, 0, sv.SV_F32) > 0
-    # a full grid of one chunk per sequence still reserves a second chunk, which the
-    # kernel uses when it re-cuts the chunks from the actual prefix lengths
-    assert f(32, 32, 4, 64, 256, 8192, sv.SV_BF16) >= 32 * 4 * 2 * 512 * 256 * 4
+    # a full grid of one chunk per sequence writes its output directly: only the merge's
+    # arrival counters and the header remain; head_dim 512 still stores its partials
+    assert f(32, 32, 4, 64, 256, 8192, sv.SV_BF16) == 256 * 1024 + 256
+    assert f(32, 32, 4, 64, 512, 8192, sv.SV_BF16) >= 32 * 4 * 512 * 512 * 4
 
 
 def test_accept_validation(lib):

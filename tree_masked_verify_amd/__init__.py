@@ -20,9 +20,10 @@ SV_TREE_OK, SV_TREE_BAD_ROOT, SV_TREE_BAD_PARENT = 0, 1, 2
 STATUS = {0: "SV_OK", -1: "SV_ERR_NULL", -2: "SV_ERR_SHAPE", -3: "SV_ERR_DTYPE",
           -4: "SV_ERR_GQA", -5: "SV_ERR_HEAD_DIM", -6: "SV_ERR_TREE_SIZE",
           -7: "SV_ERR_CAPACITY", -8: "SV_ERR_OVERFLOW", -9: "SV_ERR_WORKSPACE",
-          -10: "SV_ERR_HIP", -11: "SV_ERR_ALIGN"}
+          -10: "SV_ERR_HIP", -11: "SV_ERR_ALIGN", -12: "SV_ERR_SCRATCH"}
 ENTRY_POINTS = ("sv_build_tree_mask", "sv_tree_verify_attention_workspace_size",
-                "sv_tree_verify_attention", "sv_accept_longest_path_workspace_size",
+                "sv_tree_verify_attention", "sv_tree_verify_attention_noalloc",
+                "sv_accept_longest_path_workspace_size",
                 "sv_accept_longest_path", "sv_accept_sampled_workspace_size",
                 "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs",
                 "sv_draft_tree_workspace_size", "sv_draft_tree", "sv_kv_append",
@@ -63,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sv_tree_verify_attention.argtypes = [
         vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp, i32, i32, i32, i32, i32,
         ctypes.c_float, vp, vp, sz, i32, vp]
+    lib.sv_tree_verify_attention_noalloc.argtypes = [
+        vp, vp, vp, ctypes.POINTER(sv_kv_cache), vp, i32, vp, i32, i32, i32, i32, i32,
+        ctypes.c_float, vp, i32, vp]
     lib.sv_accept_longest_path_workspace_size.argtypes = [i32, i32, i64]
     lib.sv_accept_longest_path_workspace_size.restype = sz
     lib.sv_accept_longest_path.argtypes = [vp, vp, vp, vp, i32, i32, i64, vp, vp, vp, vp, vp,
@@ -85,7 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  i32, i32, i32, i32, vp]
     lib.sv_status_string.argtypes = [ctypes.c_int]
     lib.sv_status_string.restype = ctypes.c_char_p
-    for f in ("sv_build_tree_mask", "sv_tree_verify_attention", "sv_accept_longest_path",
+    for f in ("sv_build_tree_mask", "sv_tree_verify_attention",
+              "sv_tree_verify_attention_noalloc", "sv_accept_longest_path",
               "sv_accept_sampled", "sv_rope_tree", "sv_topk_logprobs", "sv_draft_tree",
               "sv_kv_append", "sv_kv_compact", "sv_kv_commit"):
         getattr(lib, f).restype = ctypes.c_int
@@ -158,6 +163,19 @@ def sv_tree_verify_attention(q, k_tree, v_tree, cache: sv_kv_cache, prefix_len, 
         _ptr(workspace), workspace.numel() * workspace.element_size() if workspace is not None
         else 0, int(num_splits), _stream(stream))
     _check("sv_tree_verify_attention", rc)
+
+
+def sv_tree_verify_attention_noalloc(q, k_tree, v_tree, cache: sv_kv_cache, prefix_len,
+                                     max_prefix_len, mask, scale, out, num_splits=0,
+                                     stream=None, Hkv=None) -> None:
+    """sv_tree_verify_attention with the library's own per-device scratch (no workspace)."""
+    B, Hq, T, D = q.shape
+    Hkv = k_tree.shape[1] if k_tree is not None else int(Hkv)
+    rc = load_library().sv_tree_verify_attention_noalloc(
+        _ptr(q), _ptr(k_tree), _ptr(v_tree), ctypes.byref(cache), _ptr(prefix_len),
+        int(max_prefix_len), _ptr(mask), B, Hq, Hkv, T, D, float(scale), _ptr(out),
+        int(num_splits), _stream(stream))
+    _check("sv_tree_verify_attention_noalloc", rc)
 
 
 def sv_accept_longest_path_workspace_size(B, T, V) -> int:

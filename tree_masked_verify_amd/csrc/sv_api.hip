@@ -6,6 +6,8 @@
 // rows E1 review gate, E4a and E6).  Sizes are multiplied with overflow checks.
 #include <limits.h>
 
+#include <mutex>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -127,11 +129,109 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     if (!prod_ok({units, S}, &work) || work > INT_MAX) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, D}, &o_elems)) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, 2}, &ml_elems)) return SV_ERR_OVERFLOW;
-    p->ws_o = round256((size_t)o_elems * 4);
-    p->ws_ml = round256((size_t)ml_elems * 4);
+    // one chunk per sequence merged in the kernel: every workgroup writes its output
+    // directly, and no partial results are stored
+    const bool partials = !(p->fused && S == 1);
+    p->ws_o = partials ? round256((size_t)o_elems * 4) : 0;
+    p->ws_ml = partials ? round256((size_t)ml_elems * 4) : 0;
     p->ws_total = kCounterBytes + kHeaderBytes + p->ws_ml + p->ws_o;
     return SV_OK;
 }
+
+namespace {
+
+// Every host-side check of an attention call except the workspace; *nothing when B == 0.
+int check_attention(const void *q, const void *k_tree, const void *v_tree,
+                    const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                    const uint64_t *mask, int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                    int32_t D, float scale, float *out, int32_t num_splits, AttnPlan *plan,
+                    bool *nothing) {
+    if (!cache) return SV_ERR_NULL;
+    if (!(scale > 0.0f) || scale > 3.0e38f) return SV_ERR_SHAPE;  // positive and finite
+    const int dtype = cache->dtype;
+    int rc = make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, plan);
+    if (rc != SV_OK) return rc;
+    *nothing = B == 0;
+    if (B == 0) return SV_OK;
+    // k_tree and v_tree both NULL: the tree rows are read from the cache at P + i
+    if (!q || (!k_tree != !v_tree) || !prefix_len || !mask || !out || !cache->k || !cache->v ||
+        !cache->block_table)
+        return SV_ERR_NULL;
+    rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
+    if (rc != SV_OK) return rc;
+    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+        return SV_ERR_ALIGN;
+    return SV_OK;
+}
+
+// Launches a checked attention call with its workspace laid out as the plan says.
+int launch_attention(const AttnPlan &plan, const void *q, const void *k_tree, const void *v_tree,
+                     const sv_kv_cache *cache, const int32_t *prefix_len, int32_t max_prefix_len,
+                     const uint64_t *mask, int32_t B, int32_t Hq, int32_t Hkv, int32_t T,
+                     int32_t D, float scale, float *out, void *workspace, hipStream_t stream) {
+    AttnArgs a;
+    a.q = q;
+    a.k_tree = k_tree;
+    a.v_tree = v_tree;
+    a.cache = view_of(cache);
+    a.prefix_len = prefix_len;
+    a.max_prefix_len = max_prefix_len;
+    a.mask = mask;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.D = D;
+    a.scale = scale;
+    a.out = out;
+    char *ws = static_cast<char *>(workspace);
+    a.ws_cnt = reinterpret_cast<int32_t *>(ws);
+    a.ws_c = reinterpret_cast<int32_t *>(ws + kCounterBytes);
+    a.ws_ml = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes);
+    a.ws_o = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes + plan.ws_ml);
+    hipError_t e = plan.mfma ? launch_attn_mfma(a, plan, stream)
+                             : launch_attn_valu(a, plan, cache->dtype, stream);
+    if (e != hipSuccess) return SV_ERR_HIP;
+    if (plan.fused) return SV_OK;
+    return hip_status(launch_attn_reduce(a, plan, stream));
+}
+
+// ---- scratch of the allocation-free attention entry point.  One array per device, in
+// the code object, held until the process ends.  In host code `scratch` is a host-side
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to kernels.
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ void zero_words_kernel(uint32_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// The current device's scratch address; the first call on a device looks it up and
+// clears the merge's arrival counters (a fill kernel on `stream`, so it is ordered before
+// the attention kernels the call enqueues next).
+int device_scratch(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return SV_ERR_HIP;
+        hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(ptr), kCounterBytes / 4);
+        if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return SV_OK;
+}
+
+}  // namespace
 
 }  // namespace sv
 
@@ -153,6 +253,9 @@ const char *sv_status_string(int status) {
         case SV_ERR_WORKSPACE: return "workspace missing or too small";
         case SV_ERR_HIP: return "HIP runtime error";
         case SV_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case SV_ERR_SCRATCH:
+            return "the call needs more than the 64 MiB of scratch the allocation-free entry "
+                   "point holds (use sv_tree_verify_attention with a workspace)";
         default: return "unknown status";
     }
 }
@@ -181,49 +284,33 @@ int sv_tree_verify_attention(const void *q, const void *k_tree, const void *v_tr
                              int32_t Hkv, int32_t T, int32_t D, float scale, float *out,
                              void *workspace, size_t workspace_bytes, int32_t num_splits,
                              hipStream_t stream) {
-    if (!cache) return SV_ERR_NULL;
-    if (!(scale > 0.0f) || scale > 3.0e38f) return SV_ERR_SHAPE;  // positive and finite
-    const int dtype = cache->dtype;
     AttnPlan plan;
-    int rc = make_attn_plan(B, Hq, Hkv, T, D, max_prefix_len, dtype, num_splits, &plan);
-    if (rc != SV_OK) return rc;
-    if (B == 0) return SV_OK;
-    // k_tree and v_tree both NULL: the tree rows are read from the cache at P + i
-    if (!q || (!k_tree != !v_tree) || !prefix_len || !mask || !out || !cache->k || !cache->v ||
-        !cache->block_table)
-        return SV_ERR_NULL;
-    rc = check_cache(cache, dtype, (int64_t)max_prefix_len + T, B);
-    if (rc != SV_OK) return rc;
-    if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
-        return SV_ERR_ALIGN;
+    bool nothing = false;
+    int rc = check_attention(q, k_tree, v_tree, cache, prefix_len, max_prefix_len, mask, B, Hq,
+                             Hkv, T, D, scale, out, num_splits, &plan, &nothing);
+    if (rc != SV_OK || nothing) return rc;
     if (!workspace || workspace_bytes < plan.ws_total) return SV_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SV_ERR_ALIGN;
+    return launch_attention(plan, q, k_tree, v_tree, cache, prefix_len, max_prefix_len, mask, B,
+                            Hq, Hkv, T, D, scale, out, workspace, stream);
+}
 
-    AttnArgs a;
-    a.q = q;
-    a.k_tree = k_tree;
-    a.v_tree = v_tree;
-    a.cache = view_of(cache);
-    a.prefix_len = prefix_len;
-    a.max_prefix_len = max_prefix_len;
-    a.mask = mask;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.T = T;
-    a.D = D;
-    a.scale = scale;
-    a.out = out;
-    char *ws = static_cast<char *>(workspace);
-    a.ws_cnt = reinterpret_cast<int32_t *>(ws);
-    a.ws_c = reinterpret_cast<int32_t *>(ws + kCounterBytes);
-    a.ws_ml = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes);
-    a.ws_o = reinterpret_cast<float *>(ws + kCounterBytes + kHeaderBytes + plan.ws_ml);
-    hipError_t e = plan.mfma ? launch_attn_mfma(a, plan, stream)
-                             : launch_attn_valu(a, plan, dtype, stream);
-    if (e != hipSuccess) return SV_ERR_HIP;
-    if (plan.fused) return SV_OK;
-    return hip_status(launch_attn_reduce(a, plan, stream));
+int sv_tree_verify_attention_noalloc(const void *q, const void *k_tree, const void *v_tree,
+                                     const sv_kv_cache *cache, const int32_t *prefix_len,
+                                     int32_t max_prefix_len, const uint64_t *mask, int32_t B,
+                                     int32_t Hq, int32_t Hkv, int32_t T, int32_t D, float scale,
+                                     float *out, int32_t num_splits, hipStream_t stream) {
+    AttnPlan plan;
+    bool nothing = false;
+    int rc = check_attention(q, k_tree, v_tree, cache, prefix_len, max_prefix_len, mask, B, Hq,
+                             Hkv, T, D, scale, out, num_splits, &plan, &nothing);
+    if (rc != SV_OK || nothing) return rc;
+    if (plan.ws_total > kScratchBytes) return SV_ERR_SCRATCH;
+    void *scratch_ptr = nullptr;
+    rc = device_scratch(stream, &scratch_ptr);
+    if (rc != SV_OK) return rc;
+    return launch_attention(plan, q, k_tree, v_tree, cache, prefix_len, max_prefix_len, mask, B,
+                            Hq, Hkv, T, D, scale, out, scratch_ptr, stream);
 }
 
 size_t sv_accept_longest_path_workspace_size(int32_t B, int32_t T, int64_t V) {

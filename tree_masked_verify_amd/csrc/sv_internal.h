@@ -59,6 +59,8 @@ struct AttnPlan {
 constexpr size_t kCounterBytes = 256 * 1024;
 constexpr int64_t kMaxMergeUnits = kCounterBytes / 4;
 constexpr size_t kHeaderBytes = 256;  // the chunk length a balanced call chose
+// Scratch of the allocation-free attention entry point, per device (counters included).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 
 // The most (sequence, chunk) pairs that a balanced call ranks by size.
 constexpr int kBalancedChunks = 128;
