@@ -7,9 +7,11 @@ calls back to back on one stream, inputs resident in HBM.  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--workload long32k] [--splits S]
 
 value = verified tree tokens/s = B*T / seconds per step.  The roofline object covers
-the attention call (its split kernel plus its merge kernel), timed with HIP events on
-the stream it runs on; cpu_baseline times the oracle on one sequence of the same
-workload.
+the attention call, timed with HIP events on the stream it runs on, against the HBM (or
+matrix-core) peak and against a plain device copy timed in the same process;
+cpu_baseline times the oracle on whole sequences of the same workload.  Also reported:
+each stage on its own, per-stage latencies of the three small workloads (and a chain
+verified at once vs node by node), and the batched 8K workload's attention call.
 """
 from __future__ import annotations
 
@@ -189,13 +191,194 @@ def power_probe(st, seconds):
             "gfx_clock_mhz_median": statistics.median(ck) if ck else None}
 
 
+def settle_clock(st, ms):
+    """Whole steps, back to back, until `ms` milliseconds have passed.  From idle the
+    board's graphics clock first runs high and then throttles to the 1400 W power limit
+    over the first ~10-30 ms of load (a call then takes up to 40% longer than settled);
+    the warmup and timed steps that follow run at the settled clock a serving loop runs
+    at."""
+    import torch
+    if ms <= 0:
+        return 0
+    t0, n = time.perf_counter(), 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            st.run()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
+def copy_bandwidth(dev, mib=2048, reps=10):
+    """Achievable HBM bandwidth in this process: a plain device-to-device copy of `mib`
+    MiB (torch copy_, HIP events on its stream), read + write bytes over the median
+    duration."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    return round(2 * n / (sorted(ts)[reps // 2] * 1e-3) / 1e9, 1)
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def small_config_latency(dev, seed, reps=21):
+    """Per-stage device latency (us) of the three small workloads.  Cold: median of reps
+    with a 512 MiB write before each, so that every rep starts with nothing of its inputs
+    in the 256 MB MALL (nor their pages in the address-translation caches).  Warm: the
+    mean of reps back to back, queued behind a spin kernel so that host launch gaps do
+    not count.  At the 2K chain also one 8-node chain verify against 8 single-node
+    verifies with a commit after each (the chain's nodes verified one by one)."""
+    import torch
+    from tree_masked_verify_amd import workloads as wl
+    from tree_masked_verify_amd.step import VerifyStep
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def warm(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(reps * 60_000)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1000.0 / reps, 2)
+
+    def timed(fn):
+        ts = []
+        for r in range(reps):
+            flush.fill_(r & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1000.0)
+        return round(_median(ts), 2)
+
+    out = {}
+    for name in ("tiny", "parity512", "chain2k"):
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w, seed=seed, device=dev)
+        st = VerifyStep.from_inputs(inp)
+        for _ in range(3):
+            st.run()
+        torch.cuda.synchronize()
+        calls = (("mask", st.build_mask), ("attention", st.attention), ("accept", st.accept),
+                 ("commit", st.commit), ("step", st.run))
+        res = {stage: timed(fn) for stage, fn in calls}
+        res["warm"] = {stage: warm(fn) for stage, fn in calls}
+        res["tree_tokens_per_s"] = round(w.B * w.T / (res["step"] * 1e-6), 1)
+        res["tree_tokens_per_s_warm"] = round(w.B * w.T / (res["warm"]["step"] * 1e-6), 1)
+        out[name] = res
+        if name == "chain2k":
+            # the same chain node by node: tree = 1 verify + commit, prefix advanced each time
+            kp, vp = inp.k_pool.clone(), inp.v_pool.clone()
+            P0 = inp.prefix_len.clone()
+            prefix = inp.prefix_len.clone()
+            one = []
+            for i in range(w.T):
+                sl = lambda t: t[:, :, i:i + 1].contiguous()
+                one.append(VerifyStep(sl(inp.q), sl(inp.k_tree), sl(inp.v_tree), kp, vp,
+                                      inp.block_table, prefix, int(inp.max_prefix_len) + i,
+                                      torch.full((1, 1), -1, dtype=torch.int32, device=dev),
+                                      inp.logits[:, i:i + 1].contiguous(),
+                                      inp.draft[:, i:i + 1].contiguous(), inp.scale,
+                                      new_prefix_len=prefix))
+
+            def serial():
+                for o in one:
+                    o.run()
+            def serial_from_start():
+                prefix.copy_(P0)
+                serial()
+            serial_from_start()
+            ts = []
+            for r in range(reps):
+                prefix.copy_(P0)
+                flush.fill_(r & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                serial()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1000.0)
+            res["serial_single_node_steps_us"] = round(_median(ts), 2)
+            res["serial_over_chain"] = round(res["serial_single_node_steps_us"] / res["step"], 2)
+            res["warm"]["serial_single_node_steps"] = warm(serial_from_start)
+            res["warm"]["serial_over_chain"] = round(
+                res["warm"]["serial_single_node_steps"] / res["warm"]["step"], 2)
+    del flush
+    return out
+
+
+def secondary_workload(name, dev, seed, steps=30, warmup=10):
+    """The attention call and whole step of another workload, timed like the main one
+    (HIP events on the stream; clock settled first)."""
+    import torch
+    from tree_masked_verify_amd import workloads as wl
+    from tree_masked_verify_amd.step import VerifyStep
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, seed=seed, device=dev)
+    st = VerifyStep.from_inputs(inp)
+    stream = torch.cuda.current_stream()
+    settle_clock(st, 100)
+    for _ in range(warmup):
+        st.run()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    e[0].record(stream)
+    for k in range(steps):
+        st.build_mask()
+        ea[k][0].record(stream)
+        st.attention()
+        ea[k][1].record(stream)
+        st.accept()
+        st.commit()
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = e[0].elapsed_time(e[1]) / steps
+    us_attn = sum(a.elapsed_time(b) for a, b in ea) / steps * 1000.0
+    nbytes, flops = attention_traffic(inp, st.depth)
+    return {"workload": name, "ms_per_step": round(ms_step, 4),
+            "verified_tree_tokens_per_s": round(w.B * w.T / (ms_step * 1e-3), 1),
+            "attention_us_per_launch": round(us_attn, 2),
+            "attention_bytes_per_launch": nbytes, "attention_flops_per_launch": flops,
+            "attention_hbm_gbs": round(nbytes / us_attn / 1e3, 1),
+            "attention_mfma_tflops": round(flops / us_attn / 1e6, 1),
+            "attention_mfma_frac": round(flops / us_attn / 1e6 / BF16_PEAK_TFLOPS, 4),
+            "attention_traffic": counter_traffic(name)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the clock takes ~30 steps (~35 ms) to settle at the board's power limit; the first
-    # steps after idle run ~5% slower
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="whole steps back to back for this long before the warmup, so that "
+                         "the board's clock has settled at its power limit (0: none)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the same-run copy bandwidth, the small workloads' latencies "
+                         "and the batched 8K workload")
     ap.add_argument("--workload", default="long32k")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
@@ -241,7 +424,8 @@ def main():
         log(f"[bench] power probe, {args.power} s of attention calls")
         print(json.dumps({"workload": w.name, **power_probe(st, args.power)}), flush=True)
         return
-    log(f"[bench] warmup {args.warmup}")
+    settled = settle_clock(st, args.settle_ms)
+    log(f"[bench] settled the clock with {settled} steps; warmup {args.warmup}")
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
@@ -324,8 +508,10 @@ def main():
     # the bound is the side the call's arithmetic intensity puts it on: matrix cores when
     # its flops per algorithmic byte exceed the ratio of the two peaks (2500e12 / 8000e9)
     mfma_bound = flops_attn / bytes_attn > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    fused = w.dtype == "bf16" and w.D in (128, 256) and (w.Hq // w.Hkv) * w.T >= 16
     roofline = {"bound": "mfma" if mfma_bound else "hbm",
-                "kernel": "tree-verify attention (split + merge kernels)",
+                "kernel": (f"attn_w4_kernel<{w.D}> (one launch; chunks merged in the kernel)"
+                           if fused else "attention split kernel + merge kernel"),
                 "achieved": round(tflops, 1) if mfma_bound else round(gbs, 1),
                 "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
                 "unit": "TFLOP/s" if mfma_bound else "GB/s",
@@ -369,6 +555,17 @@ def main():
         "rope_gbs": round(2 * w.B * (w.Hq + w.Hkv) * w.T * w.D * (2 if w.dtype == "bf16" else 4)
                           / (stages["rope"] * 1e-6) / 1e9, 1),
     }
+    result["settle_ms"] = args.settle_ms
+    if not args.no_extras:
+        log("[bench] copy bandwidth")
+        cbw = copy_bandwidth(dev)
+        roofline["copy_gbs"] = cbw
+        roofline["frac_of_copy"] = round(gbs / cbw, 4)
+        log("[bench] small workloads")
+        result["small_configs_latency_us"] = small_config_latency(dev, args.seed)
+        if w.name != "batched8k":
+            log("[bench] batched8k")
+            result["batched8k"] = secondary_workload("batched8k", dev, args.seed)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(inp)

@@ -200,20 +200,25 @@ def test_head_dim_512_chunk_beyond_staged_table(orc):
     run_case(orc, w, 32, num_splits=1)
 
 
-# ----------------------------------------------------------------- vector-ALU instantiations
-def test_valu_bf16_head_dim_128_single_node(orc):
-    """bf16, head_dim 128, 8 query rows per kv head (< 16): the vector-ALU kernel."""
+# ----------------------------------------------------------------- few query rows, fp32
+def test_bf16_head_dim_128_single_node(orc):
+    """bf16, head_dim 128, 8 query rows per kv head (fewer than one 16-row block): the
+    matrix-core kernel with its row block padded."""
     run_case(orc, wl.scaled(wl.WORKLOADS["parity512"], name="t1-d128", D=128, T=1,
                             tree="chain", prefix=(333, 333), capacity=352), 12)
 
 
 def test_valu_f32_head_dim_512(orc):
     """fp32 at head_dim 512 (the tiny workload's tree): the vector-ALU kernel."""
+    run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], name="tiny-d512-paged", D=512, B=3, Hq=4,
+                            Hkv=2, block_size=16, shuffled=True, prefix=(0, 700)), 15,
+             prefix_override=[0, 333, 700])
     run_case(orc, wl.scaled(wl.WORKLOADS["tiny"], name="tiny-d512", D=512), 13)
 
 
-def test_valu_bf16_head_dim_512_paged(orc):
-    """bf16, head_dim 512, single-node trees on a paged cache with ragged prefixes: the
-    vector-ALU kernel, as the serial single-node verifies of the 2K chain run it."""
+def test_bf16_head_dim_512_single_node_paged(orc):
+    """bf16, head_dim 512, single-node trees on a paged cache with ragged prefixes (the
+    shape of the 2K chain's serial single-node verifies): the head_dim-512 matrix-core
+    kernel with its row block padded."""
     w = _d512("d512t1", T=1, tree="chain", Hq=8, Hkv=1, B=4)
     run_case(orc, w, 14, prefix_override=[2040, 0, 1001, 17])

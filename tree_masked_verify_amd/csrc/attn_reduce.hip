@@ -45,20 +45,37 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
 
     const int64_t base0 = ((int64_t)b * Hkv + kvh) * S * (int64_t)R + r;
     float M = kNegInfR;
+#pragma unroll 8
     for (int s = 0; s < nv; ++s) M = fmaxf(M, ws_ml[(base0 + (int64_t)s * R) * 2]);
 
+    // chunks in groups of four whose loads are all issued before any is used, so that
+    // the merge waits for one memory round trip per group, not per chunk; the sums
+    // still run over the chunks in order
+    constexpr int GRP = 4;
     f32x4 acc[VPL];
     for (int v = 0; v < VPL; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     float L = 0.0f;
-    for (int s = 0; s < nv; ++s) {
-        const int64_t base = base0 + (int64_t)s * R;
-        const float m = ws_ml[base * 2];
-        const float l = ws_ml[base * 2 + 1];
-        const float wgt = m == kNegInfR ? 0.0f : exp2f(m - M);
-        L += wgt * l;
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(ws_o + base * D);
-        for (int v = 0; v < VPL; ++v)
-            if (lane + 64 * v < NV4) acc[v] += wgt * src[lane + 64 * v];
+    for (int s0 = 0; s0 < nv; s0 += GRP) {
+        float m[GRP], l[GRP];
+        f32x4 src[GRP][VPL];
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const int s = s0 + k < nv ? s0 + k : nv - 1;
+            const int64_t base = base0 + (int64_t)s * R;
+            m[k] = s0 + k < nv ? ws_ml[base * 2] : kNegInfR;
+            l[k] = ws_ml[base * 2 + 1];
+            const f32x4 *o = reinterpret_cast<const f32x4 *>(ws_o + base * D);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v)
+                src[k][v] = lane + 64 * v < NV4 ? o[lane + 64 * v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const float wgt = m[k] == kNegInfR ? 0.0f : exp2f(m[k] - M);
+            L += wgt * l[k];
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) acc[v] += wgt * src[k][v];
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     f32x4 *dst = reinterpret_cast<f32x4 *>(out + (((int64_t)b * T + i) * Hq + h) * D);

@@ -1,12 +1,18 @@
-// attn_valu.hip -- tree-masked split-KV attention on the vector ALUs, for fp32 inputs
-// and for kv heads with fewer than 16 query rows (single-node trees, small groups).
+// attn_valu.hip -- tree-masked split-KV attention on the vector ALUs, for fp32 inputs.
 // Same partial-result format as attn_mfma.hip, so the same merge finishes it.
 //
-// Workgroup: 256 threads own 16 query rows of one (sequence, kv head, chunk); keys
-// stream through LDS 16 at a time as fp32.  Thread (row = t / 16, sub = t % 16)
-// scores key `sub` against its row, the 16 threads of a row reduce the max and sum
-// by shuffles, and the same thread then accumulates head_dim entries sub, sub + 16,
-// ... of the row's output.
+// What is computed (ADR-037 Phase status rows E1.1-E1.5, section 4 Phase E1): every
+// query row (q head g of kv head kvh, tree node i) attends to the cached prefix of its
+// sequence and to the tree rows its ancestor mask selects.
+//
+// Workgroup: 256 threads own 16 query rows of one (sequence, kv head, chunk); keys stream
+// through LDS 16 at a time.  A tile is staged with 16-byte loads, one address computed
+// per key, and the next tile's loads are issued into registers before the current tile
+// is computed, so a tile costs one memory round trip that overlaps the arithmetic.
+// Thread (row = t / 16, sub = t % 16) scores key `sub` against its row (Q row broadcast
+// from LDS, the key row read as 16-byte vectors from a padded LDS row), the 16 threads
+// of a row reduce the max and sum by shuffles, and the same thread then accumulates
+// head_dim entries sub, sub + 16, ... of the row's output.
 #include "sv_internal.h"
 
 namespace sv {
@@ -17,11 +23,11 @@ constexpr int kKeysV = 16;
 constexpr float kNegInfV = -__builtin_huge_valf();
 
 struct ValuParams {
-    const void *q;
-    const void *kt;
-    const void *vt;
-    const void *kc;
-    const void *vc;
+    const float *q;
+    const float *kt;
+    const float *vt;
+    const float *kc;
+    const float *vc;
     const int32_t *table;
     int32_t bs, max_blocks;
     int64_t num_blocks, bstride, hstride, rstride;
@@ -35,22 +41,30 @@ struct ValuParams {
     float *ws_ml;
 };
 
-template <bool kBF16>
-__device__ __forceinline__ float ld(const void *base, int64_t idx) {
-    if (kBF16) {
-        const uint16_t hbits = static_cast<const uint16_t *>(base)[idx];
-        return __uint_as_float((uint32_t)hbits << 16);
-    }
-    return static_cast<const float *>(base)[idx];
-}
+template <int D>
+struct VCfg {
+    static constexpr int KROW = D + 4;                // padded K row (floats): 16-byte
+                                                      // reads of 16 rows hit 64 banks
+    static constexpr int PIECES = kKeysV * D / 4;     // 16-byte pieces per tile and tensor
+    static constexpr int PER = PIECES / 256;          // per thread
+    static constexpr int QS = 0;                      // [16][D]
+    static constexpr int KS = QS + kRowsV * D;        // [16][KROW]
+    static constexpr int VS = KS + kKeysV * KROW;     // [16][D]
+    static constexpr int PS = VS + kKeysV * D;        // [16][16] probabilities
+    static constexpr int OK = PS + kRowsV * kKeysV;   // [16] key exists
+    static constexpr int FLOATS = OK + kKeysV;
+    static_assert(PIECES % 256 == 0, "tile pieces");
+};
 
-template <int D, bool kBF16>
+template <int D>
 __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
+    using Cf = VCfg<D>;
     extern __shared__ __attribute__((aligned(16))) float fsm[];
-    float *qs = fsm;                           // [16][D]
-    float *ks = qs + kRowsV * D;               // [16][D + 1]
-    float *vs = ks + kKeysV * (D + 1);         // [16][D]
-    float *ps = vs + kKeysV * D;               // [16][16]
+    float *qs = fsm + Cf::QS;
+    float *ks = fsm + Cf::KS;
+    float *vs = fsm + Cf::VS;
+    float *ps = fsm + Cf::PS;
+    int *okk = reinterpret_cast<int *>(fsm + Cf::OK);
 
     const int n = gridDim.x;
     const int logical = (blockIdx.x % kNumXCD) * (n / kNumXCD) + blockIdx.x / kNumXCD;
@@ -68,49 +82,54 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     const int start = s * p.C;
     if (s > 0 && start >= P) return;
     const int end = min(start + p.C, P);
+    const int ntp = end > start ? (end - start + kKeysV - 1) / kKeysV : 0;   // prefix tiles
+    const int ntt = s == 0 ? (p.T + kKeysV - 1) / kKeysV : 0;              // tree tiles
+    const int nt = ntp + ntt;
 
     const int tid = threadIdx.x;
     const int rl = tid / kKeysV;        // local row
     const int sub = tid % kKeysV;
     const int row = rg * kRowsV + rl;
     const bool row_ok = row < p.R;
-    const int g = row_ok ? row / p.T : 0;
-    const int node = row_ok ? row - g * p.T : 0;
+    const int node = row_ok ? row - (row / p.T) * p.T : 0;
 
-    // stage Q rows
-    for (int e = tid; e < kRowsV * D; e += blockDim.x) {
-        const int r = e / D, d = e - (e / D) * D;
+    // stage Q rows (16-byte pieces)
+    for (int e = tid; e < kRowsV * D / 4; e += blockDim.x) {
+        const int r = e / (D / 4), d4 = e - r * (D / 4);
         const int rr = rg * kRowsV + r;
-        float v = 0.0f;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
         if (rr < p.R) {
             const int gg = rr / p.T, ii = rr - (rr / p.T) * p.T;
-            v = ld<kBF16>(p.q, (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gg) * p.T + ii) * D + d);
+            v = *reinterpret_cast<const f32x4 *>(
+                p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gg) * p.T + ii) * D + 4 * d4);
         }
-        qs[e] = v;
+        *reinterpret_cast<f32x4 *>(qs + r * D + 4 * d4) = v;
     }
     const uint64_t mrow = row_ok ? p.mask[(int64_t)b * p.T + node] : 0ull;
 
-    constexpr int DPT = D / kKeysV;  // output entries per thread
-    float o[DPT];
-    for (int j = 0; j < DPT; ++j) o[j] = 0.0f;
-    float m = kNegInfV, l = 0.0f;
-
-    for (int pass = 0; pass < 2; ++pass) {
-        const bool tree = pass == 1;
-        if (tree && s != 0) break;
-        const int lo = tree ? 0 : start;
-        const int hi = tree ? p.T : end;
-        for (int k0 = lo; k0 < hi; k0 += kKeysV) {
-            __syncthreads();  // previous tile fully consumed (and Q staged)
-            for (int e = tid; e < kKeysV * D; e += blockDim.x) {
-                const int kk = e / D, d = e - (e / D) * D;
-                const int pos = k0 + kk;
-                float kv = 0.0f, vv = 0.0f;
-                if (pos < hi) {
-                    int64_t off = -1;
-                    if (tree && p.kt) {
+    // Tile u: prefix keys start + 16u .. (u < ntp), else tree rows 16 (u - ntp) ...  This
+    // thread's pieces j: key kk = (tid + 256 j) / (D / 4), 16-byte piece d4 of that key.
+    // A key that does not exist (past the chunk or the tree, or behind an out-of-range
+    // block entry) is staged as zeros and marked absent.
+    f32x4 kreg[Cf::PER], vreg[Cf::PER];
+    bool kok[Cf::PER];
+    auto fetch = [&](int u) {
+        const bool tree = u >= ntp;
+        const int k0 = tree ? (u - ntp) * kKeysV : start + u * kKeysV;
+#pragma unroll
+        for (int j = 0; j < Cf::PER; ++j) {
+            const int f = tid + 256 * j;
+            const int kk = f / (D / 4), d4 = f - kk * (D / 4);
+            const int pos = k0 + kk;
+            int64_t off = -1;
+            const float *kb = p.kc, *vb = p.vc;
+            if (tree) {
+                if (pos < p.T) {
+                    if (p.kt) {
                         off = (((int64_t)b * p.Hkv + kvh) * p.T + pos) * D;
-                    } else if (tree) {
+                        kb = p.kt;
+                        vb = p.vt;
+                    } else {
                         // tree rows kept in the cache at P + pos (an out-of-range block
                         // entry reads block 0: such rows were never appended)
                         const int cpos = P + pos;
@@ -118,57 +137,93 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
                         blk = (blk >= 0 && blk < p.num_blocks) ? blk : 0;
                         off = (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
                               (int64_t)(cpos % p.bs) * p.rstride;
-                    } else {
-                        const int32_t blk = p.table[(int64_t)b * p.max_blocks + pos / p.bs];
-                        if (blk >= 0 && blk < p.num_blocks)
-                            off = (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
-                                  (int64_t)(pos % p.bs) * p.rstride;
-                    }
-                    if (off >= 0) {
-                        kv = ld<kBF16>(tree && p.kt ? p.kt : p.kc, off + d);
-                        vv = ld<kBF16>(tree && p.kt ? p.vt : p.vc, off + d);
                     }
                 }
-                ks[kk * (D + 1) + d] = kv;
-                vs[kk * D + d] = vv;
-            }
-            __syncthreads();
-
-            // score of key `sub` for row `rl`
-            const int pos = k0 + sub;
-            bool ok = pos < hi;
-            if (ok && !tree) {
+            } else if (pos < end) {
                 const int32_t blk = p.table[(int64_t)b * p.max_blocks + pos / p.bs];
-                ok = blk >= 0 && blk < p.num_blocks;
+                if (blk >= 0 && blk < p.num_blocks)
+                    off = (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
+                          (int64_t)(pos % p.bs) * p.rstride;
             }
-            if (tree) ok = ok && ((mrow >> pos) & 1ull);
-            float dot = 0.0f;
-            const float *qr = qs + rl * D;
-            const float *kr = ks + sub * (D + 1);
-            for (int d = 0; d < D; ++d) dot = fmaf(qr[d], kr[d], dot);
-            const float x = ok ? dot * p.scale_log2 : kNegInfV;
-            float mt = x;
-            for (int off = 1; off < kKeysV; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
-            const float mnew = fmaxf(m, mt);
-            const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m - mnew);
-            const float pr = x == kNegInfV ? 0.0f : exp2f(x - mnew);
-            float lt = pr;
-            for (int off = 1; off < kKeysV; off <<= 1) lt += __shfl_xor(lt, off, 64);
-            l = l * alpha + lt;
-            m = mnew;
-            ps[rl * kKeysV + sub] = pr;
-            __syncthreads();
-            for (int j = 0; j < DPT; ++j) {
-                const int d = sub + kKeysV * j;
-                float acc = o[j] * alpha;
-                for (int k = 0; k < kKeysV; ++k) acc = fmaf(ps[rl * kKeysV + k], vs[k * D + d], acc);
-                o[j] = acc;
-            }
+            kok[j] = off >= 0;
+            kreg[j] = off >= 0 ? *reinterpret_cast<const f32x4 *>(kb + off + 4 * d4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+            vreg[j] = off >= 0 ? *reinterpret_cast<const f32x4 *>(vb + off + 4 * d4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int j = 0; j < Cf::PER; ++j) {
+            const int f = tid + 256 * j;
+            const int kk = f / (D / 4), d4 = f - kk * (D / 4);
+            *reinterpret_cast<f32x4 *>(ks + kk * Cf::KROW + 4 * d4) = kreg[j];
+            *reinterpret_cast<f32x4 *>(vs + kk * D + 4 * d4) = vreg[j];
+            if (d4 == 0) okk[kk] = kok[j];
+        }
+    };
+
+    constexpr int DPT = D / kKeysV;  // output entries per thread
+    float o[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) o[j] = 0.0f;
+    float m = kNegInfV, l = 0.0f;
+
+    if (nt > 0) fetch(0);
+    for (int u = 0; u < nt; ++u) {
+        const bool tree = u >= ntp;
+        const int k0 = tree ? (u - ntp) * kKeysV : start + u * kKeysV;
+        __syncthreads();  // previous tile fully consumed (and Q staged)
+        stash();
+        __syncthreads();
+        if (u + 1 < nt) fetch(u + 1);  // in flight while this tile is computed
+
+        // score of key `sub` for row `rl`: four independent partial sums over head_dim
+        const int pos = k0 + sub;
+        bool ok = okk[sub] != 0;
+        if (tree) ok = ok && ((mrow >> pos) & 1ull);
+        const f32x4 *qr = reinterpret_cast<const f32x4 *>(qs + rl * D);
+        const f32x4 *kr = reinterpret_cast<const f32x4 *>(ks + sub * Cf::KROW);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int d4 = 0; d4 < D / 4; ++d4) {
+            const f32x4 a = qr[d4], c = kr[d4];
+            acc[0] = fmaf(a[0], c[0], acc[0]);
+            acc[1] = fmaf(a[1], c[1], acc[1]);
+            acc[2] = fmaf(a[2], c[2], acc[2]);
+            acc[3] = fmaf(a[3], c[3], acc[3]);
+        }
+        const float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        const float x = ok ? dot * p.scale_log2 : kNegInfV;
+        float mt = x;
+#pragma unroll
+        for (int off = 1; off < kKeysV; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+        const float mnew = fmaxf(m, mt);
+        const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m - mnew);
+        const float pr = x == kNegInfV ? 0.0f : exp2f(x - mnew);
+        float lt = pr;
+#pragma unroll
+        for (int off = 1; off < kKeysV; off <<= 1) lt += __shfl_xor(lt, off, 64);
+        l = l * alpha + lt;
+        m = mnew;
+        ps[rl * kKeysV + sub] = pr;
+        __syncthreads();
+        float pk[kKeysV];
+#pragma unroll
+        for (int k = 0; k < kKeysV; ++k) pk[k] = ps[rl * kKeysV + k];
+#pragma unroll
+        for (int j = 0; j < DPT; ++j) {
+            const int d = sub + kKeysV * j;
+            float a2 = o[j] * alpha;
+#pragma unroll
+            for (int k = 0; k < kKeysV; ++k) a2 = fmaf(pk[k], vs[k * D + d], a2);
+            o[j] = a2;
         }
     }
 
     if (row_ok) {
         const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
+#pragma unroll
         for (int j = 0; j < DPT; ++j) p.ws_o[base * D + sub + kKeysV * j] = o[j];
         if (sub == 0) {
             p.ws_ml[base * 2 + 0] = m;
@@ -177,19 +232,18 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     }
 }
 
-template <int D, bool kBF16>
+template <int D>
 hipError_t launch_v(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
-    const size_t smem = sizeof(float) * ((size_t)kRowsV * D + (size_t)kKeysV * (D + 1) +
-                                         (size_t)kKeysV * D + kRowsV * kKeysV);
-    hipError_t e = hipFuncSetAttribute((const void *)attn_valu_kernel<D, kBF16>,
+    const size_t smem = sizeof(float) * VCfg<D>::FLOATS;
+    hipError_t e = hipFuncSetAttribute((const void *)attn_valu_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     ValuParams p;
-    p.q = a.q;
-    p.kt = a.k_tree;
-    p.vt = a.v_tree;
-    p.kc = a.cache.k;
-    p.vc = a.cache.v;
+    p.q = static_cast<const float *>(a.q);
+    p.kt = static_cast<const float *>(a.k_tree);
+    p.vt = static_cast<const float *>(a.v_tree);
+    p.kc = static_cast<const float *>(a.cache.k);
+    p.vc = static_cast<const float *>(a.cache.v);
     p.table = a.cache.table;
     p.bs = a.cache.bs;
     p.max_blocks = a.cache.max_blocks;
@@ -214,7 +268,7 @@ hipError_t launch_v(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
     const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
-    hipLaunchKernelGGL((attn_valu_kernel<D, kBF16>), dim3(grid), dim3(256), smem, stream, p);
+    hipLaunchKernelGGL(attn_valu_kernel<D>, dim3(grid), dim3(256), smem, stream, p);
     return hipGetLastError();
 }
 
@@ -223,10 +277,10 @@ hipError_t launch_v(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
 hipError_t launch_attn_valu(const AttnArgs &a, const AttnPlan &pl, int dtype,
                             hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
-    const bool bf = dtype == SV_BF16;
-    if (a.D == 128) return bf ? launch_v<128, true>(a, pl, stream) : launch_v<128, false>(a, pl, stream);
-    if (a.D == 256) return bf ? launch_v<256, true>(a, pl, stream) : launch_v<256, false>(a, pl, stream);
-    return bf ? launch_v<512, true>(a, pl, stream) : launch_v<512, false>(a, pl, stream);
+    if (dtype != SV_F32) return hipErrorInvalidValue;  // bf16 runs on the matrix cores
+    if (a.D == 128) return launch_v<128>(a, pl, stream);
+    if (a.D == 256) return launch_v<256>(a, pl, stream);
+    return launch_v<512>(a, pl, stream);
 }
 
 }  // namespace sv

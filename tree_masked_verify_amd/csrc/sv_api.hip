@@ -86,7 +86,10 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     if (rc != SV_OK) return rc;
     const int R = (Hq / Hkv) * T;
     p->R = R;
-    p->mfma = dtype == SV_BF16 && R >= 16;
+    // bf16 always runs on the matrix cores; a kv head with fewer than 16 query rows
+    // (single-node trees, small groups) pads its row block, which costs matrix-core time
+    // but not latency.  fp32 runs on the vector ALUs.
+    p->mfma = dtype == SV_BF16;
     if (p->mfma) {
         // 32-row blocks, each shared by D/256 wavefronts (one below 256); at most 8
         // wavefronts
@@ -103,8 +106,11 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     p->n_rg = (R + p->rows_per_wg - 1) / p->rows_per_wg;
     int64_t units = (int64_t)(B > 0 ? B : 1) * Hkv * p->n_rg;
     int64_t want = num_splits > 0 ? num_splits : (kNumCU + units - 1) / units;
-    if (want < 1) want = 1;
     const int64_t P = max_prefix_len > 0 ? max_prefix_len : 1;
+    // automatic splitting keeps chunks of at least kMinChunk keys: shorter ones cost more
+    // in per-workgroup set-up and in merging partial results than they save
+    if (num_splits == 0 && want > (P + kMinChunk - 1) / kMinChunk) want = (P + kMinChunk - 1) / kMinChunk;
+    if (want < 1) want = 1;
     int64_t C = (P + want - 1) / want;
     C = (C + kKeyTile - 1) / kKeyTile * kKeyTile;
     if (C < kKeyTile) C = kKeyTile;

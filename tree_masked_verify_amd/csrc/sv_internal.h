@@ -17,6 +17,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNumCU = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCD = 8;
 constexpr int kKeyTile = 32;    // keys per attention tile; split sizes are multiples of it
+constexpr int kMinChunk = 256;  // fewest prefix keys per chunk under automatic splitting
 constexpr int kAttnMaxWaves = 8;  // wavefronts per attention workgroup
 
 // Paged cache as seen by a kernel (element strides).
@@ -34,7 +35,7 @@ struct CacheView {
 
 // How one attention call is cut into workgroups.
 struct AttnPlan {
-    int mfma;          // 1: MFMA kernel (bf16, >= 16 rows per kv head); 0: VALU kernel
+    int mfma;          // 1: matrix-core kernel (bf16); 0: vector-ALU kernel (fp32)
     int R;             // query rows per kv head = (Hq / Hkv) * T, row r = g * T + i
     int rows_per_wg;   // rows one workgroup owns
     int n_rg;          // row groups per kv head
