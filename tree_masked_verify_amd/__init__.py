@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsv.so")
+# SV_LIBRARY_PATH names another build of the library (the sanitizer tests load one)
+LIB_PATH = os.environ.get("SV_LIBRARY_PATH", os.path.join(_HERE, "libsv.so"))
 
 SV_F32, SV_BF16 = 0, 1
 SV_TREE_OK, SV_TREE_BAD_ROOT, SV_TREE_BAD_PARENT = 0, 1, 2
