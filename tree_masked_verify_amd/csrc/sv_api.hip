@@ -107,9 +107,12 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     int64_t units = (int64_t)(B > 0 ? B : 1) * Hkv * p->n_rg;
     int64_t want = num_splits > 0 ? num_splits : (kNumCU + units - 1) / units;
     const int64_t P = max_prefix_len > 0 ? max_prefix_len : 1;
-    // automatic splitting keeps chunks of at least kMinChunk keys: shorter ones cost more
-    // in per-workgroup set-up and in merging partial results than they save
-    if (num_splits == 0 && want > (P + kMinChunk - 1) / kMinChunk) want = (P + kMinChunk - 1) / kMinChunk;
+    // automatic splitting keeps chunks of at least min_chunk keys: shorter ones cost more
+    // in per-workgroup set-up and in merging partial results than they save (measured on
+    // small calls: 64 keys on the matrix-core kernels, one 32-key chunk per workgroup on
+    // the vector-ALU kernel)
+    const int64_t min_chunk = p->mfma ? kMinChunk : kKeyTile;
+    if (num_splits == 0 && want > (P + min_chunk - 1) / min_chunk) want = (P + min_chunk - 1) / min_chunk;
     if (want < 1) want = 1;
     int64_t C = (P + want - 1) / want;
     C = (C + kKeyTile - 1) / kKeyTile * kKeyTile;
@@ -127,10 +130,14 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
         p->balanced = 1;
     p->C = (int)C;
     p->S = (int)S;
-    // in-kernel merge: the arrival counters must fit their region, and one unit's
-    // partials must stay within a 31-bit byte offset (the merge addresses them so)
+    // In-kernel merge (head_dim 128/256): when each sequence is one chunk (no merge at
+    // all, every workgroup writes its output), or when the grid fills the chip, so that
+    // the merges of the many units run side by side.  A small call split into many chunks
+    // merges faster in the separate kernel, which spreads the merge over many workgroups
+    // instead of leaving each unit's to one.  The arrival counters must fit their region,
+    // and one unit's partials must stay within a 31-bit byte offset.
     p->fused = p->mfma && attn_w4_handles(D) && units <= kMaxMergeUnits &&
-               S * (int64_t)R * D * 4 < ((int64_t)1 << 31);
+               (S == 1 || units * S >= kNumCU) && S * (int64_t)R * D * 4 < ((int64_t)1 << 31);
     int64_t work, o_elems, ml_elems;
     if (!prod_ok({units, S}, &work) || work > INT_MAX) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, D}, &o_elems)) return SV_ERR_OVERFLOW;

@@ -17,7 +17,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNumCU = 256;     // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCD = 8;
 constexpr int kKeyTile = 32;    // keys per attention tile; split sizes are multiples of it
-constexpr int kMinChunk = 256;  // fewest prefix keys per chunk under automatic splitting
+constexpr int kMinChunk = 64;   // fewest prefix keys per chunk under automatic splitting
 constexpr int kAttnMaxWaves = 8;  // wavefronts per attention workgroup
 
 // Paged cache as seen by a kernel (element strides).
