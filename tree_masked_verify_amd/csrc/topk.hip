@@ -15,7 +15,7 @@
 //
 // topk_rows_kernel: one workgroup of four wavefronts per row.  Every lane streams its
 // 16-byte pieces once and keeps an online max and an fp64 sum of exponentials
-// (exp_small / exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's
+// (sum_small4 / exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's
 // element enters it when it beats the wavefront's K-th best so far (while fewer than K
 // entries exist, every element enters) and is not below the K-th best another wavefront
 // has published.  When the buffer grows, the wavefront keeps its K best (K rounds of a
@@ -36,6 +36,8 @@ constexpr int kTkThreads = 64 * kTkWaves;
 constexpr int kCap = 512;                   // candidate entries per wavefront
 constexpr int kPiece = 256;                 // the most one piece (one 16-byte load per lane) adds
 constexpr float kFltMax = 3.40282347e38f;
+constexpr int kNonTemporal = 2;             // cache policy bits of a buffer load: nt
+constexpr int kRsrcWord3 = 0x00020000;      // raw 32-bit buffer resource, gfx9 family
 
 // exp(d) for d in [-700, 0] in fp64, callers clamp d into that range first.  Table-driven
 // method (P. T. P. Tang, "Table-driven implementation of the exponential function in IEEE
@@ -68,31 +70,50 @@ __device__ __forceinline__ double exp_term(float x, double md, const double *tab
     return x > -__builtin_huge_valf() ? exp_core(d, tab) : 0.0;
 }
 
-// e^x in fp64 for a logit with |x| < 64, from its fp32 value: n = round(512 x) by the
-// rounding trick in fp32 (adding 1.5 * 2^23 + 2^15 leaves 0x4B408000 + n in the bits), after
-// which r = x - n/512 is exact in fp32 with |r| <= 2^-10; with n = 128 k + j, e^x =
-// e^(k/4) * e^(j/512) * e^r, the first two factors from tables (t1[k + 256], k in
-// [-256, 256], which is bits 7..16 of t; t2[j], j < 128, its low 7 bits) and e^r - 1 its
-// Taylor polynomial of degree 4 (remainder below 2^-56 relative).  Same table-driven method
-// as exp_core, with no reduction step and no reference maximum.
-__device__ __forceinline__ double exp_small(float x, const double *t1, const double *t2) {
+// Adds e^x for four logits, each with |x| < 31.5, in fp64 from their fp32 values, to two
+// running sums (logits 0 and 1 to s0, 2 and 3 to s1): n = round(1024 x) by the rounding
+// trick in fp32 (adding 1.5 * 2^23 + 2^15 leaves 0x4B408000 + n in the bits), after which
+// r = x - n/1024 is exact in fp32 with |r| <= 2^-11; with n = 256 k + j,
+// e^x = e^(k/4) * (e^(j/1024) * e^r), the first two factors from tables indexed by bytes
+// of those bits (t1[k + 128] by byte 1, t2[j] by byte 0) and e^r - 1 its Taylor polynomial
+// of degree 4 (remainder below 2^-61 relative).  Same table-driven method as exp_core, with
+// no reduction step and no reference maximum.  The eight table reads are issued before the
+// polynomials, which hide their latency.
+__device__ __forceinline__ void sum_small4(const f32x4 &x, const double *t1, const double *t2,
+                                           double &s0, double &s1) {
     constexpr float kMagic = 12615680.0f;              // 1.5 * 2^23 + 2^15
-    const float t = fmaf(x, 512.0f, kMagic);
-    const float rf = fmaf(t - kMagic, -1.0f / 512.0f, x);
-    const uint32_t b = __float_as_uint(t);
-    const double T = t1[(b >> 7) & 1023u] * t2[b & 127u];
-    const double r = (double)rf;
-    double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-    q = fma(q, r, 0.5);
-    return fma(T, fma(r * r, q, r), T);
+    double A[4], Bt[4], p[4];
+    float rf[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float t = fmaf(x[e], 1024.0f, kMagic);
+        rf[e] = fmaf(t - kMagic, -1.0f / 1024.0f, x[e]);
+        const uint32_t b = __float_as_uint(t);
+        A[e] = t1[(b >> 8) & 255u];
+        Bt[e] = t2[b & 255u];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double r = (double)rf[e];
+        double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+        q = fma(q, r, 0.5);
+        p[e] = fma(r * r, q, r);                       // e^r - 1
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double u = fma(Bt[e], p[e], Bt[e]);      // e^(j/1024) e^r
+        if (e < 2) s0 = fma(A[e], u, s0);
+        else s1 = fma(A[e], u, s1);
+    }
 }
 
-// Whether all four logits are finite with |x| < 64 (the range of exp_small), tested as a
-// sum of squares below 64^2: rounding is monotone and every term is >= 0, so the rounded
-// sum reaches 4096 whenever one |x| does reach 64; inf gives inf and NaN fails the test.
+// Whether all four logits are finite with |x| < 31.5 (the range of sum_small4), tested as
+// a sum of squares below 31.5^2: rounding is monotone and every term is >= 0, so the
+// rounded sum reaches 992.25 whenever one |x| does reach 31.5; inf gives inf and NaN fails
+// the test.
 __device__ __forceinline__ bool small_piece(const f32x4 &x) {
     const float q = fmaf(x[3], x[3], fmaf(x[2], x[2], fmaf(x[1], x[1], x[0] * x[0])));
-    return q < 4096.0f;
+    return q < 992.25f;
 }
 
 // A logit as the rule reads it: NaN and -inf give -inf, +inf the largest finite float, and
@@ -287,11 +308,12 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float
     }
 }
 
-// The lane's share of sum_y exp(l(y)) in two parts: pieces whose logits all have |x| < 64
-// add exp(x) directly (sf); any other piece goes, whole, to an online max m and a sum s of
+// The lane's share of sum_y exp(l(y)) in two parts: pieces whose logits all have |x| < 31.5
+// add exp(x) directly (sf, sf2); any other piece goes, whole, to an online max m and a sum s of
 // exp(x - m) (NaN and -inf add 0, +inf counts as the largest finite float).
 struct RowSum {
-    double sf;   // sum of exp(x) over the small pieces
+    double sf;   // sum of exp(x) over the small pieces, in two parts
+    double sf2;
     float m;     // running max over the other pieces (-FLT_MAX before the first)
     double md;   // m as a double
     double s;    // sum of exp(x - m) over the other pieces
@@ -312,9 +334,7 @@ __device__ __forceinline__ float max4_ordered(const f32x4 &x) {
 __device__ __forceinline__ float sum_piece(RowSum &a, const f32x4 &x, const double *tab,
                                            const double *t1, const double *t2) {
     if (__all(small_piece(x))) {
-        const double e0 = exp_small(x[0], t1, t2), e1 = exp_small(x[1], t1, t2);
-        const double e2 = exp_small(x[2], t1, t2), e3 = exp_small(x[3], t1, t2);
-        a.sf += (e0 + e1) + (e2 + e3);
+        sum_small4(x, t1, t2, a.sf, a.sf2);
         return max4_ordered(x);
     }
     const float mx = max4(x);
@@ -336,8 +356,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     __shared__ float s_cv[kTkWaves][kCap];
     __shared__ int32_t s_ci[kTkWaves][kCap];
     __shared__ double s_tab[256];
-    __shared__ double s_t1[513];
-    __shared__ double s_t2[128];
+    __shared__ double s_t1[256];
+    __shared__ double s_t2[256];
     __shared__ double s_sf[kTkWaves];
     __shared__ float s_m[kTkWaves];
     __shared__ double s_s[kTkWaves];
@@ -352,13 +372,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     constexpr float kNInf = -__builtin_huge_valf();
 
     s_tab[tid] = exp2((double)tid / 256.0);
-    for (int k = tid; k < 513; k += kTkThreads) s_t1[k] = exp((double)(k - 256) * 0.25);
-    if (tid < 128) s_t2[tid] = exp((double)tid / 512.0);
+    s_t1[tid] = exp((double)(tid - 128) * 0.25);
+    s_t2[tid] = exp((double)tid / 1024.0);
     if (tid < kTkWaves) s_pub[tid] = kNInf;
     __syncthreads();
 
     WaveCands wc{s_cv[w], s_ci[w], 0, kNInf, s_pub, kNInf};
-    RowSum acc{0.0, -kFltMax, (double)-kFltMax, 0.0};
+    RowSum acc{0.0, 0.0, -kFltMax, (double)-kFltMax, 0.0};
 
     // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
     const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);
@@ -378,21 +398,56 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     const f32x4 *vp = reinterpret_cast<const f32x4 *>(rp + a0);
     constexpr int64_t kTrip = 4 * kTkThreads;
     const int64_t nfull = nvec / kTrip * kTrip;
-    for (int64_t base = 0; base < nfull; base += kTrip) {
-        f32x4 raw[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)  // non-temporal: every logit is read once
-            raw[u] = __builtin_nontemporal_load(vp + base + u * kTkThreads + tid);
-        refresh_shared(wc);
-        float mx[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) mx[u] = sum_piece(acc, raw[u], s_tab, s_t1, s_t2);
-        // most trips hold no logit that could enter: one test for the four pieces
-        if (!__any(may_enter(wc, max4_ordered(f32x4{mx[0], mx[1], mx[2], mx[3]}), K))) continue;
+    // one trip's loads: buffer loads from the trip's start (kept in scalar registers) at
+    // 32-bit lane offsets; non-temporal, since every logit is read once
+    auto fetch = [&](f32x4 (&raw)[4], int64_t base) __attribute__((always_inline)) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<f32x4 *>(vp + base), 0,
+                                                          (int)(kTrip * 16), kRsrcWord3);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            offer_piece(wc, raw[u], mx[u], 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)),
-                        K, w, lane);
+            raw[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, (u * kTkThreads + tid) * 16, 0, kNonTemporal));
+    };
+    // one trip's sums and offers.  The common case, every piece small, is one block, so
+    // that its sixteen exponentials interleave.  Most trips hold no logit that could enter
+    // (one test for the four pieces); the others offer their pieces one at a time.
+    auto trip = [&](const f32x4 (&raw)[4], int64_t base) __attribute__((always_inline)) {
+        float mx[4];
+        if (__all(small_piece(raw[0]) & small_piece(raw[1]) & small_piece(raw[2]) &
+                  small_piece(raw[3]))) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sum_small4(raw[u], s_t1, s_t2, acc.sf, acc.sf2);
+                mx[u] = max4_ordered(raw[u]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mx[u] = sum_piece(acc, raw[u], s_tab, s_t1, s_t2);
+        }
+        refresh_shared(wc);
+        if (!__any(may_enter(wc, max4_ordered(f32x4{mx[0], mx[1], mx[2], mx[3]}), K))) return;
+        f32x4 r0 = raw[0], r1 = raw[1], r2 = raw[2], r3 = raw[3];
+        float m0 = mx[0], m1 = mx[1], m2 = mx[2], m3 = mx[3];
+#pragma unroll 1
+        for (int u = 0; u < 4; ++u) {
+            offer_piece(wc, r0, m0, 4, (int32_t)(a0 + 4 * (base + u * kTkThreads + tid)), K, w,
+                        lane);
+            r0 = r1; r1 = r2; r2 = r3;
+            m0 = m1; m1 = m2; m2 = m3;
+        }
+    };
+    // two buffers: each trip's loads are in flight during the trip before.  The loads are
+    // issued unconditionally (past the last trip they re-read the trip before, in bounds)
+    // so that the wait before a trip's math counts that trip's loads only.
+    f32x4 ra[4], rb[4];
+    if (nfull > 0) fetch(ra, 0);
+    for (int64_t base = 0; base < nfull; base += 2 * kTrip) {
+        const bool two = base + kTrip < nfull;
+        fetch(rb, two ? base + kTrip : base);
+        trip(ra, base);
+        if (!two) break;
+        fetch(ra, base + 2 * kTrip < nfull ? base + 2 * kTrip : base);
+        trip(rb, base + kTrip);
     }
     if (nfull < nvec) {
 #pragma unroll
@@ -418,7 +473,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     float M = acc.m;
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     double S = acc.s * exp_core(fmax(acc.md - (double)M, -700.0), s_tab);
-    double SF = acc.sf;
+    double SF = acc.sf + acc.sf2;
     for (int off = 32; off > 0; off >>= 1) {
         S += __shfl_xor(S, off, 64);
         SF += __shfl_xor(SF, off, 64);
@@ -477,9 +532,29 @@ __device__ __forceinline__ double readlane_f64(double x, int lane) {
     return __hiloint2double(hi, lo);
 }
 
+// Maximum over the wavefront of unsigned 32-bit values, in every lane: within each row of
+// 16 lanes by DPP butterflies (quad_perm 1032 and 2301, row_half_mirror, row_mirror), then
+// across rows by the gfx950 row swaps (permlane16_swap exchanges rows 1 and 3 of its first
+// operand with rows 0 and 2 of its second, permlane32_swap the upper half of the first
+// with the lower half of the second; with both operands equal the two results hold the
+// two partners of each lane pair).
+__device__ __forceinline__ uint32_t wave_max_all_u32(uint32_t x) {
+    x = max(x, dpp_u32<0xb1, 0xf>(x));
+    x = max(x, dpp_u32<0x4e, 0xf>(x));
+    x = max(x, dpp_u32<0x141, 0xf>(x));
+    x = max(x, dpp_u32<0x140, 0xf>(x));
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)a[0], (uint32_t)a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max((uint32_t)c[0], (uint32_t)c[1]);
+}
+
 // One wavefront per sequence (T <= 64: one lane per node).  Row i's lists sit at
-// [b][i][K] for i < T - 1.  Each lane keeps its head child (the best one not admitted yet)
-// and the one after it in registers, so an admission reads no memory on its critical path.
+// [b][i][K] for i < T - 1, staged in LDS.  Each lane keeps its head child (the best one not
+// admitted yet) and the one after it in registers; an admission is a wavefront maximum of
+// the high words of the order-preserving keys (the low words only break a tie), read-lane
+// broadcasts of the winner, and branch-free updates; every lane then re-reads the child
+// after its head, which the next admission needs only after its own maximum.
 __global__ __launch_bounds__(64) void best_first_kernel(
     const int32_t *__restrict__ top_tok, const double *__restrict__ top_logp,
     const int32_t *__restrict__ root_token, int T, int K, int max_levels,
@@ -496,16 +571,15 @@ __global__ __launch_bounds__(64) void best_first_kernel(
     }
     __syncthreads();
 
+    const int lrow = (lane < nr ? lane : 0) * K;  // this lane's row (row 0 for lanes past it)
     int rank = 0;                                 // rank of the head child
     double hlp = 0.0, nlp = 0.0;                  // log-probs of the head child and the next
     int32_t htok = -1, ntok = -1;
-    if (lane < nr) {
-        hlp = s_lp[lane * K];
-        htok = s_tk[lane * K];
-        if (K > 1) {
-            nlp = s_lp[lane * K + 1];
-            ntok = s_tk[lane * K + 1];
-        }
+    if (nr > 0) {
+        hlp = s_lp[lrow];
+        htok = s_tk[lrow];
+        nlp = s_lp[lrow + min(1, K - 1)];
+        ntok = s_tk[lrow + min(1, K - 1)];
     }
     int32_t par = -1, tok = lane == 0 ? root_token[b] : -1;
     double cj = 0.0;                              // this node's cumulative log-prob
@@ -513,28 +587,36 @@ __global__ __launch_bounds__(64) void best_first_kernel(
     bool live = lane == 0 && nr > 0 && max_levels > 1;   // has a pending child
     for (int n = 1; n < T; ++n) {
         const double key = cj + hlp;
-        const int win = wave_argmax_key(live ? ord_f64(key) : 0);
-        if (win < 0) break;    // nothing pending: excluded by the caller's shape check
+        const uint64_t ok = live ? ord_f64(key) : 0;
+        // (the maxima run in every lane: the row swaps and DPP reads need all lanes active)
+        const uint32_t hi = (uint32_t)(ok >> 32);
+        const uint32_t mhi = wave_max_all_u32(hi);
+        const bool cand = ok != 0 && hi == mhi;
+        uint64_t bal = __ballot(cand);
+        if (bal == 0) break;    // nothing pending: excluded by the caller's shape check
+        if (bal & (bal - 1)) {  // several keys share the high word
+            const uint32_t lo = cand ? (uint32_t)ok : 0u;
+            const uint32_t mlo = wave_max_all_u32(lo);
+            bal = __ballot(cand && lo == mlo);
+        }
+        const int win = (int)__builtin_ctzll(bal);
         const double wkey = readlane_f64(key, win);
         const int32_t wtok = __builtin_amdgcn_readlane(htok, win);
         const int wlevel = __builtin_amdgcn_readlane(level, win);
-        if (lane == win) {
-            ++rank;
-            live = rank < K;
-            hlp = nlp;
-            htok = ntok;
-            if (rank + 1 < K) {
-                nlp = s_lp[lane * K + rank + 1];
-                ntok = s_tk[lane * K + rank + 1];
-            }
-        }
-        if (lane == n) {
-            par = win;
-            tok = wtok;
-            cj = wkey;
-            level = wlevel + 1;
-            live = n < nr && level < max_levels;
-        }
+        const bool won = lane == win;
+        rank += won ? 1 : 0;
+        live = won ? rank < K : live;
+        hlp = won ? nlp : hlp;
+        htok = won ? ntok : htok;
+        const bool fresh = lane == n;
+        par = fresh ? win : par;
+        tok = fresh ? wtok : tok;
+        cj = fresh ? wkey : cj;
+        level = fresh ? wlevel + 1 : level;
+        live = fresh ? (n < nr && wlevel + 1 < max_levels) : live;
+        const int nx = lrow + min(rank + 1, K - 1);
+        nlp = s_lp[nx];
+        ntok = s_tk[nx];
     }
     if (lane < T) {
         parents[(int64_t)b * T + lane] = par;
