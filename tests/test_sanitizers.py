@@ -1,11 +1,14 @@
 """AddressSanitizer and UndefinedBehaviorSanitizer on the CPU.
 
-The oracle (gcc) runs all its pins, and the host side of libsv (hipcc, host pass only;
-the device code is built as usual) runs the C-ABI boundary checks, each in a subprocess
-with the sanitizer runtime preloaded; any report fails the test.  A canary -- a small
+The oracle (gcc) runs all its pins, every planted mistake of test_oracle_mutants is run
+against the pins again, and the host side of libsv (hipcc, host pass only; the device
+code is built as usual) runs the C-ABI boundary checks, each in a subprocess with the
+sanitizer runtime preloaded; any report from the real oracle or libsv fails the test, and
+a mutant counts as caught by a failing pin or by a sanitizer report.  A canary -- a small
 CPU library with a planted heap overflow and an oversized shift, built the same way --
 shows that each harness does report.  Nothing here touches a GPU.
 """
+import concurrent.futures as cf
 import ctypes.util  # noqa: F401  (the subprocesses use ctypes)
 import glob
 import os
@@ -49,7 +52,7 @@ def _clang_asan_runtime():
 
 
 def _run(code, preload, extra_env=None, timeout=600):
-    env = dict(os.environ, LD_PRELOAD=preload, **ENV_SAN, **(extra_env or {}))
+    env = {**os.environ, "LD_PRELOAD": preload, **ENV_SAN, **(extra_env or {})}
     return subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                           env=env, timeout=timeout, cwd=ROOT)
 
@@ -92,6 +95,33 @@ def test_oracle_pins_under_asan_ubsan(build_dir):
     assert r.returncode == 0, r.stderr[-4000:]
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
     assert "pins" in r.stdout
+
+
+def test_mutants_caught_under_asan_ubsan(build_dir):
+    sys.path.insert(0, HERE)
+    import test_oracle_mutants as tm
+    src = open(ORACLE_SRC).read()
+    runtime = _gcc_asan_runtime()
+
+    def one(m):
+        name, old, new, occ = m
+        path = os.path.join(build_dir, f"mutant_{name}.c")
+        with open(path, "w") as f:
+            f.write(tm._mutate(src, old, new, occ))
+        lib = os.path.join(build_dir, f"libmutant_{name}.so")
+        subprocess.run(["gcc", "-O1", "-std=c11", "-ffp-contract=off", "-fopenmp", "-shared",
+                        "-fPIC", *GCC_SAN, path, "-o", lib, "-lm"], check=True)
+        r = _run(tm._RUNNER.format(tests=HERE, root=ROOT, lib=lib), runtime,
+                 {"OMP_NUM_THREADS": "1"}, timeout=300)
+        by_pin = r.returncode == 3
+        by_sanitizer = r.returncode != 0 and ("AddressSanitizer" in r.stderr or
+                                              "runtime error" in r.stderr)
+        return name, by_pin or by_sanitizer, r.returncode, r.stderr[-1500:]
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        results = list(ex.map(one, tm.MUTANTS))
+    missed = [(n, rc, err) for n, ok, rc, err in results if not ok]
+    assert not missed, missed
 
 
 @pytest.mark.skipif(_clang_asan_runtime() is None, reason="clang ASan runtime not installed")
