@@ -25,7 +25,8 @@
 namespace sv {
 namespace {
 
-constexpr int kTile = 256;  // elements per tile of the draw's in-chunk search
+constexpr int kTile = 256;      // elements per tile of the draw's in-chunk search
+constexpr int kMaxTiles = 64;   // tiles per chunk at most (16384 elements)
 
 struct MS {
     float m;  // running max (-inf: nothing seen)
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
     __shared__ float s_f[4];          // row max, draw target (weights), row sum
     __shared__ int32_t ex_tok[64];    // tokens rejected at the final node
     __shared__ float ex_w[64];        // and their weights
-    __shared__ float tile_sum[kTile]; // per-tile weights of the chosen chunk (<= 256 tiles)
-    __shared__ float red[kTile * 65]; // lane partials of the tile weights
+    __shared__ float tile_sum[kMaxTiles];    // per-tile weights of the chosen chunk
+    __shared__ float red[kMaxTiles * 65];    // lane partials of the tile weights
     __shared__ int s_pick[2];         // chosen chunk, chosen tile
     __shared__ float s_r[2];          // residual target in the chunk, in the tile
 
@@ -305,36 +306,32 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
         const int64_t lo = (int64_t)pc * chunk;
         const int64_t hi = lo + chunk < V ? lo + chunk : V;
         const int ntile = (int)((hi - lo + kTile - 1) / kTile);
-        // tile weights: wave w owns tiles 16w .. 16w + 15 and loads 8 of them at a time
-        // (lane l: elements l, l + 64, l + 128, l + 192 of each, coalesced; groups that lie
-        // inside the chunk load without checks); each lane's partial sums go to LDS (row
-        // stride 65: no bank conflicts), then thread t adds up tile t's 64
-        for (int t0 = 16 * w; t0 < 16 * w + 16 && t0 < ntile; t0 += 8) {
-            const float *tb = row + lo + (int64_t)t0 * kTile + lane;
-            const int64_t y0 = lo + (int64_t)t0 * kTile + lane;
-            float x[8][4];
-            if (lo + (int64_t)(t0 + 8) * kTile <= hi) {
+        // tile weights: wave w owns tiles w, w + 16, w + 32, w + 48 and loads them in one
+        // round (lane l: elements l, l + 64, l + 128, l + 192 of each, coalesced); each lane's
+        // partial sums go to LDS (row stride 65: no bank conflicts), then thread t adds up
+        // tile t's 64
+        {
+            static_assert(kMaxTiles == 4 * kWalkWaves, "four tiles per wavefront");
+            float x[4][4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const int t = w + kWalkWaves * j;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) x[j][q] = tb[j * kTile + 64 * q];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        x[j][q] = y0 + j * kTile + 64 * q < hi ? tb[j * kTile + 64 * q]
-                                                              : -__builtin_huge_valf();
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t y = lo + (int64_t)t * kTile + lane + 64 * q;
+                    x[j][q] = t < ntile && y < hi ? row[y] : -__builtin_huge_valf();
+                }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 float s = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float l = clean_logit(x[j][q]);
                     if (l > -__builtin_huge_valf()) s += __builtin_amdgcn_exp2f((l - mv) * k);
                 }
-                if (t0 + j < ntile) red[(t0 + j) * 65 + lane] = s;
+                const int t = w + kWalkWaves * j;
+                if (t < ntile) red[t * 65 + lane] = s;
             }
         }
         __syncthreads();
@@ -447,8 +444,10 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
 
 int make_sample_plan(int64_t rows, int64_t V, ArgmaxPlan *p) {
     if (make_argmax_plan(rows, V, p) != 0) return SV_ERR_SHAPE;
-    // the draw searches one chunk by 256-element tiles: at most 65536 elements a chunk
-    const int64_t cap = (int64_t)kTile * kTile;
+    // the draw re-reads one chunk of the final node's row, by 256-element tiles: at most
+    // kMaxTiles tiles a chunk keep that read to one round of loads, while the streaming
+    // pass still has several workgroups per row
+    const int64_t cap = (int64_t)kTile * kMaxTiles;
     if (p->chunk > cap) {
         p->chunk = cap;
         p->nchunks = (int)((V + cap - 1) / cap);
