@@ -50,63 +50,101 @@ def attention_traffic(inp, depth):
     return kv_prefix + kv_tree + q + o, flops
 
 
-def cpu_baseline(inp, budget_s=15.0):
-    """The oracle on whole sequences of the workload, one after another, until the time
-    budget is spent: mask, attention for every head and node, accept, commit."""
+def _oracle_sequence(orc, O, inp, b, heads, threads):
+    """One sequence of a workload through the oracle (mask, attention for the first `heads`
+    q heads and every node, accept, commit); returns the seconds of each stage."""
     import numpy as np
+    from _support import to_np
+
+    w = inp.w
+    _, Hkv, bs, D = inp.k_pool.shape
+    nblk = int((inp.block_table[b] >= 0).sum())
+    blocks = inp.block_table[b, :nblk].long()
+    cache = O.Cache(k=to_np(inp.k_pool.index_select(0, blocks)),
+                    v=to_np(inp.v_pool.index_select(0, blocks)),
+                    table=np.arange(nblk, dtype=np.int32)[None], block_size=bs,
+                    block_stride=Hkv * bs * D, head_stride=bs * D, row_stride=D,
+                    num_blocks=nblk, dtype=O.BF16 if w.dtype == "bf16" else O.F32)
+    parents = to_np(inp.parents[b:b + 1])
+    q, kt, vt = to_np(inp.q[b:b + 1]), to_np(inp.k_tree[b:b + 1]), to_np(inp.v_tree[b:b + 1])
+    P = to_np(inp.prefix_len[b:b + 1])
+    logits, draft = to_np(inp.logits[b:b + 1]), to_np(inp.draft[b:b + 1])
+    rows = np.array([[0, h, i] for h in range(heads) for i in range(w.T)], dtype=np.int32)
+    t = {}
+    t0 = time.perf_counter()
+    mask, _, err = orc.build_tree_mask(parents)
+    t["mask"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
+                              nthreads=threads)
+    t["attention"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _, L, nodes, _ = orc.accept_longest_path(logits, draft, parents, err)
+    t["accept"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.kv_commit(kt, vt, L, nodes, err, cache, P, int(P.max()))
+    t["commit"] = time.perf_counter() - t0
+    return t
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(inp, seed, budget_s=15.0):
+    """The oracle on whole sequences of the workload, one after another, until the time
+    budget is spent: mask, attention for every head and node, accept, commit.  Then, with
+    one thread, one step of each small workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as O
-    from _support import to_np
+    from tree_masked_verify_amd import workloads as wl
 
     w = inp.w
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     orc = O.Oracle()
-    _, Hkv, bs, D = inp.k_pool.shape
-    done, spent, heads_used = 0, 0.0, w.Hq
+    done, heads_used = 0, w.Hq
+    stages = {"mask": 0.0, "attention": 0.0, "accept": 0.0, "commit": 0.0}
     for b in range(w.B):
-        nblk = int((inp.block_table[b] >= 0).sum())
-        blocks = inp.block_table[b, :nblk].long()
-        cache = O.Cache(k=to_np(inp.k_pool.index_select(0, blocks)),
-                        v=to_np(inp.v_pool.index_select(0, blocks)),
-                        table=np.arange(nblk, dtype=np.int32)[None], block_size=bs,
-                        block_stride=Hkv * bs * D, head_stride=bs * D, row_stride=D,
-                        num_blocks=nblk, dtype=O.BF16 if w.dtype == "bf16" else O.F32)
-        parents = to_np(inp.parents[b:b + 1])
-        q, kt, vt = to_np(inp.q[b:b + 1]), to_np(inp.k_tree[b:b + 1]), to_np(inp.v_tree[b:b + 1])
-        P = to_np(inp.prefix_len[b:b + 1])
-        logits, draft = to_np(inp.logits[b:b + 1]), to_np(inp.draft[b:b + 1])
-        heads = w.Hq
+        heads = heads_used
         if b == 0:
             # a sequence too large for the budget is sampled by heads (scaled to all heads)
-            rows = np.array([[0, 0, i] for i in range(w.T)], dtype=np.int32)
-            t0 = time.perf_counter()
-            mask, _, err = orc.build_tree_mask(parents)
-            orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale,
-                                      rows=rows, nthreads=threads)
-            t_head = time.perf_counter() - t0
+            t_head = _oracle_sequence(orc, O, inp, 0, 1, threads)["attention"]
             heads = heads_used = max(1, min(w.Hq, int(budget_s / max(t_head, 1e-9))))
-        t0 = time.perf_counter()
-        mask, _, err = orc.build_tree_mask(parents)
-        rows = np.array([[0, h, i] for h in range(heads) for i in range(w.T)], dtype=np.int32)
-        orc.tree_verify_attention(q, kt, vt, cache, P, int(P.max()), mask, inp.scale, rows=rows,
-                                  nthreads=threads)
-        t_attn = time.perf_counter() - t0
-        t1 = time.perf_counter()
-        _, L, nodes, _ = orc.accept_longest_path(logits, draft, parents, err)
-        orc.kv_commit(kt, vt, L, nodes, err, cache, P, int(P.max()))
-        t_rest = time.perf_counter() - t1
-        spent += t_attn * (w.Hq / heads) + t_rest     # that sequence's full step
+        t = _oracle_sequence(orc, O, inp, b, heads, threads)
+        t["attention"] *= w.Hq / heads                 # that sequence's full step
+        for k in stages:
+            stages[k] += t[k]
         done += 1
-        if heads < w.Hq or spent >= budget_s:
+        if heads < w.Hq or sum(stages.values()) >= budget_s:
             break
+    spent = sum(stages.values())
     t_step = spent / done * w.B
+    # one thread, one whole step of each small workload
+    single = {}
+    for name in ("tiny", "parity512", "chain2k"):
+        sw = wl.WORKLOADS[name]
+        sinp = wl.make_inputs(sw, seed=seed, device="cpu")
+        tot = {"mask": 0.0, "attention": 0.0, "accept": 0.0, "commit": 0.0}
+        for b in range(sw.B):
+            for k, v in _oracle_sequence(orc, O, sinp, b, sw.Hq, 1).items():
+                tot[k] += v
+        single[name] = {k: round(v * 1e3, 3) for k, v in tot.items()}
     return {"value": w.B * w.T / t_step, "unit": "verified tree tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"sequences 0..{done - 1} of {w.B} in full (mask, attention for "
                       f"{heads_used} of {w.Hq} q heads x {w.T} nodes"
                       f"{' scaled to all heads' if heads_used < w.Hq else ''}, accept over "
                       f"{w.V} logits, commit); step time = {w.B} x the mean sequence; "
-                      f"{spent:.1f} s of oracle time"}
+                      f"{spent:.1f} s of oracle time",
+            "stage_s_per_step": {k: round(v / done * w.B, 3) for k, v in stages.items()},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "single_thread_small_configs_ms": single}
 
 
 def counter_traffic(workload):
@@ -568,7 +606,7 @@ def main():
             result["batched8k"] = secondary_workload("batched8k", dev, args.seed)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(inp)
+        result["cpu_baseline"] = cpu_baseline(inp, args.seed)
     print(json.dumps(result), flush=True)
 
 
