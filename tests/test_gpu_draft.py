@@ -91,14 +91,21 @@ def test_topk_random(orc, R, V, K):
 
 
 @pytest.mark.parametrize("loc,std", [(0.0, 50.0), (1000.0, 3.0), (-500.0, 3.0), (60.0, 4.0),
-                                     (-62.0, 3.0), (0.0, 1e-3)])
+                                     (-62.0, 3.0), (30.0, 2.0), (-31.0, 1.0), (0.0, 1e-3)])
 def test_topk_wide_range(orc, loc, std):
-    """Logits beyond the small-range path (|x| >= 64) alone and mixed with small ones:
-    far above and far below zero, straddling +-64, and tightly packed."""
+    """Logits beyond the small-range path (|x| >= 31.5) alone and mixed with small ones:
+    far above and far below zero, straddling +-31.5 and +-64, the values at the edge of the
+    range's tables, and tightly packed."""
     rng = np.random.default_rng(int(abs(loc)) + 7)
     x = (loc + std * rng.normal(size=(6, 20011))).astype(np.float32)
     x[1, ::97] = np.float32(loc + 200.0)           # a few far larger entries
     x[2, :] = np.where(rng.random(20011) < 0.5, x[2, :], np.float32(-70.0))
+    edge = np.float32(31.5)
+    below = np.nextafter(edge, np.float32(0))
+    x[3, ::53] = edge                              # just outside the small range
+    x[3, 1::53] = -edge
+    x[3, 2::53] = below                            # the largest logits inside it
+    x[3, 3::53] = -below
     check_topk(orc, x, 16, label=f"loc {loc} std {std}")
 
 

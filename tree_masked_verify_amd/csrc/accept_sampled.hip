@@ -18,8 +18,9 @@
 // workgroup per sequence: wave 0 merges the pairs of each row, checks the tree and
 // walks it (one lane per node, proposals in order through a uniform loop); then the
 // workgroup locates the drawn token: the chunk from the chunk pairs (a wave prefix scan),
-// the 256-element tile inside it from tile sums (one coalesced pass over the chunk), and
-// the element inside the tile from a wavefront prefix scan over its 256 logits.
+// the 256-element tile inside it from tile sums (one coalesced pass over the chunk, which
+// leaves the element weights in LDS), and the element inside the tile from a wavefront
+// prefix scan over its 256 weights.
 #include "sv_internal.h"
 
 namespace sv {
@@ -115,11 +116,6 @@ __device__ __forceinline__ float weight_of(float raw, float m, float k) {
     return l == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f((l - m) * k);
 }
 
-// Weight of token y in a row whose max is m.
-__device__ __forceinline__ float weight(const float *row, int64_t y, float m, float k) {
-    return weight_of(row[y], m, k);
-}
-
 constexpr int kWalkWaves = 16;  // wavefronts of the walk kernel's workgroup
 
 __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
@@ -139,6 +135,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
     __shared__ float ex_w[64];        // and their weights
     __shared__ float tile_sum[kMaxTiles];    // per-tile weights of the chosen chunk
     __shared__ float red[kMaxTiles * 65];    // lane partials of the tile weights
+    __shared__ float ew[kMaxTiles * kTile];  // the chosen chunk's element weights
     __shared__ int s_pick[2];         // chosen chunk, chosen tile
     __shared__ float s_r[2];          // residual target in the chunk, in the tile
 
@@ -156,13 +153,13 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
         MS st{-__builtin_huge_valf(), 0.0f};
         if (in) {
             const MS *pr = part + (row0 + lane) * nchunks;
-            for (int c0 = 0; c0 < nchunks; c0 += 8) {  // eight pairs in flight
-                MS q[8];
+            for (int c0 = 0; c0 < nchunks; c0 += 16) {  // sixteen pairs in flight
+                MS q[16];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < 16; ++j)
                     q[j] = c0 + j < nchunks ? pr[c0 + j] : MS{-__builtin_huge_valf(), 0.0f};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) st = ms_merge(st, q[j], k);
+                for (int j = 0; j < 16; ++j) st = ms_merge(st, q[j], k);
             }
         }
         const bool bad = (lane == 0 && p != -1) || (lane >= 1 && in && (p < 0 || p >= lane));
@@ -307,9 +304,10 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
         const int64_t hi = lo + chunk < V ? lo + chunk : V;
         const int ntile = (int)((hi - lo + kTile - 1) / kTile);
         // tile weights: wave w owns tiles w, w + 16, w + 32, w + 48 and loads them in one
-        // round (lane l: elements l, l + 64, l + 128, l + 192 of each, coalesced); each lane's
-        // partial sums go to LDS (row stride 65: no bank conflicts), then thread t adds up
-        // tile t's 64
+        // round (lane l: elements l, l + 64, l + 128, l + 192 of each, coalesced); the
+        // element weights stay in LDS for the search inside the chosen tile, each lane's
+        // partial sums go to LDS too (row stride 65: no bank conflicts), then thread t adds
+        // up tile t's 64
         {
             static_assert(kMaxTiles == 4 * kWalkWaves, "four tiles per wavefront");
             float x[4][4];
@@ -324,13 +322,16 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                const int t = w + kWalkWaves * j;
                 float s = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float l = clean_logit(x[j][q]);
-                    if (l > -__builtin_huge_valf()) s += __builtin_amdgcn_exp2f((l - mv) * k);
+                    const float wy =
+                        l > -__builtin_huge_valf() ? __builtin_amdgcn_exp2f((l - mv) * k) : 0.0f;
+                    s += wy;
+                    if (t < ntile) ew[t * kTile + lane + 64 * q] = wy;
                 }
-                const int t = w + kWalkWaves * j;
                 if (t < ntile) red[t * 65 + lane] = s;
             }
         }
@@ -395,12 +396,13 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
         __syncthreads();
         const int tp = s_pick[1];
         if (w == 0 && tp >= 0) {
-            // lane l owns elements 4l .. 4l+3 of the tile, in index order
+            // lane l owns elements 4l .. 4l+3 of the tile, in index order (their weights
+            // from LDS; elements past the chunk hold 0)
             const int64_t base = lo + (int64_t)tp * kTile + 4 * lane;
             float e[4];
             for (int q = 0; q < 4; ++q) {
                 const int64_t y = base + q;
-                float wy = y < hi ? weight(row, y, mv, k) : 0.0f;
+                float wy = ew[tp * kTile + 4 * lane + q];
                 for (int j = 0; j < nex; ++j)
                     if (ex_tok[j] == y) wy = 0.0f;
                 e[q] = wy;
