@@ -25,9 +25,19 @@ __device__ __forceinline__ double load_x(const void *base, int64_t idx) {
     return (double)static_cast<const float *>(base)[idx];
 }
 
+// fp64 -> fp32, nearest with ties to even.  The empty statement keeps the compiler from
+// fusing this rounding with a following fp32 -> bf16 one into a single fp64 -> bf16
+// rounding (round to odd in between), which would differ from rounding twice to nearest
+// and costs a compare-and-adjust sequence per element.
+__device__ __forceinline__ float to_f32(double v) {
+    float f = (float)v;
+    asm volatile("" : "+v"(f));
+    return f;
+}
+
 template <bool kBF16>
 __device__ __forceinline__ void store_x(void *base, int64_t idx, double v) {
-    const float f = (float)v;  // nearest, ties to even
+    const float f = to_f32(v);  // nearest, ties to even
     if (kBF16)
         static_cast<__bf16 *>(base)[idx] = (__bf16)f;  // nearest, ties to even
     else
@@ -91,7 +101,7 @@ struct RopeVec<true> {
     static constexpr int V = 8;
     static __device__ __forceinline__ double get(const T &x, int v) { return (double)(float)x[v]; }
     static __device__ __forceinline__ void put(T &x, int v, double r) {
-        x[v] = (__bf16)(float)r;  // nearest even, twice
+        x[v] = (__bf16)to_f32(r);  // nearest even, twice
     }
 };
 template <>
@@ -99,7 +109,7 @@ struct RopeVec<false> {
     using T = f32x4;
     static constexpr int V = 4;
     static __device__ __forceinline__ double get(const T &x, int v) { return (double)x[v]; }
-    static __device__ __forceinline__ void put(T &x, int v, double r) { x[v] = (float)r; }
+    static __device__ __forceinline__ void put(T &x, int v, double r) { x[v] = to_f32(r); }
 };
 
 template <bool kBF16>
