@@ -190,7 +190,9 @@ __device__ __forceinline__ Cursor cursor_add(Cursor c, int n, int bs) {
 // read); completion is tracked explicitly with vmcnt, and the stages a load writes
 // are ordered against their readers by the barriers (which carry memory clobbers).
 // M0 carries the LDS base; an SALU write of M0 needs one wait state before an
-// LDS-DMA instruction reads it.  kNT adds the non-temporal hint (nt), for keys that one
+// LDS-DMA instruction reads it.  M0 is listed as clobbered; the compiler reserves it (and
+// warns about the clobber) but emits no use of M0 of its own in these kernels, so no value
+// of it lives across the statement.  kNT adds the non-temporal hint (nt), for keys that one
 // workgroup alone streams through once: at the board's power limit the call then takes
 // ~2% less time.  Row groups that share a chunk go without it, as it makes them meet in
 // L2 less often (+16% HBM reads at the batched 8K shape).

@@ -413,8 +413,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     // (one test for the four pieces); the others offer their pieces one at a time.
     auto trip = [&](const f32x4 (&raw)[4], int64_t base) __attribute__((always_inline)) {
         float mx[4];
-        if (__all(small_piece(raw[0]) & small_piece(raw[1]) & small_piece(raw[2]) &
-                  small_piece(raw[3]))) {
+        // (all four tested, without short-circuit branches: a bitwise and of the lane masks)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wbitwise-instead-of-logical"
+        const bool all_small = small_piece(raw[0]) & small_piece(raw[1]) & small_piece(raw[2]) &
+                               small_piece(raw[3]);
+#pragma clang diagnostic pop
+        if (__all(all_small)) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 sum_small4(raw[u], s_t1, s_t2, acc.sf, acc.sf2);
