@@ -252,3 +252,76 @@ def test_append_compact_validation(lib):
         assert f(c=cache(k=FAKE + 8)) == -11
     assert app(kt=FAKE + 2) == -11 and app(kt=None) == -1 and app(err=None) == -1
     assert cmp(L=None) == -1
+
+
+# ----------------------------------------------------------------------------- fuzzing
+# Random (often extreme) sizes through every size query and every entry point.  Each
+# entry-point call leaves one required pointer NULL, so no call may get past the host
+# checks: it returns a negative status, or 0 for an empty batch (nothing enqueued).  Under
+# the sanitizer build (test_sanitizers.py) this also checks the host code's size
+# arithmetic for overflow and out-of-bounds reads.
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+I32 = st.one_of(st.integers(-3, 70), st.sampled_from([128, 256, 512, 1000, 1024, 4096, 65536,
+                                                      1 << 20, (1 << 31) - 1, -(1 << 31)]),
+                st.integers(-(1 << 31), (1 << 31) - 1))
+I64 = st.one_of(I32, st.sampled_from([1 << 32, 1 << 40, (1 << 62), (1 << 63) - 1, -(1 << 63)]))
+FUZZ = settings(max_examples=150, deadline=None,
+                suppress_health_check=[HealthCheck.function_scoped_fixture])
+
+
+def _ok_or_empty(rc, *sizes):
+    assert rc < 0 or (rc == 0 and min(sizes) <= 0), (rc, sizes)
+
+
+@FUZZ
+@given(B=I32, Hq=I32, Hkv=I32, T=I32, D=I32, P=I32, dt=st.integers(-2, 4), splits=I32,
+       V=I64, K=I32)
+def test_fuzz_workspace_sizes(lib, B, Hq, Hkv, T, D, P, dt, splits, V, K):
+    n = lib.sv_tree_verify_attention_workspace_size(B, Hq, Hkv, T, D, P, dt, splits)
+    assert n == 0 or (n >= 256 * 1024 + 256 and n % 256 == 0), n
+    for f in (lib.sv_accept_longest_path_workspace_size, lib.sv_accept_sampled_workspace_size):
+        assert f(B, T, V) >= 0
+    assert lib.sv_draft_tree_workspace_size(B, T, K) >= 0
+
+
+@FUZZ
+@given(B=I32, Hq=I32, Hkv=I32, T=I32, D=I32, P=I32, splits=I32, bs=I32, mbs=I32, nb=I64,
+       bstr=I64, hstr=I64, rstr=I64, dt=st.integers(-2, 4), which=st.integers(0, 2))
+def test_fuzz_attention_rejects(lib, B, Hq, Hkv, T, D, P, splits, bs, mbs, nb, bstr, hstr, rstr,
+                                dt, which):
+    c = sv.sv_kv_cache(k=FAKE, v=FAKE, block_table=FAKE, block_size=bs, max_blocks_per_seq=mbs,
+                       num_blocks=nb, block_stride=bstr, head_stride=hstr, row_stride=rstr,
+                       dtype=dt)
+    q, out, mask = (None if which == 0 else FAKE, None if which == 1 else FAKE,
+                    None if which == 2 else FAKE)
+    rc = lib.sv_tree_verify_attention(q, FAKE, FAKE, ctypes.byref(c), FAKE, P, mask, B, Hq, Hkv,
+                                      T, D, 0.0625, out, FAKE, 1 << 40, splits, None)
+    _ok_or_empty(rc, B)
+    rc = lib.sv_tree_verify_attention_noalloc(q, FAKE, FAKE, ctypes.byref(c), FAKE, P, mask, B,
+                                              Hq, Hkv, T, D, 0.0625, out, splits, None)
+    _ok_or_empty(rc, B)
+
+
+@FUZZ
+@given(B=I32, Hq=I32, Hkv=I32, T=I32, D=I32, P=I32, V=I64, K=I32, lv=I32, bs=I32, mbs=I32,
+       nb=I64, dt=st.integers(-2, 4), temp=st.floats(allow_nan=True, allow_infinity=True))
+def test_fuzz_entry_points_reject(lib, B, Hq, Hkv, T, D, P, V, K, lv, bs, mbs, nb, dt, temp):
+    c = sv.sv_kv_cache(k=FAKE, v=FAKE, block_table=FAKE, block_size=bs, max_blocks_per_seq=mbs,
+                       num_blocks=nb, block_stride=(1 << 20), head_stride=(1 << 12),
+                       row_stride=256, dtype=dt)
+    cr = ctypes.byref(c)
+    _ok_or_empty(lib.sv_build_tree_mask(None, B, T, FAKE, FAKE, FAKE, None), B)
+    _ok_or_empty(lib.sv_accept_longest_path(None, FAKE, FAKE, None, B, T, V, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, 1 << 40, None), B)
+    _ok_or_empty(lib.sv_accept_sampled(None, FAKE, FAKE, None, FAKE, FAKE, temp, B, T, V, FAKE,
+                                       FAKE, FAKE, FAKE, 1 << 40, None), B)
+    _ok_or_empty(lib.sv_rope_tree(None, FAKE, FAKE, FAKE, B, Hq, Hkv, T, D, dt, 10000.0, None),
+                 B)
+    _ok_or_empty(lib.sv_kv_append(None, FAKE, FAKE, cr, FAKE, P, B, Hkv, T, D, None), B)
+    _ok_or_empty(lib.sv_kv_compact(None, FAKE, FAKE, cr, FAKE, P, FAKE, B, Hkv, T, D, None), B)
+    _ok_or_empty(lib.sv_kv_commit(None, FAKE, FAKE, FAKE, FAKE, cr, FAKE, P, FAKE, B, Hkv, T, D,
+                                  None), B)
+    _ok_or_empty(lib.sv_topk_logprobs(None, B, V, K, FAKE, FAKE, None), B)
+    _ok_or_empty(lib.sv_draft_tree(None, FAKE, B, T, V, K, lv, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                   None), B)
