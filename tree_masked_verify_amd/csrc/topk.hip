@@ -14,8 +14,9 @@
 //   next, ties to the one offered first; until T nodes.
 //
 // topk_rows_kernel: one workgroup of four wavefronts per row.  Every lane streams its
-// 16-byte pieces once and keeps an online max and an fp64 sum of exponentials
-// (sum_small4 / exp_core below).  Each wavefront keeps a candidate buffer in LDS: a piece's
+// 16-byte pieces once (buffer loads, each trip's loads in flight during the trip before)
+// and keeps fp64 sums of exponentials (sum_small4 for pieces of logits below 31.5 in
+// magnitude; otherwise an online max and exp_core, below).  Each wavefront keeps a candidate buffer in LDS: a piece's
 // element enters it when it beats the wavefront's K-th best so far (while fewer than K
 // entries exist, every element enters) and is not below the K-th best another wavefront
 // has published.  When the buffer grows, the wavefront keeps its K best (K rounds of a
