@@ -74,6 +74,7 @@ struct Geo {
     static constexpr int SMEM = FLAG_OFF + 16;
     static_assert(D == 128 || D == 256, "head_dim 128 or 256");
     static_assert(SMEM <= 160 * 1024, "LDS budget");
+    static_assert(NST * STAGE_BYTES >= kW * DB * 4 * 64 * 16, "stages hold the O staging");
     static_assert((KU % 256) == 16 && (VU % 256) == 64, "bank offsets");
 };
 
@@ -794,12 +795,48 @@ void attn_w4_kernel(MfmaParams p) {
     // below); otherwise the chunk's partial result (O unnormalised, reference max, sum)
     const bool direct = p.counters && nv == 1;
     const int64_t ubase = ((int64_t)b * p.Hkv + kvh) * p.S * (int64_t)p.R;  // slot (s, r): ubase + s R + r
+    if (direct) {
+        // The whole prefix in this chunk: O is normalised on its way out.  Row block by row
+        // block, the accumulators go to LDS (the ring's stages, free once every wavefront
+        // is past its last tile: 8 KiB per d block and wavefront), straight from the
+        // accumulation registers (only stores read those, which keeps the allocator from
+        // moving them out), and come back one d block at a time to be scaled and stored.
+        // (Writing O unnormalised to the output and rescaling it there wrote it to HBM
+        // twice whenever L2 evicted the lines in between: 1.8x the output's bytes at the
+        // batched 8K workload.)
+        __syncthreads();
+        f32x4 *lds_o = reinterpret_cast<f32x4 *>(smem) + w * (DB * 4 * 64);  // [db*4+g4][lane]
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4)
+                    lds_o[(db * 4 + g4) * 64 + lane] =
+                        f32x4{o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2],
+                              o[rb][db][4 * g4 + 3]};
+            const int row = rbase + rb * 32;
+            const float inv = ltot[rb] > 0.0f ? 1.0f / ltot[rb] : 0.0f;
+            float *op = out_row(p, b, kvh, row < p.R ? row : 0) + 4 * h;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                asm volatile("" ::: "memory");  // one d block's lines in flight at a time
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 v = lds_o[(db * 4 + g4) * 64 + lane];
+                    if (row < p.R) *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8) = v * inv;
+                }
+            }
+            asm volatile("" ::: "memory");
+        }
+        return;
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int row = rbase + rb * 32;
         if (row < p.R) {
             const int64_t base = ubase + (int64_t)s * p.R + row;
-            float *op = (direct ? out_row(p, b, kvh, row) : p.ws_o + base * D) + 4 * h;
+            float *op = p.ws_o + base * D + 4 * h;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -807,37 +844,11 @@ void attn_w4_kernel(MfmaParams p) {
                     *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8) =
                         f32x4{o[rb][db][4 * g4], o[rb][db][4 * g4 + 1], o[rb][db][4 * g4 + 2],
                               o[rb][db][4 * g4 + 3]};
-            if (!direct && h == 0) {
+            if (h == 0) {
                 p.ws_ml[base * 2 + 0] = mfin[rb];
                 p.ws_ml[base * 2 + 1] = ltot[rb];
             }
         }
-    }
-    if (direct) {
-        // O went out unnormalised (the accumulators are only ever read by stores, which
-        // keeps the allocator from moving them out of the accumulation registers); each
-        // lane now scales the lines it wrote, which are still in L2
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int row = rbase + rb * 32;
-            if (row < p.R) {
-                const float inv = ltot[rb] > 0.0f ? 1.0f / ltot[rb] : 0.0f;
-                float *op = out_row(p, b, kvh, row) + 4 * h;
-                f32x4 v[DB][4];  // all of the row's pieces in flight at once
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-                        v[db][g4] = *reinterpret_cast<const f32x4 *>(op + db * 32 + g4 * 8);
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4)
-                        *reinterpret_cast<f32x4 *>(op + db * 32 + g4 * 8) = v[db][g4] * inv;
-            }
-        }
-        return;
     }
     if (!p.counters) return;  // merged by the separate merge kernel
 
