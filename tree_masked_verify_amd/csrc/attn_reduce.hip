@@ -44,14 +44,16 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(const float *__restric
     nv = nv < 1 ? 1 : (nv > S ? S : nv);
 
     const int64_t base0 = ((int64_t)b * Hkv + kvh) * S * (int64_t)R + r;
+    // the chunks' reference maxima across the lanes (lane s: chunk s, then s + 64, ...):
+    // their maximum M in one round trip per 64 chunks
     float M = kNegInfR;
-#pragma unroll 8
-    for (int s = 0; s < nv; ++s) M = fmaxf(M, ws_ml[(base0 + (int64_t)s * R) * 2]);
+    for (int s = lane; s < nv; s += 64) M = fmaxf(M, ws_ml[(base0 + (int64_t)s * R) * 2]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
 
-    // chunks in groups of four whose loads are all issued before any is used, so that
-    // the merge waits for one memory round trip per group, not per chunk; the sums
-    // still run over the chunks in order
-    constexpr int GRP = 4;
+    // chunks in groups of eight whose loads are all issued before any is used, so that
+    // the merge waits for one memory round trip per group, not per chunk; the sums run
+    // over the chunks in order
+    constexpr int GRP = 8;
     f32x4 acc[VPL];
     for (int v = 0; v < VPL; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
     float L = 0.0f;
