@@ -5,7 +5,8 @@ the workspace: they must be zero before a call and every call must leave them ze
 the shapes of the calls before it.  Here one zero-filled workspace serves, in turn, calls
 whose chunks are merged inside the kernel (several chunks per sequence, with partials;
 balanced and explicit splits), calls whose one chunk per sequence is written directly,
-calls merged by the separate kernel (small splits, head_dim 512), at head_dim 128 and 256.
+calls merged by the separate kernel (small splits, head_dim 512), at head_dim 128 and 256,
+and fp32 calls on the vector-ALU kernel (merged inside it, or one chunk written directly).
 After every call the counters are read back (all zero) and the output is compared with the
 oracle's, every row.
 """
@@ -45,6 +46,10 @@ def _cases():
         # head_dim 128, written directly
         (wl.scaled(long, name="ws-direct-d128", B=32, T=8, max_levels=4, D=128,
                    prefix=(200, 400), V=11), 64, 0),
+        # fp32 on the vector ALUs: chunks merged inside the kernel, and one chunk written
+        # directly
+        (wl.scaled(wl.WORKLOADS["tiny"], name="ws-f32", B=4, prefix=(100, 300)), 67, 0),
+        (wl.WORKLOADS["tiny"], 68, 1),
         # head_dim 512 (separate merge), then the first shape again on the used workspace
         (wl.WORKLOADS["chain2k"], 65, 0),
         (wl.scaled(long, name="ws-fused-again", B=8, prefix=(900, 1400), V=11), 66, 0),

@@ -1,6 +1,7 @@
-// attn_common.h -- device helpers shared by the matrix-core attention kernels: the
-// kernel parameters, direct global->LDS tile loads and their bookkeeping, LDS-only
-// barriers, the paged-cache cursor and block-table lookups, and key validity.
+// attn_common.h -- device helpers shared by the attention kernels: the matrix-core
+// kernels' parameters, direct global->LDS tile loads and their bookkeeping, LDS-only
+// barriers, the paged-cache cursor and block-table lookups, key validity, and the
+// device-coherent loads of the in-kernel chunk merges.
 #pragma once
 
 #include "sv_internal.h"
@@ -217,6 +218,21 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Wait until at most N of this wavefront's tile loads are still in flight (loads
 // complete in issue order).
+// Device-coherent reads of what other workgroups (possibly on other XCDs) wrote: buffer
+// loads with the device-scope cache policy (sc1), through a resource covering `bytes`
+// from `base` (reads past it return 0).
+constexpr int kCoherent = 16;                       // sc1
+constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
+}
+__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_loads() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

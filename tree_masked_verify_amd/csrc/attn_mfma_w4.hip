@@ -383,20 +383,6 @@ __device__ __forceinline__ float *out_row(const MfmaParams &p, int b, int kvh, i
     return p.out + (((int64_t)b * p.T + i) * p.Hq + (int64_t)kvh * p.G + g) * (int64_t)p.D;
 }
 
-// Device-coherent reads of what other workgroups (possibly on other XCDs) wrote: buffer
-// loads with the device-scope cache policy (sc1), through a resource covering `bytes`
-// from `base` (reads past it return 0).
-constexpr int kCoherent = 16;                       // sc1
-constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw 32-bit buffer, gfx9 family
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
-}
-__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
-}
-__device__ __forceinline__ float coherent_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent));
-}
 
 // The merge of the nv chunks of one (sequence, kv head, row group), rows rbase and
 // rbase + 32 of this lane (its half h of each 8-wide d piece), from their partials:

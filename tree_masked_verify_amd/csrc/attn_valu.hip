@@ -1,5 +1,7 @@
 // attn_valu.hip -- tree-masked split-KV attention on the vector ALUs, for fp32 inputs.
-// Same partial-result format as attn_mfma.hip, so the same merge finishes it.
+// A sequence whose prefix is one chunk writes its output directly; otherwise the chunks'
+// partial results (the format attn_mfma.hip uses) are merged by the last chunk of each
+// (sequence, kv head, row group) to finish, or by the separate merge kernel.
 //
 // What is computed (ADR-037 Phase status rows E1.1-E1.5, section 4 Phase E1): every
 // query row (q head g of kv head kvh, tree node i) attends to the cached prefix of its
@@ -13,7 +15,7 @@
 // from LDS, the key row read as 16-byte vectors from a padded LDS row), the 16 threads
 // of a row reduce the max and sum by shuffles, and the same thread then accumulates
 // head_dim entries sub, sub + 16, ... of the row's output.
-#include "sv_internal.h"
+#include "attn_common.h"
 
 namespace sv {
 namespace {
@@ -39,6 +41,9 @@ struct ValuParams {
     int S, C, n_rg, total;
     float *ws_o;
     float *ws_ml;
+    float *out;            // [B][T][Hq][D]
+    int32_t *counters;     // arrivals per (sequence, kv head, row group); NULL: the
+                           // separate merge kernel combines the chunks
 };
 
 template <int D>
@@ -52,7 +57,8 @@ struct VCfg {
     static constexpr int VS = KS + kKeysV * KROW;     // [16][D]
     static constexpr int PS = VS + kKeysV * D;        // [16][16] probabilities
     static constexpr int OK = PS + kRowsV * kKeysV;   // [16] key exists
-    static constexpr int FLOATS = OK + kKeysV;
+    static constexpr int FLAG = OK + kKeysV;          // the merge's arrival flag
+    static constexpr int FLOATS = FLAG + 1;
     static_assert(PIECES % 256 == 0, "tile pieces");
 };
 
@@ -221,8 +227,22 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
         }
     }
 
+    // chunks of this sequence: chunk 0, and every later one that starts inside the prefix
+    const int nv = (int)min((int64_t)p.S, P > 0 ? ((int64_t)P + p.C - 1) / p.C : (int64_t)1);
+    const int gg = row_ok ? row / p.T : 0;
+    float *op = p.out + (((int64_t)b * p.T + node) * p.Hq + (int64_t)kvh * p.G + gg) * D;
+    if (p.counters && nv == 1) {
+        // the whole prefix in this chunk: the normalised output goes straight to out
+        if (row_ok) {
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int j = 0; j < DPT; ++j) op[sub + kKeysV * j] = o[j] * inv;
+        }
+        return;
+    }
+    const int64_t ubase = ((int64_t)b * p.Hkv + kvh) * p.S * (int64_t)p.R;  // slot (s, r)
     if (row_ok) {
-        const int64_t base = (((int64_t)b * p.Hkv + kvh) * p.S + s) * p.R + row;
+        const int64_t base = ubase + (int64_t)s * p.R + row;
 #pragma unroll
         for (int j = 0; j < DPT; ++j) p.ws_o[base * D + sub + kKeysV * j] = o[j];
         if (sub == 0) {
@@ -230,6 +250,63 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
             p.ws_ml[base * 2 + 1] = l;
         }
     }
+    if (!p.counters) return;  // merged by the separate merge kernel
+
+    // The last of the nv chunks of this (sequence, kv head, row group) to finish merges
+    // them, in chunk order.  Each thread waits until its partial stores have reached L2;
+    // one thread then counts the arrival with a device-scope release (which writes this
+    // XCD's L2 back, so the partials are visible from every XCD).  The last arrival resets
+    // the counter for the next call and reads the partials with device-coherent loads.
+    wait_loads<0>();
+    __syncthreads();
+    int *flag = reinterpret_cast<int *>(fsm + Cf::FLAG);
+    if (tid == 0) {
+        int32_t *cnt = p.counters + ((int64_t)b * p.Hkv + kvh) * p.n_rg + rg;
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == nv - 1;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    __syncthreads();
+    if (!*flag || !row_ok) return;
+    // the 16 threads of the row: the chunks' reference maxima across them, then the
+    // chunks four at a time with every load issued before any is used
+    const uint32_t rows = (uint32_t)nv * (uint32_t)p.R;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(p.ws_o + ubase * D, rows * D * 4);
+    const __amdgpu_buffer_rsrc_t rml = coherent_rsrc(p.ws_ml + ubase * 2, rows * 8);
+    float M = kNegInfV;
+    for (int c = sub; c < nv; c += kKeysV)
+        M = fmaxf(M, coherent_load1(rml, ((uint32_t)c * p.R + row) * 8));
+#pragma unroll
+    for (int off = 1; off < kKeysV; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    constexpr int GRP = 4;
+    float acc[DPT];
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) acc[j] = 0.0f;
+    float L = 0.0f;
+    for (int c0 = 0; c0 < nv; c0 += GRP) {
+        float mc[GRP], lc[GRP], oc[GRP][DPT];
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const int c = c0 + k < nv ? c0 + k : nv - 1;
+            const uint32_t slot = (uint32_t)c * p.R + row;
+            mc[k] = c0 + k < nv ? coherent_load1(rml, slot * 8) : kNegInfV;
+            lc[k] = coherent_load1(rml, slot * 8 + 4);
+#pragma unroll
+            for (int j = 0; j < DPT; ++j)
+                oc[k][j] = coherent_load1(ro, (slot * D + sub + kKeysV * j) * 4);
+        }
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) {
+            const float wgt = mc[k] == kNegInfV ? 0.0f : exp2f(mc[k] - M);
+            L += wgt * lc[k];
+#pragma unroll
+            for (int j = 0; j < DPT; ++j) acc[j] += wgt * oc[k][j];
+        }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) op[sub + kKeysV * j] = acc[j] * inv;
 }
 
 template <int D>
@@ -267,6 +344,8 @@ hipError_t launch_v(const AttnArgs &a, const AttnPlan &pl, hipStream_t stream) {
     p.total = a.B * a.Hkv * pl.S * pl.n_rg;
     p.ws_o = a.ws_o;
     p.ws_ml = a.ws_ml;
+    p.out = a.out;
+    p.counters = pl.fused ? a.ws_cnt : nullptr;
     const int grid = (p.total + kNumXCD - 1) / kNumXCD * kNumXCD;
     hipLaunchKernelGGL(attn_valu_kernel<D>, dim3(grid), dim3(256), smem, stream, p);
     return hipGetLastError();

@@ -136,8 +136,11 @@ int make_attn_plan(int B, int Hq, int Hkv, int T, int D, int max_prefix_len, int
     // merges faster in the separate kernel, which spreads the merge over many workgroups
     // instead of leaving each unit's to one.  The arrival counters must fit their region,
     // and one unit's partials must stay within a 31-bit byte offset.
-    p->fused = p->mfma && attn_w4_handles(D) && units <= kMaxMergeUnits &&
-               (S == 1 || units * S >= kNumCU) && S * (int64_t)R * D * 4 < ((int64_t)1 << 31);
+    // The fp32 kernel merges inside itself whenever the counters and offsets allow: its
+    // units are 16 rows, so one workgroup's merge is as short as the separate kernel's.
+    const bool merge_fits = units <= kMaxMergeUnits && S * (int64_t)R * D * 4 < ((int64_t)1 << 31);
+    p->fused = merge_fits && ((p->mfma && attn_w4_handles(D) && (S == 1 || units * S >= kNumCU)) ||
+                              !p->mfma);
     int64_t work, o_elems, ml_elems;
     if (!prod_ok({units, S}, &work) || work > INT_MAX) return SV_ERR_OVERFLOW;
     if (!prod_ok({(int64_t)B, Hkv, S, R, D}, &o_elems)) return SV_ERR_OVERFLOW;

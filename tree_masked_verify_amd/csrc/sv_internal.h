@@ -44,9 +44,9 @@ struct AttnPlan {
     int C;             // keys per chunk, multiple of kKeyTile (unless balanced)
     int balanced;      // 1: the kernel sizes chunks from the actual prefix lengths and
                        // starts the largest first (attn_w4 kernel, B * S <= kBalancedChunks)
-    int fused;         // 1: the attention kernel merges the chunks itself (attn_w4 kernel,
-                       // at most kMaxMergeUnits (sequence, kv head, row group) units);
-                       // 0: the separate merge kernel does
+    int fused;         // 1: the attention kernel merges the chunks itself (attn_w4 and
+                       // fp32 kernels, at most kMaxMergeUnits (sequence, kv head, row
+                       // group) units); 0: the separate merge kernel does
     // Workspace layout: [arrival counters][header][partial (m, l)][partial O].  The
     // counters sit at offset 0 in a region of fixed size, so that they stay where they
     // were whatever the shapes of earlier calls on the same workspace.

@@ -263,7 +263,8 @@ def make_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu",
 
     # cache geometry: every sequence owns ceil((P_b + T) / block_size) blocks
     if w.block_size == 0:
-        cap = capacity_override or max(w.capacity, max_p + w.T)
+        # one block per sequence; block sizes are multiples of 16 rows
+        cap = capacity_override or -(-max(w.capacity, max_p + w.T) // 16) * 16
         bs = cap
         nblk = np.ones(w.B, dtype=np.int64)
     else:
