@@ -546,10 +546,15 @@ def main():
     # the bound is the side the call's arithmetic intensity puts it on: matrix cores when
     # its flops per algorithmic byte exceed the ratio of the two peaks (2500e12 / 8000e9)
     mfma_bound = flops_attn / bytes_attn > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    fused = w.dtype == "bf16" and w.D in (128, 256) and (w.Hq // w.Hkv) * w.T >= 16
+    if w.dtype != "bf16":
+        kernel = f"attn_valu_kernel<{w.D}> (chunks merged in the kernel)"
+    elif w.D in (128, 256):
+        kernel = (f"attn_w4_kernel<{w.D}> (chunks merged in the kernel when the grid fills the "
+                  "chip, else by attn_reduce_kernel)")
+    else:
+        kernel = f"attn_mfma_kernel<{w.D}> + attn_reduce_kernel"
     roofline = {"bound": "mfma" if mfma_bound else "hbm",
-                "kernel": (f"attn_w4_kernel<{w.D}> (one launch; chunks merged in the kernel)"
-                           if fused else "attention split kernel + merge kernel"),
+                "kernel": kernel,
                 "achieved": round(tflops, 1) if mfma_bound else round(gbs, 1),
                 "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
                 "unit": "TFLOP/s" if mfma_bound else "GB/s",
