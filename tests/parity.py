@@ -22,16 +22,21 @@ ATOL = 1e-2
 REL_RMS = 2.0 ** -6
 
 
-def gpu_step(inp: wl.Inputs, num_splits: int = 0, repeats: int = 1):
-    st = VerifyStep.from_inputs(inp, num_splits=num_splits)
-    for _ in range(repeats):
-        st.run()
+def step_result(st: VerifyStep, inp: wl.Inputs) -> dict:
+    """Every output of a step that has run, and both cache pools, on the host."""
     torch.cuda.synchronize()
     return dict(mask=to_np(st.mask).view(np.uint64), depth=to_np(st.depth),
                 tree_err=to_np(st.tree_err), out=to_np(st.out), argmax=to_np(st.argmax),
                 L=to_np(st.accepted_len), nodes=to_np(st.accepted_nodes),
                 toks=to_np(st.out_tokens), npl=to_np(st.new_prefix_len),
                 k_pool=to_np(inp.k_pool), v_pool=to_np(inp.v_pool))
+
+
+def gpu_step(inp: wl.Inputs, num_splits: int = 0, repeats: int = 1):
+    st = VerifyStep.from_inputs(inp, num_splits=num_splits)
+    for _ in range(repeats):
+        st.run()
+    return step_result(st, inp)
 
 
 def host_copy(inp: wl.Inputs):
@@ -48,6 +53,22 @@ def oracle_step(orc: O.Oracle, inp: wl.Inputs, h: dict, rows=None):
     am, L, nodes, toks = orc.accept_longest_path(h["logits"], h["draft"], h["parents"], err)
     npl = orc.kv_commit(h["k_tree"], h["v_tree"], L, nodes, err, h["cache"], h["prefix"],
                         inp.max_prefix_len)
+    return dict(mask=mask, depth=depth, tree_err=err, out=out, argmax=am, L=L, nodes=nodes,
+                toks=toks, npl=npl, k_pool=h["cache"].k, v_pool=h["cache"].v)
+
+
+def oracle_in_cache(orc: O.Oracle, inp: wl.Inputs, h: dict, rows=None):
+    """The write-before-accept step in the oracle: append every tree row to the cache,
+    attend over the cache-resident tree, accept, then compact the accepted rows."""
+    w = inp.w
+    mask, depth, err = orc.build_tree_mask(h["parents"])
+    err = orc.kv_append(h["k_tree"], h["v_tree"], err, h["cache"], h["prefix"],
+                        inp.max_prefix_len)
+    out = orc.tree_verify_attention(h["q"], None, None, h["cache"], h["prefix"],
+                                    inp.max_prefix_len, mask, inp.scale, rows=rows)
+    am, L, nodes, toks = orc.accept_longest_path(h["logits"], h["draft"], h["parents"], err)
+    npl = orc.kv_compact(L, nodes, err, h["cache"], h["prefix"], inp.max_prefix_len, w.Hkv, w.T,
+                         w.D)
     return dict(mask=mask, depth=depth, tree_err=err, out=out, argmax=am, L=L, nodes=nodes,
                 toks=toks, npl=npl, k_pool=h["cache"].k, v_pool=h["cache"].v)
 

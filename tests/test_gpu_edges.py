@@ -208,14 +208,14 @@ def test_unattended_cache_rows_may_be_nonfinite(orc, case):
     # the cache-resident variant reads the tree rows at P + j; the rows after them stay
     # poisoned
     if case in ("d256", "d512"):
-        from test_gpu_incache import _result, oracle_in_cache
+        from parity import oracle_in_cache, step_result
         inp = wl.make_inputs(w, seed=27, device=DEV, prefix_override=[333, 517, 130])
         _poison_unattended(inp)
         h = host_copy(inp)
         st = VerifyStep.from_inputs(inp)
         st.run_in_cache()
         torch.cuda.synchronize()
-        compare(_result(st, inp), oracle_in_cache(orc, inp, h))
+        compare(step_result(st, inp), oracle_in_cache(orc, inp, h))
 
 
 def test_attended_nan_stays_in_its_rows(orc):

@@ -14,7 +14,7 @@ import torch
 
 import oracle as O
 from _support import oracle_cache, to_np
-from parity import compare, host_copy, sample_rows
+from parity import compare, host_copy, oracle_in_cache, sample_rows, step_result
 from tree_masked_verify_amd import make_cache, sv_kv_append, sv_kv_compact
 from tree_masked_verify_amd import workloads as wl
 from tree_masked_verify_amd.step import VerifyStep
@@ -34,29 +34,6 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _result(st, inp):
-    torch.cuda.synchronize()
-    return dict(mask=to_np(st.mask).view(np.uint64), depth=to_np(st.depth),
-                tree_err=to_np(st.tree_err), out=to_np(st.out), argmax=to_np(st.argmax),
-                L=to_np(st.accepted_len), nodes=to_np(st.accepted_nodes),
-                toks=to_np(st.out_tokens), npl=to_np(st.new_prefix_len),
-                k_pool=to_np(inp.k_pool), v_pool=to_np(inp.v_pool))
-
-
-def oracle_in_cache(orc, inp, h, rows=None):
-    w = inp.w
-    mask, depth, err = orc.build_tree_mask(h["parents"])
-    err = orc.kv_append(h["k_tree"], h["v_tree"], err, h["cache"], h["prefix"],
-                        inp.max_prefix_len)
-    out = orc.tree_verify_attention(h["q"], None, None, h["cache"], h["prefix"],
-                                    inp.max_prefix_len, mask, inp.scale, rows=rows)
-    am, L, nodes, toks = orc.accept_longest_path(h["logits"], h["draft"], h["parents"], err)
-    npl = orc.kv_compact(L, nodes, err, h["cache"], h["prefix"], inp.max_prefix_len, w.Hkv, w.T,
-                         w.D)
-    return dict(mask=mask, depth=depth, tree_err=err, out=out, argmax=am, L=L, nodes=nodes,
-                toks=toks, npl=npl, k_pool=h["cache"].k, v_pool=h["cache"].v)
-
-
 def committed_rows(inp, pool, P, L, b):
     """Rows [0, P + L) of sequence b (all kv heads) from a host pool, via the table."""
     table = to_np(inp.block_table)
@@ -72,7 +49,7 @@ def run_case(orc, w, seed, rows=None, num_splits=0, also_write_through=True):
     h = host_copy(inp)
     st = VerifyStep.from_inputs(inp, num_splits=num_splits)
     st.run_in_cache()
-    g = _result(st, inp)
+    g = step_result(st, inp)
     o = oracle_in_cache(orc, inp, h, rows=rows)
     err = compare(g, o, rows=rows)
     _say(f"       attention max-abs {err['max_abs']:.3e}, accepted {list(g['L'][:8])}")
@@ -80,7 +57,7 @@ def run_case(orc, w, seed, rows=None, num_splits=0, also_write_through=True):
         inp2 = wl.make_inputs(w, seed=seed, device=DEV)
         st2 = VerifyStep.from_inputs(inp2, num_splits=num_splits)
         st2.run()
-        g2 = _result(st2, inp2)
+        g2 = step_result(st2, inp2)
         assert np.array_equal(g["out"], g2["out"]), "attention differs from the buffer path"
         assert np.array_equal(g["L"], g2["L"]) and np.array_equal(g["npl"], g2["npl"])
         P = h["prefix"]
@@ -123,7 +100,7 @@ def test_refused_sequence(orc):
     h = host_copy(inp)
     st = VerifyStep.from_inputs(inp)
     st.run_in_cache()
-    g = _result(st, inp)
+    g = step_result(st, inp)
     o = oracle_in_cache(orc, inp, h)
     assert g["tree_err"].tolist() == [0, 3, 0] and o["tree_err"].tolist() == [0, 3, 0]
     assert g["L"][1] == 0 and g["npl"][1] == P[1]
