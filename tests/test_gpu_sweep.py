@@ -14,6 +14,13 @@ are held to max-abs 1e-2 and relative RMS 2^-6 on every row.  Every other case t
 the write-before-accept step on fresh inputs from the same seed (append, attention over
 the cache-resident tree, acceptance, compaction) against the oracle's, the same way.  The
 oracle's work per case is bounded, so the sweep takes well under a minute of host time.
+
+Two more sweeps of 60 cases each cover the other stages the same way: sampled acceptance
+(temperatures from 0.05 to 2, vocabularies from 1 to 151936, trees and draft-match rates
+as above), held to the sampled tests' rule (identical results except a decision within
+5e-5 of its boundary, which must pass the fp64 replay); and the draft tree (top-K of every
+drafter row, then the best-first expansion; K from 1 to 64, level limits, logits from
+narrow to wide and on coarse grids that make ties common), held to the draft tests' rule.
 """
 import sys
 
@@ -25,11 +32,15 @@ import oracle as O
 from parity import compare, gpu_step, host_copy, oracle_in_cache, oracle_step, step_result
 from tree_masked_verify_amd import workloads as wl
 from tree_masked_verify_amd.step import VerifyStep
+from test_gpu_draft import check_draft, check_topk
+from test_gpu_sampled import run as run_sampled
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 N_CASES = 120
 ORACLE_BUDGET = 4e8          # B * Hq * T * (max prefix + T) * D per case
+N_STAGE_CASES = 60
+LOGIT_BUDGET = 2e7           # B * T * V per case of the sampled and draft sweeps
 
 
 def _say(*a):
@@ -47,6 +58,23 @@ def _tree_ok(w: wl.Workload, seed: int) -> bool:
         return False
 
 
+def _tree_kind(rng: np.random.Generator, T: int):
+    """A tree kind for T nodes and its parameters (random trees get enough levels and
+    children per node for T nodes to fit)."""
+    kind = str(rng.choice(["chain", "random", "eagle2"])) if T > 1 else "chain"
+    levels, children, topk = 0, 0, 0
+    if kind == "random":
+        children = int(rng.integers(2, 5))
+        need = 1
+        while sum(children ** j for j in range(need)) < T:
+            need += 1
+        levels = int(rng.integers(need, max(need, min(T, 8)) + 1))
+    elif kind == "eagle2":
+        topk = int(rng.integers(2, 9))
+        levels = int(rng.integers(3, 9))
+    return kind, levels, children, topk
+
+
 def _draw(rng: np.random.Generator, i: int):
     while True:
         dtype = "bf16" if rng.random() < 0.7 else "f32"
@@ -62,17 +90,7 @@ def _draw(rng: np.random.Generator, i: int):
         V = int(rng.choice([1, 7, 100, 1000, 5000, 32000]))
         std = float(rng.choice([0.5, 1.0, 2.0]))
         draft_p = float(rng.choice([0.0, 0.5, 0.9, 1.0]))
-        kind = str(rng.choice(["chain", "random", "eagle2"])) if T > 1 else "chain"
-        levels, children, topk = 0, 0, 0
-        if kind == "random":
-            children = int(rng.integers(2, 5))
-            need = 1
-            while sum(children ** j for j in range(need)) < T:
-                need += 1
-            levels = int(rng.integers(need, max(need, min(T, 8)) + 1))
-        elif kind == "eagle2":
-            topk = int(rng.integers(2, 9))
-            levels = int(rng.integers(3, 9))
+        kind, levels, children, topk = _tree_kind(rng, T)
         if B * Hkv * G * T * (hi + T) * D > ORACLE_BUDGET:
             continue
         w = wl.Workload(name=f"sweep{i:02d}", B=B, Hq=Hkv * G, Hkv=Hkv, D=D, dtype=dtype,
@@ -90,6 +108,55 @@ def _cases():
 
 
 CASES = _cases()
+
+
+VOCABS = [1, 2, 7, 100, 1000, 17000, 65537, 151936]
+TREE_SIZES = [1, 2, 3, 5, 8, 13, 16, 17, 31, 32, 33, 48, 63, 64]
+
+
+def _draw_sampled(rng: np.random.Generator, i: int):
+    while True:
+        B = int(rng.integers(1, 9))
+        T = int(rng.choice(TREE_SIZES))
+        V = int(rng.choice(VOCABS))
+        if B * T * V > LOGIT_BUDGET:
+            continue
+        kind, levels, children, topk = _tree_kind(rng, T)
+        w = wl.Workload(name=f"sampled{i:02d}", B=B, Hq=1, Hkv=1, D=128, dtype="bf16",
+                        prefix=(0, 0), T=T, tree=kind, V=V,
+                        logit_std=float(rng.choice([0.5, 2.0, 8.0])),
+                        draft_p=float(rng.choice([0.0, 0.5, 0.9, 1.0])), block_size=0,
+                        max_levels=levels, max_children=children, topk=topk,
+                        temperature=float(rng.choice([0.05, 0.3, 1.0, 2.0])))
+        seed = 2000 + i
+        if _tree_ok(w, seed):
+            return w, seed
+
+
+def _tree_capacity(K: int, levels: int) -> int:
+    return sum(min(K ** j, 65) for j in range(levels))
+
+
+def _draw_draft(rng: np.random.Generator, i: int):
+    while True:
+        B = int(rng.integers(1, 9))
+        T = int(rng.choice(TREE_SIZES))
+        V = int(rng.choice(VOCABS))
+        if B * T * V > LOGIT_BUDGET:
+            continue
+        K = int(rng.integers(1, min(64, V) + 1))
+        levels = int(rng.integers(1, 9))
+        if _tree_capacity(K, levels) < T:
+            continue
+        return dict(name=f"draft{i:02d}", B=B, T=T, V=V, K=K, levels=levels,
+                    std=float(rng.choice([0.5, 2.0, 8.0, 40.0])),
+                    grid=bool(rng.random() < 0.3), seed=3000 + i)
+
+
+SAMPLED_CASES = [_draw_sampled(np.random.Generator(np.random.PCG64([20261202, 1, i])), i)
+                 for i in range(N_STAGE_CASES)]
+DRAFT_CASES = [_draw_draft(np.random.Generator(np.random.PCG64([20261202, 2, i])), i)
+               for i in range(N_STAGE_CASES)]
 
 
 @pytest.fixture(scope="module")
@@ -118,3 +185,25 @@ def test_sweep(orc, case):
         st.run_in_cache()
         err = compare(step_result(st, inp), oracle_in_cache(orc, inp, h))
         _say(f"       write-before-accept: attention max-abs {err['max_abs']:.3e}")
+
+
+@pytest.mark.parametrize("case", range(N_STAGE_CASES), ids=[c[0].name for c in SAMPLED_CASES])
+def test_sweep_sampled(orc, case):
+    w, seed = SAMPLED_CASES[case]
+    inp = wl.make_inputs(w, seed=seed, device=DEV)
+    run_sampled(orc, inp.logits, inp.draft, inp.parents, w.temperature, seed,
+                label=f"{w.name} {w.tree} std={w.logit_std} draft_p={w.draft_p}")
+
+
+@pytest.mark.parametrize("case", range(N_STAGE_CASES), ids=[c["name"] for c in DRAFT_CASES])
+def test_sweep_draft(orc, case):
+    c = DRAFT_CASES[case]
+    rng = np.random.default_rng(c["seed"])
+    x = rng.normal(0.0, c["std"], size=(c["B"], c["T"], c["V"]))
+    if c["grid"]:  # a coarse grid: many tied logits
+        x = np.round(x * 4.0) / 4.0
+    x = x.astype(np.float32)
+    roots = rng.integers(0, c["V"], size=c["B"]).astype(np.int32)
+    label = f"{c['name']} std={c['std']}{' grid' if c['grid'] else ''}"
+    check_topk(orc, x.reshape(-1, c["V"]), c["K"], label=label)
+    check_draft(orc, x, roots, c["K"], c["levels"], label=label)
