@@ -21,6 +21,8 @@ as above), held to the sampled tests' rule (identical results except a decision 
 5e-5 of its boundary, which must pass the fp64 replay); and the draft tree (top-K of every
 drafter row, then the best-first expansion; K from 1 to 64, level limits, logits from
 narrow to wide and on coarse grids that make ties common), held to the draft tests' rule.
+A last sweep of 40 cases covers the tree-position RoPE (even head_dims from 2 to 1024, bf16
+and fp32, theta from 100 to 10^6, positions up to 2^20), held to the RoPE tests' rules.
 """
 import sys
 
@@ -33,6 +35,7 @@ from parity import compare, gpu_step, host_copy, oracle_in_cache, oracle_step, s
 from tree_masked_verify_amd import workloads as wl
 from tree_masked_verify_amd.step import VerifyStep
 from test_gpu_draft import check_draft, check_topk
+from test_gpu_rope import check as check_rope
 from test_gpu_sampled import run as run_sampled
 
 pytestmark = pytest.mark.gpu
@@ -153,10 +156,31 @@ def _draw_draft(rng: np.random.Generator, i: int):
                     grid=bool(rng.random() < 0.3), seed=3000 + i)
 
 
+def _draw_rope(rng: np.random.Generator, i: int):
+    while True:
+        B = int(rng.integers(1, 9))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        T = int(rng.choice(TREE_SIZES))
+        D = int(rng.choice([2, 4, 6, 32, 64, 96, 128, 256, 512, 1024]))
+        kind, levels, children, topk = _tree_kind(rng, T)
+        w = wl.Workload(name=f"rope{i:02d}", B=B, Hq=Hkv * G, Hkv=Hkv, D=D,
+                        dtype=str(rng.choice(["bf16", "f32"])), prefix=(0, 0), T=T, tree=kind,
+                        V=1, logit_std=1.0, draft_p=0.0, block_size=0, max_levels=levels,
+                        max_children=children, topk=topk)
+        prefix = rng.integers(0, int(rng.choice([64, 4096, 65536, 1 << 20])) + 1, size=B)
+        theta = float(rng.choice([100.0, 10000.0, 500000.0, 1000000.0]))
+        seed = 4000 + i
+        if _tree_ok(w, seed):
+            return w, seed, [int(v) for v in prefix], theta
+
+
 SAMPLED_CASES = [_draw_sampled(np.random.Generator(np.random.PCG64([20261202, 1, i])), i)
                  for i in range(N_STAGE_CASES)]
 DRAFT_CASES = [_draw_draft(np.random.Generator(np.random.PCG64([20261202, 2, i])), i)
                for i in range(N_STAGE_CASES)]
+ROPE_CASES = [_draw_rope(np.random.Generator(np.random.PCG64([20261202, 3, i])), i)
+              for i in range(40)]
 
 
 @pytest.fixture(scope="module")
@@ -207,3 +231,13 @@ def test_sweep_draft(orc, case):
     label = f"{c['name']} std={c['std']}{' grid' if c['grid'] else ''}"
     check_topk(orc, x.reshape(-1, c["V"]), c["K"], label=label)
     check_draft(orc, x, roots, c["K"], c["levels"], label=label)
+
+
+@pytest.mark.parametrize("case", range(len(ROPE_CASES)), ids=[c[0].name for c in ROPE_CASES])
+def test_sweep_rope(orc, case):
+    w, seed, prefix, theta = ROPE_CASES[case]
+    inp = wl.make_inputs(w, seed=seed, device=DEV, with_logits=False)
+    # beyond 2^16 a last-bit difference of a frequency can flip more roundings than the
+    # ordinary rule allows: there the RoPE tests' absolute rule applies
+    check_rope(orc, inp, theta, prefix=prefix, label=f"{w.name} {w.tree} P<={max(prefix)}",
+               large=max(prefix) > 65536)
