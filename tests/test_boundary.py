@@ -325,3 +325,30 @@ def test_fuzz_entry_points_reject(lib, B, Hq, Hkv, T, D, P, V, K, lv, bs, mbs, n
     _ok_or_empty(lib.sv_topk_logprobs(None, B, V, K, FAKE, FAKE, None), B)
     _ok_or_empty(lib.sv_draft_tree(None, FAKE, B, T, V, K, lv, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                    None), B)
+
+
+def test_entry_point_imports_resolve():
+    """Every `from M import a, b` inside the functions of __graft_entry__.py (the build
+    and smoke entry points) names something M defines, so that the smoke run does not
+    fail on a helper that moved.  Checked on the CPU by importing M, without running
+    anything on a GPU."""
+    import ast
+    import importlib
+
+    with open(os.path.join(ROOT, "__graft_entry__.py")) as f:
+        src = f.read()
+    missing = []
+    for fn in ast.parse(src).body:
+        if not isinstance(fn, ast.FunctionDef):
+            continue
+        for node in ast.walk(fn):
+            if isinstance(node, ast.ImportFrom) and node.module and node.level == 0:
+                mod = importlib.import_module(node.module)
+                for a in node.names:
+                    if hasattr(mod, a.name):
+                        continue
+                    try:  # a submodule
+                        importlib.import_module(f"{node.module}.{a.name}")
+                    except ImportError:
+                        missing.append(f"{node.module}.{a.name}")
+    assert not missing, missing
