@@ -105,8 +105,10 @@ def test_many_copies_of_one_tree(orc):
 
 
 def test_odd_vocabulary_and_chunks(orc):
-    """V odd (rows not 16-byte aligned) and above one 65536-element chunk."""
-    for V in (70001, 131073, 5):
+    """V odd (rows not 16-byte aligned), over several 16384-element chunks, and rows of
+    more than 16 chunks (the walk merges a row's chunk pairs sixteen at a time): 524288 =
+    32 chunks, 600001 = 37."""
+    for V in (70001, 131073, 5, 524288, 600001):
         w = wl.scaled(wl.WORKLOADS["parity512"], V=V, B=4)
         inp = wl.make_inputs(w, seed=V % 97, device=DEV)
         run(orc, inp.logits, inp.draft, inp.parents, 0.3, V % 97, label=f"V={V}")

@@ -20,7 +20,9 @@
 // workgroup locates the drawn token: the chunk from the chunk pairs (a wave prefix scan),
 // the 256-element tile inside it from tile sums (one coalesced pass over the chunk, which
 // leaves the element weights in LDS), and the element inside the tile from a wavefront
-// prefix scan over its 256 weights.
+// prefix scan over its 256 weights.  A lane the whole wavefront agrees on is read with
+// readlane, and the prefix scans are DPP row shifts and broadcasts, not permutes through
+// LDS.
 #include "sv_internal.h"
 
 namespace sv {
@@ -116,6 +118,34 @@ __device__ __forceinline__ float weight_of(float raw, float m, float k) {
     return l == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f((l - m) * k);
 }
 
+// The value lane l holds, for a lane index every lane agrees on: a scalar read of one
+// lane instead of a cross-lane permute through LDS.
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+__device__ __forceinline__ float lane_f(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// A float moved across lanes by one DPP control; lanes without a source, or outside the
+// rows of kRowMask, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes (every lane active): shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then the last lane of row 0 (row 2) added to row 1 (row 3)
+// and lane 31 to rows 2 and 3.
+__device__ __forceinline__ float wave_incl_sum(float x) {
+    x += dpp_f<0x111, 0xf>(x);
+    x += dpp_f<0x112, 0xf>(x);
+    x += dpp_f<0x114, 0xf>(x);
+    x += dpp_f<0x118, 0xf>(x);
+    x += dpp_f<0x142, 0xa>(x);
+    x += dpp_f<0x143, 0xc>(x);
+    return x;
+}
+
 constexpr int kWalkWaves = 16;  // wavefronts of the walk kernel's workgroup
 
 __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
@@ -182,8 +212,8 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
             float wx = 0.0f;         // weight of this lane's token in its parent's row
             for (;;) {
                 R = 1.0f;
-                const float mv = __shfl(st.m, v, 64);
-                const float zv = __shfl(st.s, v, 64);
+                const float mv = lane_f(st.m, v);
+                const float zv = lane_f(st.s, v);
                 const bool kid = in && p == v && lane > 0;
                 wx = (kid && xin && zv > 0.0f) ? weight_of(lx, mv, k) : 0.0f;  // kid: p < lane
                 const float px = zv > 0.0f ? wx / zv : 0.0f;
@@ -193,11 +223,11 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 while (kids) {
                     const int c = __builtin_ctzll(kids);
                     kids &= kids - 1;
-                    const int32_t xc = __shfl(x, c, 64);
-                    const bool okc = __shfl((int)xin, c, 64) != 0;
+                    const int32_t xc = lane_i(x, c);
+                    const bool okc = lane_i((int)xin, c) != 0;
                     const bool dup = __ballot(rej && x == xc) != 0ull;
-                    const float pc = (okc && !dup) ? __shfl(px, c, 64) : 0.0f;
-                    const float u = __shfl(ux, c, 64);
+                    const float pc = (okc && !dup) ? lane_f(px, c) : 0.0f;
+                    const float u = lane_f(ux, c);
                     if (u * R < pc) {
                         next = c;
                         break;
@@ -208,7 +238,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                     }
                 }
                 if (next < 0) break;
-                const int32_t xn = __shfl(x, next, 64);
+                const int32_t xn = lane_i(x, next);
                 if (lane == 0) out_tokens[row0 + L - 1] = xn;
                 path |= 1ull << next;
                 ++L;
@@ -229,8 +259,8 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 ex_tok[slot] = x;
                 ex_w[slot] = wx;
             }
-            const float mv = __shfl(st.m, v, 64);
-            const float zv = __shfl(st.s, v, 64);
+            const float mv = lane_f(st.m, v);
+            const float zv = lane_f(st.s, v);
             if (lane == 0) {
                 s_state[0] = 0;
                 s_state[1] = v;
@@ -270,20 +300,16 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                         if (ex_tok[j] >= lo && ex_tok[j] < hi) wc -= ex_w[j];
                     wc = wc > 0.0f ? wc : 0.0f;
                 }
-                float incl = wc;  // inclusive prefix over the lanes
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float o = __shfl_up(incl, off, 64);
-                    if (lane >= off) incl += o;
-                }
+                const float incl = wave_incl_sum(wc);  // inclusive prefix over the lanes
                 const uint64_t hm = __ballot(wc > 0.0f && carry + incl > target);
                 if (hm) {
                     const int hl = __builtin_ctzll(hm);
                     pick = c0 + hl;
-                    r = target - (carry + __shfl(incl - wc, hl, 64));
+                    r = target - (carry + lane_f(incl - wc, hl));
                 } else {
                     const uint64_t pm = __ballot(wc > 0.0f);
                     if (pm) lastc = c0 + 63 - __builtin_clzll(pm);
-                    carry += __shfl(incl, 63, 64);
+                    carry += lane_f(incl, 63);
                 }
             }
             if (pick < 0 && lastc >= 0) {  // rounding: the last chunk with weight, its end
@@ -355,11 +381,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 tw[q] = x > 0.0f ? x : 0.0f;
                 mine += tw[q];
             }
-            float incl = mine;
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            const float incl = wave_incl_sum(mine);
             const float r = s_r[0];
             float acc = incl - mine;
             int hit = -1, lastq = -1;
@@ -380,12 +402,12 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
             const uint64_t hm = __ballot(hit >= 0);
             if (hm) {
                 const int hl = __builtin_ctzll(hm);
-                pick = 4 * hl + __shfl(hit, hl, 64);
-                rr = r - __shfl(before_hit, hl, 64);
+                pick = 4 * hl + lane_i(hit, hl);
+                rr = r - lane_f(before_hit, hl);
             } else {  // rounding: the last tile with weight, its end
                 const uint64_t lm = __ballot(lastq >= 0);
                 const int ll = lm ? 63 - __builtin_clzll(lm) : 0;
-                pick = lm ? 4 * ll + __shfl(lastq, ll, 64) : -1;
+                pick = lm ? 4 * ll + lane_i(lastq, ll) : -1;
                 rr = __builtin_huge_valf();
             }
             if (lane == 0) {
@@ -408,11 +430,7 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
                 e[q] = wy;
             }
             const float mine = e[0] + e[1] + e[2] + e[3];
-            float incl = mine;  // inclusive prefix over lanes
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            const float incl = wave_incl_sum(mine);  // inclusive prefix over lanes
             const float r = s_r[1];
             float acc = incl - mine;
             int hit = -1, lastpos = -1;
@@ -426,12 +444,12 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
             const uint64_t hm = __ballot(hit >= 0);
             if (hm) {
                 const int hl = __builtin_ctzll(hm);
-                tok = (int32_t)(__shfl((int)(base + (hit < 0 ? 0 : hit)), hl, 64));
+                tok = lane_i((int)(base + (hit < 0 ? 0 : hit)), hl);
             } else {
                 // rounding: the last element with weight in the tile
                 const uint64_t lm = __ballot(lastpos >= 0);
                 const int ll = lm ? 63 - __builtin_clzll(lm) : 0;
-                tok = (int32_t)(__shfl((int)(base + (lastpos < 0 ? 0 : lastpos)), ll, 64));
+                tok = lane_i((int)(base + (lastpos < 0 ? 0 : lastpos)), ll);
                 if (!lm) tok = 0;
             }
         }
