@@ -585,12 +585,20 @@ def main():
         "stages_us": stages,
         "accepted_tokens_per_step": int(st.accepted_len.sum()),
         "argmax_gbs": round(bytes_argmax / (stages["accept"] * 1e-6) / 1e9, 1),
+        # KV commit: the accepted rows of K and V read from the tree buffers and written to
+        # the cache (a few hundred KB per call: latency-bound, not a bandwidth figure)
+        "commit_gbs": round(2 * 2 * int(st.accepted_len.sum()) * w.Hkv * w.D
+                            * (2 if w.dtype == "bf16" else 4) / (stages["commit"] * 1e-6) / 1e9, 1),
         # sampled acceptance: one read of every logit row (the walk and the draw touch a
         # few more bytes per sequence, not counted)
         "accept_sampled_gbs": round(bytes_argmax / (stages["accept_sampled"] * 1e-6) / 1e9, 1),
         # the whole step with the write-before-accept cache update (append, attention over
         # the cache-resident tree, compaction) instead of delayed write-through
         "ms_per_step_write_before_accept": round(ms_step_in_cache, 4),
+        # its append: every tree row of K and V read from the tree buffers and written to
+        # the cache
+        "append_gbs": round(2 * 2 * w.B * w.Hkv * w.T * w.D * (2 if w.dtype == "bf16" else 4)
+                            / (stages["append"] * 1e-6) / 1e9, 1),
         # draft tree: one read of the drafter rows that can be expanded (all but the last)
         "draft_tree_gbs": round(w.B * (w.T - 1) * w.V * 4 / (stages["draft_tree"] * 1e-6) / 1e9,
                                 1),
