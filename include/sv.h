@@ -193,8 +193,8 @@ size_t sv_tree_verify_attention_workspace_size(int32_t B, int32_t Hq, int32_t Hk
  * out-of-range entry would have named -- may be anything, NaN included, without
  * affecting any output.  A non-finite value in an attended row gives an
  * unspecified (typically NaN) output for the rows that attend to it, and, on the
- * matrix-core paths (bf16, >= 16 query rows per kv head), possibly for the other
- * rows of the same sequence and kv head (0 * inf in the weighted sum).
+ * matrix-core paths (every bf16 call), possibly for the other rows of the same
+ * sequence and kv head (0 * inf in the weighted sum).
  * Errors: SV_ERR_NULL, SV_ERR_SHAPE (B < 0, max_prefix_len < 0, block_size not a
  * positive multiple of 16, num_splits < 0, strides not positive, scale not
  * positive and finite),
