@@ -10,11 +10,12 @@
 // Workgroup: 256 threads own 16 query rows of one (sequence, kv head, chunk); keys stream
 // through LDS 16 at a time.  A tile is staged with 16-byte loads, one address computed
 // per key, and the next tile's loads are issued into registers before the current tile
-// is computed, so a tile costs one memory round trip that overlaps the arithmetic.
-// Thread (row = t / 16, sub = t % 16) scores key `sub` against its row (Q row broadcast
-// from LDS, the key row read as 16-byte vectors from a padded LDS row), the 16 threads
-// of a row reduce the max and sum by shuffles, and the same thread then accumulates
-// head_dim entries sub, sub + 16, ... of the row's output.
+// is computed, so a tile costs one memory round trip that overlaps the arithmetic (the
+// first tile's loads go out before Q is staged).  Thread (row = t / 16, sub = t % 16)
+// scores key `sub` against its row (Q row broadcast from LDS, the key row read as 16-byte
+// vectors from a padded LDS row); the 16 threads of a row, one row of 16 lanes, reduce the
+// max and sum by DPP; the same thread then accumulates head_dim entries 4 sub .. 4 sub + 3
+// of every 64 of the row's output, reading the V rows 16 bytes at a time.
 #include "attn_common.h"
 
 namespace sv {
@@ -23,6 +24,26 @@ namespace {
 constexpr int kRowsV = 16;
 constexpr int kKeysV = 16;
 constexpr float kNegInfV = -__builtin_huge_valf();
+
+// Maximum / sum over each row of 16 lanes, in every lane of the row (a row is the 16
+// threads of one query row): DPP butterflies (quad_perm 1032 and 2301, row_half_mirror,
+// row_mirror) instead of permutes through LDS.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_row(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_row<0xb1>(x));
+    x = fmaxf(x, dpp_row<0x4e>(x));
+    x = fmaxf(x, dpp_row<0x141>(x));
+    return fmaxf(x, dpp_row<0x140>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_row<0xb1>(x);
+    x += dpp_row<0x4e>(x);
+    x += dpp_row<0x141>(x);
+    return x + dpp_row<0x140>(x);
+}
 
 struct ValuParams {
     const float *q;
@@ -99,27 +120,19 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     const bool row_ok = row < p.R;
     const int node = row_ok ? row - (row / p.T) * p.T : 0;
 
-    // stage Q rows (16-byte pieces)
-    for (int e = tid; e < kRowsV * D / 4; e += blockDim.x) {
-        const int r = e / (D / 4), d4 = e - r * (D / 4);
-        const int rr = rg * kRowsV + r;
-        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (rr < p.R) {
-            const int gg = rr / p.T, ii = rr - (rr / p.T) * p.T;
-            v = *reinterpret_cast<const f32x4 *>(
-                p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gg) * p.T + ii) * D + 4 * d4);
-        }
-        *reinterpret_cast<f32x4 *>(qs + r * D + 4 * d4) = v;
-    }
-    const uint64_t mrow = row_ok ? p.mask[(int64_t)b * p.T + node] : 0ull;
-
     // Tile u: prefix keys start + 16u .. (u < ntp), else tree rows 16 (u - ntp) ...  This
     // thread's pieces j: key kk = (tid + 256 j) / (D / 4), 16-byte piece d4 of that key.
     // A key that does not exist (past the chunk or the tree, or behind an out-of-range
     // block entry) is staged as zeros and marked absent.
     f32x4 kreg[Cf::PER], vreg[Cf::PER];
     bool kok[Cf::PER];
-    auto fetch = [&](int u) {
+    // The 16 keys of a prefix tile start at a multiple of 16 and so lie in one cache block
+    // (block sizes are multiples of 16): one block-table entry per tile, read a tile ahead
+    // of the fetch that uses it, so no fetch waits on the table.
+    auto tile_block = [&](int u) -> int32_t {
+        return u < ntp ? p.table[(int64_t)b * p.max_blocks + (start + u * kKeysV) / p.bs] : -1;
+    };
+    auto fetch = [&](int u, int32_t tblk) {
         const bool tree = u >= ntp;
         const int k0 = tree ? (u - ntp) * kKeysV : start + u * kKeysV;
 #pragma unroll
@@ -145,11 +158,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
                               (int64_t)(cpos % p.bs) * p.rstride;
                     }
                 }
-            } else if (pos < end) {
-                const int32_t blk = p.table[(int64_t)b * p.max_blocks + pos / p.bs];
-                if (blk >= 0 && blk < p.num_blocks)
-                    off = (int64_t)blk * p.bstride + (int64_t)kvh * p.hstride +
-                          (int64_t)(pos % p.bs) * p.rstride;
+            } else if (pos < end && tblk >= 0 && tblk < p.num_blocks) {
+                off = (int64_t)tblk * p.bstride + (int64_t)kvh * p.hstride +
+                      (int64_t)(pos % p.bs) * p.rstride;
             }
             kok[j] = off >= 0;
             kreg[j] = off >= 0 ? *reinterpret_cast<const f32x4 *>(kb + off + 4 * d4)
@@ -169,20 +180,50 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
         }
     };
 
-    constexpr int DPT = D / kKeysV;  // output entries per thread
+    // Output entries of this thread: head_dim 4 sub + 64 jj + e (e < 4), DPT in all, so that
+    // the V rows are read 16 bytes at a time.
+    constexpr int DPT = D / kKeysV;
+    constexpr int NV = D / 64;
     float o[DPT];
 #pragma unroll
     for (int j = 0; j < DPT; ++j) o[j] = 0.0f;
     float m = kNegInfV, l = 0.0f;
 
-    if (nt > 0) fetch(0);
+    int32_t blk_next = tile_block(1);
+    if (nt > 0) fetch(0, tile_block(0));
+    // stage Q rows (16-byte pieces; all loads issued before the first store), while the
+    // first tile's loads are in flight
+    constexpr int QPER = kRowsV * D / 4 / 256;
+    f32x4 qv[QPER];
+#pragma unroll
+    for (int j = 0; j < QPER; ++j) {
+        const int e = tid + 256 * j;
+        const int r = e / (D / 4), d4 = e - r * (D / 4);
+        const int rr = rg * kRowsV + r;
+        qv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (rr < p.R) {
+            const int gg = rr / p.T, ii = rr - (rr / p.T) * p.T;
+            qv[j] = *reinterpret_cast<const f32x4 *>(
+                p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gg) * p.T + ii) * D + 4 * d4);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < QPER; ++j) {
+        const int e = tid + 256 * j;
+        const int r = e / (D / 4), d4 = e - r * (D / 4);
+        *reinterpret_cast<f32x4 *>(qs + r * D + 4 * d4) = qv[j];
+    }
+    const uint64_t mrow = row_ok ? p.mask[(int64_t)b * p.T + node] : 0ull;
     for (int u = 0; u < nt; ++u) {
         const bool tree = u >= ntp;
         const int k0 = tree ? (u - ntp) * kKeysV : start + u * kKeysV;
         __syncthreads();  // previous tile fully consumed (and Q staged)
         stash();
         __syncthreads();
-        if (u + 1 < nt) fetch(u + 1);  // in flight while this tile is computed
+        if (u + 1 < nt) {  // in flight while this tile is computed
+            fetch(u + 1, blk_next);
+            blk_next = tile_block(u + 2);
+        }
 
         // score of key `sub` for row `rl`: four independent partial sums over head_dim
         const int pos = k0 + sub;
@@ -201,15 +242,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
         }
         const float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         const float x = ok ? dot * p.scale_log2 : kNegInfV;
-        float mt = x;
-#pragma unroll
-        for (int off = 1; off < kKeysV; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off, 64));
+        const float mt = row16_max(x);
         const float mnew = fmaxf(m, mt);
-        const float alpha = mnew == kNegInfV ? 1.0f : exp2f(m - mnew);
-        const float pr = x == kNegInfV ? 0.0f : exp2f(x - mnew);
-        float lt = pr;
-#pragma unroll
-        for (int off = 1; off < kKeysV; off <<= 1) lt += __shfl_xor(lt, off, 64);
+        const float alpha = mnew == kNegInfV ? 1.0f : __builtin_amdgcn_exp2f(m - mnew);
+        const float pr = x == kNegInfV ? 0.0f : __builtin_amdgcn_exp2f(x - mnew);
+        const float lt = row16_sum(pr);
         l = l * alpha + lt;
         m = mnew;
         ps[rl * kKeysV + sub] = pr;
@@ -218,12 +255,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
 #pragma unroll
         for (int k = 0; k < kKeysV; ++k) pk[k] = ps[rl * kKeysV + k];
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) {
-            const int d = sub + kKeysV * j;
-            float a2 = o[j] * alpha;
+        for (int jj = 0; jj < NV; ++jj) {
+            f32x4 a2 = f32x4{o[4 * jj], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]} * alpha;
 #pragma unroll
-            for (int k = 0; k < kKeysV; ++k) a2 = fmaf(pk[k], vs[k * D + d], a2);
-            o[j] = a2;
+            for (int k = 0; k < kKeysV; ++k) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(vs + k * D + 4 * sub + 64 * jj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a2[e] = fmaf(pk[k], v[e], a2[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[4 * jj + e] = a2[e];
         }
     }
 
@@ -236,7 +277,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
         if (row_ok) {
             const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-            for (int j = 0; j < DPT; ++j) op[sub + kKeysV * j] = o[j] * inv;
+            for (int jj = 0; jj < NV; ++jj)
+                *reinterpret_cast<f32x4 *>(op + 4 * sub + 64 * jj) =
+                    f32x4{o[4 * jj], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]} * inv;
         }
         return;
     }
@@ -244,7 +287,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     if (row_ok) {
         const int64_t base = ubase + (int64_t)s * p.R + row;
 #pragma unroll
-        for (int j = 0; j < DPT; ++j) p.ws_o[base * D + sub + kKeysV * j] = o[j];
+        for (int jj = 0; jj < NV; ++jj)
+            *reinterpret_cast<f32x4 *>(p.ws_o + base * D + 4 * sub + 64 * jj) =
+                f32x4{o[4 * jj], o[4 * jj + 1], o[4 * jj + 2], o[4 * jj + 3]};
         if (sub == 0) {
             p.ws_ml[base * 2 + 0] = m;
             p.ws_ml[base * 2 + 1] = l;
@@ -277,15 +322,15 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     float M = kNegInfV;
     for (int c = sub; c < nv; c += kKeysV)
         M = fmaxf(M, coherent_load1(rml, ((uint32_t)c * p.R + row) * 8));
-#pragma unroll
-    for (int off = 1; off < kKeysV; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    M = row16_max(M);
     constexpr int GRP = 4;
-    float acc[DPT];
+    f32x4 acc[NV];
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) acc[j] = 0.0f;
+    for (int jj = 0; jj < NV; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     float L = 0.0f;
     for (int c0 = 0; c0 < nv; c0 += GRP) {
-        float mc[GRP], lc[GRP], oc[GRP][DPT];
+        float mc[GRP], lc[GRP];
+        f32x4 oc[GRP][NV];
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
             const int c = c0 + k < nv ? c0 + k : nv - 1;
@@ -293,20 +338,20 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
             mc[k] = c0 + k < nv ? coherent_load1(rml, slot * 8) : kNegInfV;
             lc[k] = coherent_load1(rml, slot * 8 + 4);
 #pragma unroll
-            for (int j = 0; j < DPT; ++j)
-                oc[k][j] = coherent_load1(ro, (slot * D + sub + kKeysV * j) * 4);
+            for (int jj = 0; jj < NV; ++jj)
+                oc[k][jj] = coherent_load4(ro, (slot * D + 4 * sub + 64 * jj) * 4);
         }
 #pragma unroll
         for (int k = 0; k < GRP; ++k) {
-            const float wgt = mc[k] == kNegInfV ? 0.0f : exp2f(mc[k] - M);
+            const float wgt = mc[k] == kNegInfV ? 0.0f : __builtin_amdgcn_exp2f(mc[k] - M);
             L += wgt * lc[k];
 #pragma unroll
-            for (int j = 0; j < DPT; ++j) acc[j] += wgt * oc[k][j];
+            for (int jj = 0; jj < NV; ++jj) acc[jj] += wgt * oc[k][jj];
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int j = 0; j < DPT; ++j) op[sub + kKeysV * j] = acc[j] * inv;
+    for (int jj = 0; jj < NV; ++jj) *reinterpret_cast<f32x4 *>(op + 4 * sub + 64 * jj) = acc[jj] * inv;
 }
 
 template <int D>
