@@ -73,8 +73,7 @@ struct VCfg {
                                                       // reads of 16 rows hit 64 banks
     static constexpr int PIECES = kKeysV * D / 4;     // 16-byte pieces per tile and tensor
     static constexpr int PER = PIECES / 256;          // per thread
-    static constexpr int QS = 0;                      // [16][D]
-    static constexpr int KS = QS + kRowsV * D;        // [16][KROW]
+    static constexpr int KS = 0;                      // [16][KROW]
     static constexpr int VS = KS + kKeysV * KROW;     // [16][D]
     static constexpr int PS = VS + kKeysV * D;        // [16][16] probabilities
     static constexpr int OK = PS + kRowsV * kKeysV;   // [16] key exists
@@ -87,7 +86,6 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
     using Cf = VCfg<D>;
     extern __shared__ __attribute__((aligned(16))) float fsm[];
-    float *qs = fsm + Cf::QS;
     float *ks = fsm + Cf::KS;
     float *vs = fsm + Cf::VS;
     float *ps = fsm + Cf::PS;
@@ -191,33 +189,24 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
 
     int32_t blk_next = tile_block(1);
     if (nt > 0) fetch(0, tile_block(0));
-    // stage Q rows (16-byte pieces; all loads issued before the first store), while the
-    // first tile's loads are in flight
-    constexpr int QPER = kRowsV * D / 4 / 256;
-    f32x4 qv[QPER];
+    // this thread's slice of its Q row (head_dim QW sub .. QW sub + QW - 1), kept in
+    // registers, loaded while the first tile's loads are in flight
+    constexpr int QW = D / kKeysV;
+    f32x4 qreg[QW / 4];
+    {
+        const int gq = row_ok ? row / p.T : 0;
+        const float *qp =
+            p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gq) * p.T + node) * D + QW * sub;
 #pragma unroll
-    for (int j = 0; j < QPER; ++j) {
-        const int e = tid + 256 * j;
-        const int r = e / (D / 4), d4 = e - r * (D / 4);
-        const int rr = rg * kRowsV + r;
-        qv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (rr < p.R) {
-            const int gg = rr / p.T, ii = rr - (rr / p.T) * p.T;
-            qv[j] = *reinterpret_cast<const f32x4 *>(
-                p.q + (((int64_t)b * p.Hq + (int64_t)kvh * p.G + gg) * p.T + ii) * D + 4 * d4);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < QPER; ++j) {
-        const int e = tid + 256 * j;
-        const int r = e / (D / 4), d4 = e - r * (D / 4);
-        *reinterpret_cast<f32x4 *>(qs + r * D + 4 * d4) = qv[j];
+        for (int q4 = 0; q4 < QW / 4; ++q4)
+            qreg[q4] = row_ok ? *reinterpret_cast<const f32x4 *>(qp + 4 * q4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const uint64_t mrow = row_ok ? p.mask[(int64_t)b * p.T + node] : 0ull;
     for (int u = 0; u < nt; ++u) {
         const bool tree = u >= ntp;
         const int k0 = tree ? (u - ntp) * kKeysV : start + u * kKeysV;
-        __syncthreads();  // previous tile fully consumed (and Q staged)
+        __syncthreads();  // previous tile fully consumed
         stash();
         __syncthreads();
         if (u + 1 < nt) {  // in flight while this tile is computed
@@ -225,22 +214,31 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(ValuParams p) {
             blk_next = tile_block(u + 2);
         }
 
-        // score of key `sub` for row `rl`: four independent partial sums over head_dim
+        // score of key `sub` for row `rl`.  Each thread first forms the partial dot products
+        // of its head_dim slice with all 16 keys, key (sub + j) % 16 in slot j (rotated, so
+        // that the 16 lanes read 16 different K rows, on distinct banks); then a ring over
+        // the row's 16 lanes (each step takes the neighbour's sum, row_ror 1, and adds one
+        // slot) leaves lane sub with the sum over all slices for key sub.
         const int pos = k0 + sub;
         bool ok = okk[sub] != 0;
         if (tree) ok = ok && ((mrow >> pos) & 1ull);
-        const f32x4 *qr = reinterpret_cast<const f32x4 *>(qs + rl * D);
-        const f32x4 *kr = reinterpret_cast<const f32x4 *>(ks + sub * Cf::KROW);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-            const f32x4 a = qr[d4], c = kr[d4];
-            acc[0] = fmaf(a[0], c[0], acc[0]);
-            acc[1] = fmaf(a[1], c[1], acc[1]);
-            acc[2] = fmaf(a[2], c[2], acc[2]);
-            acc[3] = fmaf(a[3], c[3], acc[3]);
+        float vr[kKeysV];
+#pragma unroll
+        for (int j = 0; j < kKeysV; ++j) {
+            const f32x4 *kr =
+                reinterpret_cast<const f32x4 *>(ks + ((sub + j) & (kKeysV - 1)) * Cf::KROW + QW * sub);
+            f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q4 = 0; q4 < QW / 4; ++q4) {
+                const f32x4 c = kr[q4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = fmaf(qreg[q4][e], c[e], a[e]);
+            }
+            vr[j] = (a[0] + a[1]) + (a[2] + a[3]);
         }
-        const float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        float dot = vr[kKeysV - 1];
+#pragma unroll
+        for (int t = 1; t < kKeysV; ++t) dot = dpp_row<0x121>(dot) + vr[kKeysV - 1 - t];
         const float x = ok ? dot * p.scale_log2 : kNegInfV;
         const float mt = row16_max(x);
         const float mnew = fmaxf(m, mt);
