@@ -222,3 +222,24 @@ def test_bf16_head_dim_512_single_node_paged(orc):
     kernel with its row block padded."""
     w = _d512("d512t1", T=1, tree="chain", Hq=8, Hkv=1, B=4)
     run_case(orc, w, 14, prefix_override=[2040, 0, 1001, 17])
+
+
+@pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("bf16", 3), ("f32", 0), ("f32", 2)])
+def test_wide_batch(orc, dtype, splits):
+    """300 sequences with short ragged prefixes (0 to 200 keys) on a shuffled paged cache:
+    grids of hundreds of workgroups per kv head mapped across the XCDs, one chunk per
+    sequence written directly or (explicit splits) several merged inside the kernel across
+    hundreds of units.  Every row against the oracle."""
+    w = wl.scaled(wl.WORKLOADS["batched8k"], name=f"wide-{dtype}-{splits}", B=300, Hq=4, Hkv=2,
+                  D=128, dtype=dtype, T=4, tree="random", max_levels=3, max_children=2,
+                  prefix=(0, 200), V=64)
+    run_case(orc, w, 16, num_splits=splits)
+
+
+def test_more_units_than_arrival_counters(orc):
+    """4200 sequences x 16 kv heads: 67200 (sequence, kv head, row group) units, more than
+    the 65536 arrival counters the merge region holds, so the call takes the separate merge
+    kernel instead of merging inside the attention kernel.  Every row against the oracle."""
+    w = wl.scaled(wl.WORKLOADS["batched8k"], name="units67200", B=4200, Hq=16, Hkv=16, D=128,
+                  T=1, tree="chain", prefix=(0, 48), V=8)
+    run_case(orc, w, 17)

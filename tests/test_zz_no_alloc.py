@@ -5,13 +5,12 @@ output compared byte for byte with the workspace entry point's, and the smaller 
 against the oracle.  A call larger than the scratch is refused before any launch."""
 import sys
 
-import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import tree_masked_verify_amd as sv
-from parity import compare, gpu_step, host_copy, oracle_step
+from parity import ATOL, REL_RMS, attention_error, host_copy
 from tree_masked_verify_amd import workloads as wl
 from tree_masked_verify_amd.step import VerifyStep
 
@@ -56,14 +55,14 @@ def test_noalloc_matches_workspace_entry():
     o = orc.tree_verify_attention(h["q"], h["k_tree"], h["v_tree"], h["cache"], h["prefix"],
                                   inp.max_prefix_len, orc.build_tree_mask(h["parents"])[0],
                                   inp.scale)
-    from parity import attention_error, ATOL, REL_RMS
     mx, rel = attention_error(got.cpu().numpy(), o)
     assert mx <= ATOL and rel <= REL_RMS, (mx, rel)
 
 
 def test_noalloc_head_dim_512_and_vector_alu():
-    """The separate-merge paths (head_dim 512 matrix cores, fp32 vector ALU) keep their
-    partials in the scratch too; again two calls, larger first."""
+    """head_dim 512 on the matrix cores (partials in the scratch, merged by the separate
+    kernel) and fp32 on the vector ALUs (merged inside its kernel, with the arrival
+    counters at the start of the scratch); again two calls, larger first."""
     for w, seed in [(wl.WORKLOADS["chain2k"], 52), (wl.WORKLOADS["tiny"], 53)]:
         _say(f"[case] noalloc {w.name} D={w.D} {w.dtype}")
         inp = wl.make_inputs(w, seed=seed, device=DEV)
