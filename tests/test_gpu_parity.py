@@ -243,3 +243,16 @@ def test_more_units_than_arrival_counters(orc):
     w = wl.scaled(wl.WORKLOADS["batched8k"], name="units67200", B=4200, Hq=16, Hkv=16, D=128,
                   T=1, tree="chain", prefix=(0, 48), V=8)
     run_case(orc, w, 17)
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,T,D,dtype", [
+    ("mqa64", 64, 1, 32, 128, "bf16"),      # 2048 query rows on one kv head: 8 row groups
+    ("gqa16", 32, 2, 64, 256, "bf16"),      # 1024 rows per kv head: 4 row groups
+    ("gqa16-f32", 16, 1, 16, 128, "f32"),   # 256 rows: 16 vector-ALU row groups
+])
+def test_large_gqa_groups(orc, name, Hq, Hkv, T, D, dtype):
+    """GQA groups beyond the sweep's 8 query heads per kv head: many row groups per kv head
+    reading the same K/V, ragged paged prefixes, every row against the oracle."""
+    w = wl.scaled(wl.WORKLOADS["batched8k"], name=name, B=3, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, T=T,
+                  tree="random", max_levels=5, max_children=3, prefix=(100, 900), V=128)
+    run_case(orc, w, 18)
