@@ -249,6 +249,7 @@ def test_more_units_than_arrival_counters(orc):
     ("mqa64", 64, 1, 32, 128, "bf16"),      # 2048 query rows on one kv head: 8 row groups
     ("gqa16", 32, 2, 64, 256, "bf16"),      # 1024 rows per kv head: 4 row groups
     ("gqa16-f32", 16, 1, 16, 128, "f32"),   # 256 rows: 16 vector-ALU row groups
+    ("gqa32-d512", 32, 1, 16, 512, "bf16"),  # 512 rows at head_dim 512: 4 row groups
 ])
 def test_large_gqa_groups(orc, name, Hq, Hkv, T, D, dtype):
     """GQA groups beyond the sweep's 8 query heads per kv head: many row groups per kv head
