@@ -279,3 +279,35 @@ def test_determinism_soak_full_size(name):
             torch.cuda.synchronize()
         for a, b in zip(ref[k % 2], outs(st)):
             assert torch.equal(a, b), f"serial step {k} differs"
+
+
+def test_concurrent_streams():
+    """The library keeps no state between calls: two different steps, each with its own
+    workspaces, enqueued on two streams with no ordering between them (ten rounds), give
+    byte for byte the outputs each gives alone.  One merges several chunks per sequence
+    inside the attention kernel (arrival counters in its workspace), the other is fp32."""
+    shapes = [wl.scaled(wl.WORKLOADS["long32k"], name="cs-a", B=6, prefix=(1200, 2000), V=300),
+              wl.scaled(wl.WORKLOADS["tiny"], name="cs-b", B=5, Hq=4, Hkv=2, prefix=(100, 600),
+                        block_size=16, shuffled=True)]
+    inps = [wl.make_inputs(w, seed=19 + j, device=DEV) for j, w in enumerate(shapes)]
+    steps = [VerifyStep.from_inputs(inp) for inp in inps]
+    pools0 = [(inp.k_pool.clone(), inp.v_pool.clone()) for inp in inps]
+    alone = []
+    for st in steps:
+        st.run()
+        torch.cuda.synchronize()
+        alone.append((st.out.clone(), st.accepted_len.clone(), st.new_prefix_len.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(10):
+        _say(f"[case] concurrent streams round {rnd}")
+        for st, (k0, v0), inp in zip(steps, pools0, inps):
+            inp.k_pool.copy_(k0)
+            inp.v_pool.copy_(v0)
+            st.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for st, s in zip(steps, streams):
+            st.run(stream=s)
+        torch.cuda.synchronize()
+        for st, (o, L, npl) in zip(steps, alone):
+            assert torch.equal(st.out, o), f"round {rnd}: attention output differs"
+            assert torch.equal(st.accepted_len, L) and torch.equal(st.new_prefix_len, npl)
