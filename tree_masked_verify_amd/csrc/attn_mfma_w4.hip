@@ -230,7 +230,9 @@ __device__ __forceinline__ void mask_scores(f32x16 (&sacc)[2], uint32_t kvalid, 
 //        row block per piece), in five stages one piece apart: the fma, the exp2, the
 //        rounding to bf16 into the P^T fragment (element j of fragment c is score element
 //        8c + j), the sum of exactly those two bf16 values (widened by bit shifts), and
-//        its addition to the row sum.  A masked score (-inf) gives 0.
+//        its addition to the row sum.  At head_dim 128, where half as many product steps
+//        hide the pieces, the last two stages are one packed dot product of the pair with
+//        (1, 1) into the row sum.  A masked score (-inf) gives 0.
 constexpr float kNoRef = -1.0e30f;
 
 struct RowState {
@@ -243,6 +245,7 @@ struct SoftTmp {
     float x[16][2], y[16][2], t[16];
 };
 
+template <bool kDotSum>
 __device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowState &rs, SoftTmp &t,
                                               bf16x8 (&pf)[2][2], float scale_log2) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -285,10 +288,15 @@ __device__ __forceinline__ void softmax_piece(int k, const f32x16 (&sp)[2], RowS
             }
             if (k == 7 + i) {
                 const bf16x2 pk = {pf[rb][i >> 2][2 * (i & 3)], pf[rb][i >> 2][2 * (i & 3) + 1]};
-                const uint32_t wv = __builtin_bit_cast(uint32_t, pk);
-                t.t[q] = __uint_as_float(wv << 16) + __uint_as_float(wv & 0xffff0000u);
+                if constexpr (kDotSum) {
+                    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+                    rs.lsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, rs.lsum[rb], false);
+                } else {
+                    const uint32_t wv = __builtin_bit_cast(uint32_t, pk);
+                    t.t[q] = __uint_as_float(wv << 16) + __uint_as_float(wv & 0xffff0000u);
+                }
             }
-            if (k == 8 + i) rs.lsum[rb] += t.t[q];
+            if (!kDotSum && k == 8 + i) rs.lsum[rb] += t.t[q];
         }
     }
 }
@@ -677,7 +685,7 @@ void attn_w4_kernel(MfmaParams p) {
             // the softmax's 16 pieces over the product's 2 DB steps
             constexpr int per = 16 / (2 * DB);
 #pragma unroll
-            for (int r = 0; r < per; ++r) softmax_piece(i * per + r, sc, rs, tmp, pf[cur], p.scale_log2);
+            for (int r = 0; r < per; ++r) softmax_piece<D == 128>(i * per + r, sc, rs, tmp, pf[cur], p.scale_log2);
         });
         settle(pf[cur], rs);
         rescale<D>(o, rs);
