@@ -463,7 +463,8 @@ __global__ __launch_bounds__(64 * kWalkWaves) void sample_walk_kernel(
 }  // namespace
 
 int make_sample_plan(int64_t rows, int64_t V, ArgmaxPlan *p) {
-    if (make_argmax_plan(rows, V, p) != 0) return SV_ERR_SHAPE;
+    const int rc = make_argmax_plan(rows, V, p);
+    if (rc != 0) return rc;
     // the draw re-reads one chunk of the final node's row, by 256-element tiles: at most
     // kMaxTiles tiles a chunk keep that read to one round of loads, while the streaming
     // pass still has several workgroups per row

@@ -350,7 +350,8 @@ int sv_accept_longest_path(const float *logits, const int32_t *draft, const int3
         return SV_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return SV_ERR_ALIGN;
     ArgmaxPlan p;
-    if (make_argmax_plan((int64_t)B * T, V, &p) != 0) return SV_ERR_SHAPE;
+    const int rc = make_argmax_plan((int64_t)B * T, V, &p);
+    if (rc != 0) return rc;
     if (!workspace || workspace_bytes < p.ws_bytes) return SV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SV_ERR_ALIGN;
     hipError_t e = launch_argmax_partial(logits, (int64_t)B * T, V, p, workspace, stream);
@@ -382,7 +383,8 @@ int sv_accept_sampled(const float *logits, const int32_t *draft, const int32_t *
         return SV_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(logits) & 3u) != 0) return SV_ERR_ALIGN;
     ArgmaxPlan p;
-    if (make_sample_plan((int64_t)B * T, V, &p) != 0) return SV_ERR_SHAPE;
+    const int rc = make_sample_plan((int64_t)B * T, V, &p);
+    if (rc != 0) return rc;
     if (!workspace || workspace_bytes < p.ws_bytes) return SV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SV_ERR_ALIGN;
     return hip_status(launch_accept_sampled(logits, draft, parents, tree_err, u_accept, u_sample,

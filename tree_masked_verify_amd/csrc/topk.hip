@@ -77,7 +77,9 @@ __device__ __forceinline__ double exp_term(float x, double md, const double *tab
 // r = x - n/1024 is exact in fp32 with |r| <= 2^-11; with n = 256 k + j,
 // e^x = e^(k/4) * (e^(j/1024) * e^r), the first two factors from tables indexed by bytes
 // of those bits (t1[k + 128] by byte 1, t2[j] by byte 0) and e^r - 1 its Taylor polynomial
-// of degree 4 (remainder below 2^-61 relative).  Same table-driven method as exp_core, with
+// of degree 3 (the remainder, r^4/24 and beyond, stays below 2^-48 relative: under the
+// rounding of the fp64 sum of a row's terms, and one fp64 operation per logit fewer than
+// degree 4).  Same table-driven method as exp_core, with
 // no reduction step and no reference maximum.  The eight table reads are issued before the
 // polynomials, which hide their latency.
 __device__ __forceinline__ void sum_small4(const f32x4 &x, const double *t1, const double *t2,
@@ -96,9 +98,8 @@ __device__ __forceinline__ void sum_small4(const f32x4 &x, const double *t1, con
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const double r = (double)rf[e];
-        double q = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-        q = fma(q, r, 0.5);
-        p[e] = fma(r * r, q, r);                       // e^r - 1
+        const double q = fma(r, 1.0 / 6.0, 0.5);
+        p[e] = fma(r * r, q, r);                       // e^r - 1, to degree 3
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
