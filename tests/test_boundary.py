@@ -147,6 +147,12 @@ def test_accept_validation(lib):
     assert f(*args(B=0)) == 0
     assert sv.sv_accept_longest_path_workspace_size(2, 8, 1000) > 0
     assert sv.sv_accept_longest_path_workspace_size(2, 0, 1000) == 0
+    # rows cut into chunks of at most 16384 logits: one (value, index) pair per row and chunk
+    assert sv.sv_accept_longest_path_workspace_size(1, 1, 151936) >= 10 * 8
+    # one workgroup per row and chunk: 2^26 rows of 31 chunks fit in 2^31 - 1 workgroups,
+    # 33 chunks do not (size 0: the plan is refused)
+    assert sv.sv_accept_longest_path_workspace_size(1 << 20, 64, 16384 * 31) > 0
+    assert sv.sv_accept_longest_path_workspace_size(1 << 20, 64, 16384 * 33) == 0
 
 
 def test_accept_sampled_validation(lib):
@@ -166,8 +172,10 @@ def test_accept_sampled_validation(lib):
     assert f(*args(B=0)) == 0
     assert sv.sv_accept_sampled_workspace_size(2, 8, 1000) > 0
     assert sv.sv_accept_sampled_workspace_size(2, 0, 1000) == 0
-    # chunks of at most 65536 elements: (max, sum) per row and chunk
-    assert sv.sv_accept_sampled_workspace_size(1, 1, 151936) >= 3 * 8
+    # chunks of at most 16384 elements: (max, sum) per row and chunk
+    assert sv.sv_accept_sampled_workspace_size(1, 1, 151936) >= 10 * 8
+    assert sv.sv_accept_sampled_workspace_size(1 << 20, 64, 16384 * 31) > 0
+    assert sv.sv_accept_sampled_workspace_size(1 << 20, 64, 16384 * 33) == 0
 
 
 def test_rope_validation(lib):
