@@ -310,6 +310,24 @@ __device__ __forceinline__ void offer_piece(WaveCands &wc, const f32x4 &x, float
     }
 }
 
+// A lower bound of a row's K-th best logit from a wavefront's first trip: the K-th largest
+// of its 64 lanes' maxima (K <= 64).  K distinct logits reach it, so a logit below it cannot
+// be among the row's K best (one equal to it still can: ties go to the smaller token); the
+// wavefront publishes it as it publishes its K-th best, which filters the rest of the trip
+// instead of taking every logit of its first piece into the buffer.  K rounds of a 64-lane
+// max over order-preserving keys, each taking out the lowest lane that holds the maximum.
+__device__ __forceinline__ float kth_lane_max(float lm, int K, int lane) {
+    const uint32_t u = __float_as_uint(lm);
+    uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // lm is not NaN: key > 0
+    uint32_t m = 0;
+    for (int r = 0; r < K; ++r) {
+        m = wave_max_dpp32(key);
+        const uint64_t bal = __ballot(key == m);
+        if (lane == (int)__builtin_ctzll(bal)) key = 0;
+    }
+    return __uint_as_float((m & 0x80000000u) ? (m & 0x7fffffffu) : ~m);
+}
+
 // The lane's share of sum_y exp(l(y)) in two parts: pieces whose logits all have |x| < 31.5
 // add exp(x) directly (sf, sf2); any other piece goes, whole, to an online max m and a sum s of
 // exp(x - m) (NaN and -inf add 0, +inf counts as the largest finite float).
@@ -373,28 +391,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     const float *rp = logits + src * V;
     constexpr float kNInf = -__builtin_huge_valf();
 
-    s_tab[tid] = exp2((double)tid / 256.0);
-    s_t1[tid] = exp((double)(tid - 128) * 0.25);
-    s_t2[tid] = exp((double)tid / 1024.0);
-    if (tid < kTkWaves) s_pub[tid] = kNInf;
-    __syncthreads();
-
-    WaveCands wc{s_cv[w], s_ci[w], 0, kNInf, s_pub, kNInf};
-    RowSum acc{0.0, 0.0, -kFltMax, (double)-kFltMax, 0.0};
-
     // head: elements before the first 16-byte aligned one (wavefront 0, lanes 0..2)
     const int64_t mis = (int64_t)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);
     int64_t a0 = (4 - mis) & 3;
     if (a0 > V) a0 = V;
     const int64_t nvec = (V - a0) >> 2;
     const int64_t a1 = a0 + 4 * nvec;
-    if (w == 0) {
-        const int nok = lane < a0 ? 1 : 0;
-        const f32x4 x{nok ? rp[lane] : kNInf, kNInf, kNInf, kNInf};
-        const float mx = sum_piece(acc, x, s_tab, s_t1, s_t2);
-        offer_piece(wc, x, mx, nok, lane, K, w, lane);
-    }
-
     // body: 16-byte pieces, piece p = base + u * 256 + tid holds elements a0 + 4p .. + 3;
     // whole trips of four pieces per lane, then one trip with the pieces that are left
     const f32x4 *vp = reinterpret_cast<const f32x4 *>(rp + a0);
@@ -410,9 +412,31 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
             raw[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    rs, (u * kTkThreads + tid) * 16, 0, kNonTemporal));
     };
+    // the first trip's loads go out before the tables are built
+    f32x4 ra[4], rb[4];
+    if (nfull > 0) fetch(ra, 0);
+
+    s_tab[tid] = exp2((double)tid / 256.0);
+    s_t1[tid] = exp((double)(tid - 128) * 0.25);
+    s_t2[tid] = exp((double)tid / 1024.0);
+    if (tid < kTkWaves) s_pub[tid] = kNInf;
+    __syncthreads();
+
+    WaveCands wc{s_cv[w], s_ci[w], 0, kNInf, s_pub, kNInf};
+    RowSum acc{0.0, 0.0, -kFltMax, (double)-kFltMax, 0.0};
+
+    // the head's elements, before the first 16-byte aligned one
+    if (w == 0) {
+        const int nok = lane < a0 ? 1 : 0;
+        const f32x4 x{nok ? rp[lane] : kNInf, kNInf, kNInf, kNInf};
+        const float mx = sum_piece(acc, x, s_tab, s_t1, s_t2);
+        offer_piece(wc, x, mx, nok, lane, K, w, lane);
+    }
+
     // one trip's sums and offers.  The common case, every piece small, is one block, so
     // that its sixteen exponentials interleave.  Most trips hold no logit that could enter
-    // (one test for the four pieces); the others offer their pieces one at a time.
+    // (one test for the four pieces); the others offer their pieces one at a time.  The
+    // first trip first publishes the K-th largest of its lane maxima (kth_lane_max).
     auto trip = [&](const f32x4 (&raw)[4], int64_t base) __attribute__((always_inline)) {
         float mx[4];
         // (all four tested, without short-circuit branches: a bitwise and of the lane masks)
@@ -431,8 +455,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
 #pragma unroll
             for (int u = 0; u < 4; ++u) mx[u] = sum_piece(acc, raw[u], s_tab, s_t1, s_t2);
         }
+        const float tmax = max4_ordered(f32x4{mx[0], mx[1], mx[2], mx[3]});
+        if (base == 0) {
+            const float th = kth_lane_max(tmax, K, lane);
+            if (lane == 0) __hip_atomic_store(wc.pub + w, th, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         refresh_shared(wc);
-        if (!__any(may_enter(wc, max4_ordered(f32x4{mx[0], mx[1], mx[2], mx[3]}), K))) return;
+        if (!__any(may_enter(wc, tmax, K))) return;
         f32x4 r0 = raw[0], r1 = raw[1], r2 = raw[2], r3 = raw[3];
         float m0 = mx[0], m1 = mx[1], m2 = mx[2], m3 = mx[3];
 #pragma unroll 1
@@ -446,8 +475,6 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(
     // two buffers: each trip's loads are in flight during the trip before.  The loads are
     // issued unconditionally (past the last trip they re-read the trip before, in bounds)
     // so that the wait before a trip's math counts that trip's loads only.
-    f32x4 ra[4], rb[4];
-    if (nfull > 0) fetch(ra, 0);
     for (int64_t base = 0; base < nfull; base += 2 * kTrip) {
         const bool two = base + kTrip < nfull;
         fetch(rb, two ? base + kTrip : base);
